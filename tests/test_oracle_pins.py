@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle: each checks it against something other than
+itself -- hand-worked values, format definitions, closed forms, invariants,
+library routines on special cases, and brute force on tiny inputs.
+
+Each pin targets a plausible mistake: a dropped term, a wrong sign or index,
+a transposed operand, a swapped bias axis, a wrong rounding rule.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def bf16_codes(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_codes(x):
+    return np.asarray(x, dtype=np.float16).view(np.uint16)
+
+
+# ---- golden: hand-worked example -------------------------------------------
+def test_worked_example_by_hand():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    A, B = f32(g["A"]), f32(g["B"])
+    C = oracle.gemm(A, "f32", B, "f32")
+    assert np.array_equal(C, np.array(g["C"], dtype=np.float64))
+    for axis in ("row", "col"):
+        e = g[axis]
+        bias = f32(e["bias"])
+        P = oracle.bias_pass(C, bias, "f32", axis)
+        assert np.array_equal(P, np.array(e["P"], dtype=np.float64)), axis
+        Y = oracle.act_pass(P, "relu_bias")
+        assert np.array_equal(Y, np.array(e["relu"], dtype=np.float64)), axis
+        M = oracle.mask_pass(P, 4)
+        assert list(M[:, 0]) == e["mask_words"], axis
+        assert not M[:, 1:].any()
+        # the BIAS epilogue is the identity on P, NONE skips the bias
+        assert np.array_equal(oracle.act_pass(P, "bias"), P)
+
+
+# ---- P1: identity -------------------------------------------------------------
+def test_p1_identity_selects_rows_of_b():
+    m, n, k = 128, 64, 256
+    rng = np.random.default_rng(1)
+    A = np.zeros((m, k), np.float32)
+    A[np.arange(m), np.arange(m)] = 1.0
+    B = f32(rng.standard_normal((k, n)))
+    C = oracle.gemm(A, "f32", B, "f32")
+    assert np.array_equal(C, B[:m].astype(np.float64))
+
+
+# ---- P2: permutation -------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_p2_permutation(dt):
+    m = k = 37
+    n = 23
+    rng = np.random.default_rng(2)
+    perm = rng.permutation(m)
+    Pm = np.zeros((m, k), np.float32)
+    Pm[np.arange(m), perm] = 1.0
+    Bv = rng.standard_normal((k, n)).astype(np.float32)
+    enc = {"bf16": bf16_codes, "f16": f16_codes, "f32": f32}[dt]
+    Bc = enc(Bv)
+    Ac = enc(Pm)
+    C = oracle.gemm(Ac, dt, Bc, dt)
+    Bd = oracle.decode(Bc, dt)
+    assert np.array_equal(C, Bd[perm])
+
+
+# ---- P3: bias axis with A = 0 ----------------------------------------------------
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("ep", ["bias", "relu_bias", "gelu_bias"])
+def test_p3_zero_product_gives_activated_bias(axis, ep):
+    m, n, k = 5, 7, 3
+    A = np.zeros((m, k), np.float32)
+    B = f32(np.random.default_rng(3).standard_normal((k, n)))
+    ramp = np.arange(m if axis == "row" else n, dtype=np.float32) - 2.5  # index ramp
+    Y, P, _ = oracle.reference(A, "f32", B, "f32", ramp, "f32", ep, axis)
+    want_p = np.broadcast_to(ramp[:, None] if axis == "row" else ramp[None, :], (m, n))
+    assert np.array_equal(P, want_p.astype(np.float64))
+    for i in range(m):
+        for j in range(n):
+            x = ramp[i] if axis == "row" else ramp[j]
+            if ep == "bias":
+                assert Y[i, j] == x
+            elif ep == "relu_bias":
+                assert Y[i, j] == max(float(x), 0.0)
+            else:
+                assert Y[i, j] == oracle.act1(x, "gelu_bias")
+
+
+def test_bias_shape_checked():
+    C = np.zeros((3, 4))
+    with pytest.raises(ValueError):
+        oracle.bias_pass(C, f32([1, 2, 3, 4]), "f32", "row")
+
+
+# ---- P4: integer-exact inputs ------------------------------------------------------
+def test_p4_small_integer_inputs_exact():
+    rng = np.random.default_rng(4)
+    m, n, k = 33, 41, 300
+    A = rng.integers(-16, 17, size=(m, k)).astype(np.float32)
+    B = rng.integers(-16, 17, size=(k, n)).astype(np.float32)
+    C = oracle.gemm(bf16_codes(A), "bf16", bf16_codes(B), "bf16")
+    exact = A.astype(np.int64) @ B.astype(np.int64)
+    assert np.array_equal(C, exact.astype(np.float64))
+
+
+# ---- P5: rank-1 closed form --------------------------------------------------------
+def test_p5_rank_one_closed_form():
+    m, n, k = 9, 11, 64
+    u = np.arange(1, m + 1, dtype=np.float32) * 0.5
+    v = np.arange(1, n + 1, dtype=np.float32) * -0.25
+    A = np.repeat(u[:, None], k, axis=1)
+    B = np.repeat(v[None, :], k, axis=0)
+    C = oracle.gemm(f32(A), "f32", f32(B), "f32")
+    assert np.array_equal(C, k * np.outer(u.astype(np.float64), v.astype(np.float64)))
+
+
+# ---- P6: brute force on tiny shapes, both B layouts --------------------------------
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_p6_brute_force_tiny(op_b):
+    rng = np.random.default_rng(6)
+    for m, n, k in itertools.product([1, 2, 3, 5], repeat=3):
+        A = f32(rng.standard_normal((m, k)))
+        Bkn = f32(rng.standard_normal((k, n)))
+        Bstore = np.ascontiguousarray(Bkn.T) if op_b else Bkn
+        C = oracle.gemm(A, "f32", Bstore, "f32", op_b=op_b)
+        # explicit triple sum in Python
+        for i in range(m):
+            for j in range(n):
+                s = 0.0
+                for p in range(k):
+                    s += float(A[i, p]) * float(Bkn[p, j])
+                assert C[i, j] == s
+        # numpy float64 matmul (library routine); equal up to summation order
+        np.testing.assert_allclose(C, A.astype(np.float64) @ Bkn.astype(np.float64),
+                                   rtol=1e-14, atol=1e-14)
+
+
+def test_p6_leading_dimensions_and_scales():
+    """Padded leading dimensions and the fp8 dequantisation factors."""
+    rng = np.random.default_rng(61)
+    m, n, k, lda, ldb = 4, 5, 6, 10, 7
+    Af = rng.standard_normal((m, lda)).astype(np.float32)
+    Bf = rng.standard_normal((k, ldb)).astype(np.float32)
+    C = oracle.gemm(Af.ravel(), "f32", Bf.ravel(), "f32", 0, 0.5, 3.0,
+                    m=m, n=n, k=k, lda=lda, ldb=ldb)
+    want = 1.5 * (Af[:, :k].astype(np.float64) @ Bf[:, :n].astype(np.float64))
+    np.testing.assert_allclose(C, want, rtol=1e-14)
+
+
+def test_gemm_entries_match_brute_force():
+    rng = np.random.default_rng(62)
+    m, n, k = 6, 9, 17
+    A = f16_codes(rng.standard_normal((m, k)))
+    W = f16_codes(rng.standard_normal((n, k)))  # op_b = 1
+    rows = np.array([5, 0, 3, 3])
+    cols = np.array([8, 0, 2, 7])
+    slot = np.arange(4)
+    got = oracle.gemm_entries(np.ascontiguousarray(A[rows]), "f16", slot, cols, W, "f16", op_b=1,
+                              sa=2.0, sb=0.25)
+    Ad = A.view(np.float16).astype(np.float64)
+    Wd = W.view(np.float16).astype(np.float64)
+    for t in range(4):
+        s = sum(Ad[rows[t], p] * Wd[cols[t], p] for p in range(k))
+        assert got[t] == 0.5 * s
+    b = f16_codes(np.arange(n) * 0.5)
+    P = oracle.bias_entries(got, rows, cols, b, "f16", "col")
+    assert np.array_equal(P, got + cols * 0.5)
+    b2 = f16_codes(np.arange(m) * 0.25)
+    P2 = oracle.bias_entries(got, rows, cols, b2, "f16", "row")
+    assert np.array_equal(P2, got + rows * 0.25)
+
+
+# ---- P7: ReLU and mask invariants ----------------------------------------------------
+def test_p7_relu_mask_invariants():
+    rng = np.random.default_rng(7)
+    P = rng.standard_normal((31, 77))
+    P[0, :5] = [0.0, -0.0, 1e-300, -1e-300, np.nan]
+    Y = oracle.act_pass(P, "relu_bias")
+    ldw = 4
+    M = oracle.mask_pass(P, ldw)
+    bits = np.unpackbits(M.view(np.uint8), axis=1, bitorder="little")
+    assert (Y[~np.isnan(P)] >= 0).all()
+    for i in range(P.shape[0]):
+        for j in range(P.shape[1]):
+            b = bits[i, j]
+            if b:
+                assert Y[i, j] == P[i, j] and P[i, j] > 0
+            else:
+                assert Y[i, j] == 0.0
+    assert bits[:, 77:].sum() == 0  # padding bits are zero
+    assert bits[0, :5].tolist() == [0, 0, 1, 0, 0]   # P == 0 -> 0, NaN -> 0
+
+
+# ---- P8: GELU properties --------------------------------------------------------------
+@pytest.mark.parametrize("form", ["gelu_bias", "gelu_erf"])
+def test_p8_gelu_properties(form):
+    g = lambda x: oracle.act1(x, form)
+    assert g(0.0) == 0.0
+    for x in np.linspace(-6, 6, 241):
+        # x*Phi(x) - (-x)*Phi(-x) = x (Phi(x) + Phi(-x)) = x, for both forms
+        assert abs((g(x) - g(-x)) - x) <= 4e-15 * max(1.0, abs(x))
+    h = 1e-6
+    assert abs((g(h) - g(-h)) / (2 * h) - 0.5) < 1e-9       # GELU'(0) = 1/2
+    assert abs(g(30.0) - 30.0) < 1e-12 and abs(g(-30.0)) < 1e-12
+    assert g(-1.0) < 0 and g(1.0) > 0.8                       # dips below zero
+
+
+def test_p8_tanh_form_close_to_erf_form():
+    xs = np.linspace(-8, 8, 16001)
+    d = np.array([oracle.act1(x, "gelu_bias") - 0.5 * x * (1 + math.erf(x / math.sqrt(2))) for x in xs])
+    mx = np.abs(d).max()
+    # the tanh approximation stays within ~5e-4 of the exact form; dropping
+    # the cubic term or misplacing sqrt(2/pi) gives errors of order 1e-2
+    assert 4.0e-4 < mx < 5.0e-4
+    assert 2.4 < abs(xs[np.abs(d).argmax()]) < 3.0
+
+
+# ---- P9: e4m3 codec ---------------------------------------------------------------------
+def test_p9_e4m3_spec_points():
+    spec = json.load(open(os.path.join(GOLDEN, "e4m3_spec.json")))
+    for code, val in spec["codes"].items():
+        got = oracle.decode(np.array([int(code, 16)], np.uint8), "e4m3")[0]
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in spec["nan_codes"]:
+        assert math.isnan(oracle.decode(np.array([int(code, 16)], np.uint8), "e4m3")[0])
+
+
+def test_p9_e4m3_table_vs_torch_and_roundtrip():
+    codes = np.arange(256, dtype=np.uint8)
+    dec = oracle.decode(codes, "e4m3")
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    fin = ~np.isnan(dec)
+    assert np.array_equal(dec[fin], ref[fin])
+    # encode round trip on all finite codes
+    enc = oracle.encode(dec[fin], "e4m3")
+    rt = oracle.decode(enc, "e4m3")
+    assert np.array_equal(rt, dec[fin])
+    # midpoints between neighbours tie to the even code; saturation at 448
+    pos = np.sort(np.unique(dec[fin & (dec >= 0)]))
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        ca, cb = oracle.encode([a], "e4m3")[0], oracle.encode([b], "e4m3")[0]
+        want = ca if ca % 2 == 0 else cb
+        assert oracle.encode([mid], "e4m3")[0] == want, (a, b)
+    assert oracle.decode(oracle.encode([1e6, -1e6, 464.0, 480.0], "e4m3"), "e4m3").tolist() == \
+        [448.0, -448.0, 448.0, 448.0]
+
+
+def test_p9_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(20000) * 50).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ours = oracle.encode(x.astype(np.float64), "e4m3")
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # +0/-0 of tiny values may differ only in sign handling; compare values
+    assert np.array_equal(oracle.decode(ours, "e4m3"), oracle.decode(ref, "e4m3"))
+
+
+# ---- P10: fp16 / bf16 codecs ------------------------------------------------------------
+def test_p10_f16_all_patterns():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    dec = oracle.decode(codes, "f16")
+    ref = codes.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(dec[fin], ref[fin])
+
+
+def test_p10_bf16_all_patterns():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    dec = oracle.decode(codes, "bf16")
+    ref = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(dec[fin], ref[fin])
+
+
+def test_p10_rne_encode_vs_libraries():
+    rng = np.random.default_rng(10)
+    x = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-8, 5, 5000),
+                        [65504.0, 65519.0, 65520.0, 1e-8, 2.0 ** -24, 3 * 2.0 ** -25]]).astype(np.float32)
+    ours16 = oracle.encode(x.astype(np.float64), "f16")
+    assert np.array_equal(ours16, x.astype(np.float16).view(np.uint16))
+    oursb = oracle.encode(x.astype(np.float64), "bf16")
+    refb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oursb, refb)
+
+
+# ---- P11: mask layout ----------------------------------------------------------------------
+def test_p11_mask_layout_vs_packbits():
+    rng = np.random.default_rng(11)
+    m, n = 13, 200
+    ldw = ((n + 127) // 128) * 128 // 32
+    P = rng.standard_normal((m, n))
+    W = oracle.mask_pass(P, ldw)
+    bits = np.zeros((m, ldw * 32), np.uint8)
+    bits[:, :n] = P > 0
+    ref = np.packbits(bits, axis=1, bitorder="little").view("<u4")
+    assert np.array_equal(W, ref)
