@@ -1,0 +1,13 @@
+"""Fused GEMM + bias/activation epilogue for AMD MI355X (gfx950).
+
+D = epilogue(A*B + bias) in one hand-written HIP kernel, behind the C ABI in
+include/gemm_epilog.h.  ``binding`` is the thin ctypes layer with the ABI's
+names; ``build`` compiles the library in-tree with hipcc.
+"""
+from .binding import (GE_BIAS_COL, GE_BIAS_ROW, GE_EPILOG_BIAS, GE_EPILOG_GELU_BIAS,  # noqa: F401
+                      GE_EPILOG_NONE, GE_EPILOG_RELU_AUX_BIAS, GE_EPILOG_RELU_BIAS, GE_F8_E4M3,
+                      GE_F16, GE_F32, GE_BF16, GE_OP_N, GE_OP_T, GemmEpilog, GemmEpilogError,
+                      gemm_epilog_aux_ld, gemm_epilog_create, gemm_epilog_describe,
+                      gemm_epilog_execute, gemm_epilog_free, gemm_epilog_plan,
+                      gemm_epilog_status_string, gemm_epilog_workspace_size, ge_desc, ge_pref,
+                      make_desc)

@@ -1,0 +1,226 @@
+"""ctypes binding of libgemm_epilog.so -- argument marshalling only.
+
+The functions carry the C ABI's names (include/gemm_epilog.h) and raise
+GemmEpilogError (with the status code) instead of returning one.  Every step
+of the computation runs in the library's HIP kernels; torch provides device
+memory and streams.  There is no fallback: if the library is missing, import
+of this module's loader raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loaded first so the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_epilog.so")
+
+# ---- ABI constants (mirror include/gemm_epilog.h) ----------------------------
+GE_OK, GE_ERR_NULL, GE_ERR_SHAPE, GE_ERR_DTYPE, GE_ERR_EPILOG, GE_ERR_ALIGN, \
+    GE_ERR_STATE, GE_ERR_WORKSPACE, GE_ERR_HIP, GE_ERR_ALLOC = range(10)
+GE_F32, GE_F16, GE_BF16, GE_F8_E4M3 = 0, 1, 2, 3
+GE_OP_N, GE_OP_T = 0, 1
+GE_EPILOG_NONE, GE_EPILOG_BIAS, GE_EPILOG_RELU_BIAS, GE_EPILOG_RELU_AUX_BIAS, \
+    GE_EPILOG_GELU_BIAS = range(5)
+GE_BIAS_ROW, GE_BIAS_COL = 0, 1
+
+DTYPE_CODE = {"f32": GE_F32, "f16": GE_F16, "bf16": GE_BF16, "e4m3": GE_F8_E4M3,
+              torch.float32: GE_F32, torch.float16: GE_F16, torch.bfloat16: GE_BF16,
+              torch.float8_e4m3fn: GE_F8_E4M3}
+EPILOG_CODE = {"none": GE_EPILOG_NONE, "bias": GE_EPILOG_BIAS, "relu_bias": GE_EPILOG_RELU_BIAS,
+               "relu_aux_bias": GE_EPILOG_RELU_AUX_BIAS, "gelu_bias": GE_EPILOG_GELU_BIAS}
+AXIS_CODE = {"row": GE_BIAS_ROW, "col": GE_BIAS_COL}
+TORCH_DTYPE = {GE_F32: torch.float32, GE_F16: torch.float16, GE_BF16: torch.bfloat16,
+               GE_F8_E4M3: torch.float8_e4m3fn}
+ELEM_SIZE = {GE_F32: 4, GE_F16: 2, GE_BF16: 2, GE_F8_E4M3: 1}
+
+
+class ge_desc(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32),
+                ("d_type", ctypes.c_int32), ("bias_type", ctypes.c_int32),
+                ("op_b", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldd", ctypes.c_int64)]
+
+
+class ge_pref(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("unfused", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+
+
+class GemmEpilogError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {gemm_epilog_status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              f"(hipcc for gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.gemm_epilog_create.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ge_desc)]
+        L.gemm_epilog_plan.argtypes = [vp, i32, i32, ctypes.POINTER(ge_pref)]
+        L.gemm_epilog_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
+        L.gemm_epilog_aux_ld.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
+        L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gemm_epilog_free.argtypes = [vp]
+        L.gemm_epilog_status_string.argtypes = [ctypes.c_int]
+        L.gemm_epilog_status_string.restype = ctypes.c_char_p
+        L.gemm_epilog_describe.argtypes = [vp, ctypes.c_char_p, sz]
+        for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
+                  "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
+                  "gemm_epilog_describe"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != GE_OK:
+        raise GemmEpilogError(status, what)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def make_desc(m, n, k, a_type, d_type, op_b=GE_OP_N, lda=None, ldb=None, ldd=None,
+              b_type=None, bias_type=None) -> ge_desc:
+    a = DTYPE_CODE[a_type] if not isinstance(a_type, int) else a_type
+    d = DTYPE_CODE[d_type] if not isinstance(d_type, int) else d_type
+    b = a if b_type is None else (DTYPE_CODE[b_type] if not isinstance(b_type, int) else b_type)
+    bt = d if bias_type is None else (DTYPE_CODE[bias_type] if not isinstance(bias_type, int) else bias_type)
+    return ge_desc(m, n, k, a, b, d, bt, op_b, 0,
+                   k if lda is None else lda,
+                   (n if op_b == GE_OP_N else k) if ldb is None else ldb,
+                   n if ldd is None else ldd)
+
+
+# ---- the ABI, same names ---------------------------------------------------------
+def gemm_epilog_create(desc: ge_desc) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().gemm_epilog_create(ctypes.byref(h), ctypes.byref(desc)), "gemm_epilog_create")
+    return h.value
+
+
+def gemm_epilog_plan(h: int, epilog, axis=GE_BIAS_ROW, pref: Optional[ge_pref] = None) -> None:
+    e = EPILOG_CODE[epilog] if isinstance(epilog, str) else epilog
+    a = AXIS_CODE[axis] if isinstance(axis, str) else axis
+    _check(lib().gemm_epilog_plan(h, e, a, ctypes.byref(pref) if pref is not None else None),
+           "gemm_epilog_plan")
+
+
+def gemm_epilog_workspace_size(h: int) -> int:
+    s = ctypes.c_size_t()
+    _check(lib().gemm_epilog_workspace_size(h, ctypes.byref(s)), "gemm_epilog_workspace_size")
+    return s.value
+
+
+def gemm_epilog_aux_ld(h: int) -> int:
+    s = ctypes.c_int64()
+    _check(lib().gemm_epilog_aux_ld(h, ctypes.byref(s)), "gemm_epilog_aux_ld")
+    return s.value
+
+
+def gemm_epilog_execute(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,
+                        workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if isinstance(workspace, torch.Tensor) else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    _check(lib().gemm_epilog_execute(h, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux),
+                                     _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
+                                     workspace_bytes, stream or None),
+           "gemm_epilog_execute")
+
+
+def gemm_epilog_free(h: Optional[int]) -> None:
+    _check(lib().gemm_epilog_free(h), "gemm_epilog_free")
+
+
+def gemm_epilog_status_string(status: int) -> str:
+    return lib().gemm_epilog_status_string(status).decode()
+
+
+def gemm_epilog_describe(h: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().gemm_epilog_describe(h, buf, 512), "gemm_epilog_describe")
+    return buf.value.decode()
+
+
+# ---- convenience object over torch tensors (still marshalling only) ---------------
+class GemmEpilog:
+    """create -> plan -> execute -> free, on torch device tensors.
+
+    A is m x k; B is k x n (op_b=N) or n x k (op_b=T); D is m x n.  The
+    bias holds m (axis 'row') or n (axis 'col') values of D's dtype.
+    """
+
+    def __init__(self, m, n, k, a_dtype, d_dtype, op_b=GE_OP_N, lda=None, ldb=None, ldd=None):
+        self.desc = make_desc(m, n, k, a_dtype, d_dtype, op_b, lda, ldb, ldd)
+        self.h = gemm_epilog_create(self.desc)
+        self.epilog = None
+
+    def plan(self, epilog="bias", axis="row", path=0, unfused=0, tile=0, split_k=0):
+        gemm_epilog_plan(self.h, epilog, axis, ge_pref(path, unfused, tile, split_k))
+        self.epilog = EPILOG_CODE[epilog] if isinstance(epilog, str) else epilog
+        self.ws_bytes = gemm_epilog_workspace_size(self.h)
+        self.aux_ld_bits = gemm_epilog_aux_ld(self.h)
+        return self
+
+    def alloc_outputs(self, device="cuda"):
+        d = self.desc
+        D = torch.empty((d.m, d.ldd), dtype=TORCH_DTYPE[d.d_type], device=device)[:, :d.n]
+        aux = None
+        if self.epilog == GE_EPILOG_RELU_AUX_BIAS:
+            aux = torch.empty((d.m, self.aux_ld_bits // 32), dtype=torch.int32, device=device)
+        ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device) if self.ws_bytes else None
+        return D, aux, ws
+
+    def execute(self, A, B, bias=None, D=None, aux=None, scale_a=None, scale_b=None,
+                workspace=None, stream=None):
+        if D is None:
+            D, aux_new, ws_new = self.alloc_outputs(A.device)
+            aux = aux if aux is not None else aux_new
+            workspace = workspace if workspace is not None else ws_new
+        gemm_epilog_execute(self.h, A, B, bias, D, aux, scale_a, scale_b, workspace,
+                            None if workspace is None else workspace.numel() * workspace.element_size(),
+                            stream)
+        return D, aux
+
+    def describe(self) -> str:
+        return gemm_epilog_describe(self.h)
+
+    def free(self):
+        if self.h:
+            gemm_epilog_free(self.h)
+            self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

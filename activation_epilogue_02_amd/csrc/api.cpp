@@ -1,0 +1,307 @@
+// api.cpp -- the C-ABI front end: handle life cycle, validation, the
+// planner (tile / small-m / unfused choice and launch shape) and execute.
+//
+// Every check runs on the host before any HIP runtime call, so that a call
+// that fails launches nothing (nvmath page, paragraph on dtype and shape
+// rules: mismatched dtypes or a wrongly shaped bias make the fusion fail;
+// epilog page, paragraph on epilog_inputs: tensors must be 16-byte aligned).
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "ge_params.h"
+
+using namespace ge;
+
+struct ge_plan_s {
+    ge_desc d;
+    bool planned = false;
+    int32_t epilog = 0, axis = 0;
+    int32_t path = 0, tile_id = 0, unfused = 0;
+    int32_t split_k = 1, k_per_split = 0;
+    int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
+    unsigned grid = 0;
+    size_t ws_c = 0;         // unfused intermediate bytes
+    size_t ws_partial = 0;   // split-K partial bytes
+    size_t ws_counters = 0;  // split-K counter bytes
+    int64_t ldaux = 0;       // mask row stride, 32-bit words
+};
+
+namespace {
+
+int elem_size(int t) {
+    switch (t) {
+    case GE_F32: return 4;
+    case GE_F16: return 2;
+    case GE_BF16: return 2;
+    case GE_F8_E4M3: return 1;
+    }
+    return 0;
+}
+
+bool dtype_combo_ok(int a, int b, int d) {
+    if (a != b) return false;
+    switch (a) {
+    case GE_F32: return d == GE_F32;
+    case GE_F16: return d == GE_F16 || d == GE_F32;
+    case GE_BF16: return d == GE_BF16 || d == GE_F32;
+    case GE_F8_E4M3: return d == GE_BF16 || d == GE_F16 || d == GE_F32;
+    }
+    return false;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+const TileShape* find_tile(int id) {
+    for (int i = 0; i < kNumTiles; ++i)
+        if (kTiles[i].id == id) return &kTiles[i];
+    return nullptr;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile heuristic: the largest block tile that still gives every CU at least
+// two tiles (256 CUs); below that, the shape with the most tiles.  Large
+// tiles halve the L2 -> LDS traffic per flop; small problems need the
+// parallelism more than the reuse.
+int choose_tile(int64_t m, int64_t n) {
+    const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
+    const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    if (t256 >= 512) return 3;
+    if (t128 >= 512) return 2;
+    if (t256 >= 256 && t128 < 256) return 3;
+    if (t128 >= 256) return 2;
+    return 1;
+}
+
+bool smallm_supported(const ge_desc& d) {
+    return d.m <= 16 && d.op_b == GE_OP_T && (d.a_type == GE_F16 || d.a_type == GE_BF16) &&
+           (d.d_type == d.a_type || d.d_type == GE_F32);
+}
+
+bool test_fail_launch() {
+    const char* e = getenv("GE_TEST_FAIL_LAUNCH");
+    return e && e[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
+    if (!h || !desc) return GE_ERR_NULL;
+    *h = nullptr;
+    const ge_desc& d = *desc;
+    if (d.m < 0 || d.n < 0 || d.k < 0) return GE_ERR_SHAPE;
+    if (d.m > INT32_MAX || d.n > INT32_MAX || d.k > INT32_MAX) return GE_ERR_SHAPE;
+    if (d.reserved != 0 || (d.op_b != GE_OP_N && d.op_b != GE_OP_T)) return GE_ERR_SHAPE;
+    if (!dtype_combo_ok(d.a_type, d.b_type, d.d_type)) return GE_ERR_DTYPE;
+    if (d.bias_type != d.d_type) return GE_ERR_DTYPE;
+    if (d.lda < d.k || d.ldd < d.n) return GE_ERR_SHAPE;
+    if (d.ldb < (d.op_b == GE_OP_N ? d.n : d.k)) return GE_ERR_SHAPE;
+    if ((d.lda * elem_size(d.a_type)) % 16 || (d.ldb * elem_size(d.b_type)) % 16 ||
+        (d.ldd * elem_size(d.d_type)) % 16)
+        return GE_ERR_ALIGN;
+    ge_plan_s* p = new (std::nothrow) ge_plan_s();
+    if (!p) return GE_ERR_ALLOC;
+    p->d = d;
+    *h = p;
+    return GE_OK;
+}
+
+int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* pref) {
+    if (!h) return GE_ERR_NULL;
+    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_GELU_BIAS) return GE_ERR_EPILOG;
+    if (bias_axis != GE_BIAS_ROW && bias_axis != GE_BIAS_COL) return GE_ERR_EPILOG;
+    ge_pref pr = {0, 0, 0, 0};
+    if (pref) pr = *pref;
+    if (pr.path < 0 || pr.path > PATH_SMALLM || pr.unfused < 0 || pr.unfused > 1 || pr.split_k < 0)
+        return GE_ERR_SHAPE;
+    if (pr.tile != 0 && !find_tile(pr.tile)) return GE_ERR_SHAPE;
+    const ge_desc& d = h->d;
+
+    ge_plan_s q = *h;
+    q.planned = false;
+    q.epilog = epilog;
+    q.axis = bias_axis;
+    q.unfused = (pr.unfused && epilog != GE_EPILOG_NONE) ? 1 : 0;
+    q.ldaux = (epilog == GE_EPILOG_RELU_AUX_BIAS) ? (int64_t)round_up((size_t)d.n, 128) / 32 : 0;
+    if (q.ldaux > INT32_MAX) return GE_ERR_SHAPE;
+
+    int path = pr.path;
+    if (path == 0) path = smallm_supported(d) ? PATH_SMALLM : PATH_TILE;
+    if (path == PATH_SMALLM && !smallm_supported(d)) return GE_ERR_SHAPE;
+    q.path = path;
+    q.split_k = 1;
+    q.ws_partial = q.ws_counters = 0;
+    if (path == PATH_SMALLM) {
+        q.tile_id = 0;
+        q.tiles_m = 1;
+        q.tiles_n = (int32_t)ceil_div(d.n, 16);
+        int split = pr.split_k > 0 ? pr.split_k : 1;
+        const int64_t steps = ceil_div(d.k, 32);
+        if (split > steps) split = steps > 0 ? (int)steps : 1;
+        q.k_per_split = (int32_t)(ceil_div(steps, split) * 32);
+        split = q.k_per_split > 0 ? (int)ceil_div(d.k, q.k_per_split) : 1;
+        q.split_k = split;
+        q.group_m = 1;
+        const int64_t grid = (int64_t)q.tiles_n * split;
+        if (grid > INT32_MAX) return GE_ERR_SHAPE;
+        q.grid = (unsigned)grid;
+        if (split > 1) {
+            q.ws_partial = round_up((size_t)split * q.tiles_n * 256 * sizeof(float), 256);
+            q.ws_counters = round_up((size_t)q.tiles_n * sizeof(uint32_t), 256);
+        }
+    } else {
+        if (pr.split_k > 1) return GE_ERR_SHAPE;
+        q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n);
+        const TileShape* t = find_tile(q.tile_id);
+        const int64_t tm = ceil_div(d.m, t->bm), tn = ceil_div(d.n, t->bn);
+        if (tm * tn > INT32_MAX) return GE_ERR_SHAPE;
+        q.tiles_m = (int32_t)tm;
+        q.tiles_n = (int32_t)tn;
+        q.group_m = (int32_t)(tm < 8 ? (tm > 0 ? tm : 1) : 8);
+        q.grid = (unsigned)(tm * tn);
+        q.k_per_split = (int32_t)d.k;
+    }
+    q.ws_c = q.unfused ? round_up((size_t)d.m * (size_t)d.ldd * elem_size(d.d_type), 256) : 0;
+    q.planned = true;
+    *h = q;
+    return GE_OK;
+}
+
+int gemm_epilog_workspace_size(ge_handle h, size_t* bytes) {
+    if (!h || !bytes) return GE_ERR_NULL;
+    if (!h->planned) return GE_ERR_STATE;
+    *bytes = h->ws_c + h->ws_partial + h->ws_counters;
+    return GE_OK;
+}
+
+int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
+    if (!h || !ld_bits) return GE_ERR_NULL;
+    *ld_bits = (int64_t)round_up((size_t)h->d.n, 128);
+    return GE_OK;
+}
+
+int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                        const float* scale_a, const float* scale_b, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (!h) return GE_ERR_NULL;
+    if (!h->planned) return GE_ERR_STATE;
+    const ge_desc& d = h->d;
+    // a pointer may be NULL only when its buffer holds no elements
+    if ((!A && d.m * d.k > 0) || (!B && d.k * d.n > 0) || (!D && d.m * d.n > 0)) return GE_ERR_NULL;
+    const int64_t bias_len = h->axis == GE_BIAS_ROW ? d.m : d.n;
+    if (h->epilog != GE_EPILOG_NONE && !bias && bias_len > 0) return GE_ERR_NULL;
+    const bool want_aux = h->epilog == GE_EPILOG_RELU_AUX_BIAS && d.m > 0;
+    if (aux && h->epilog != GE_EPILOG_RELU_AUX_BIAS) return GE_ERR_EPILOG;
+    if (want_aux && !aux) return GE_ERR_EPILOG;
+    if (d.a_type != GE_F8_E4M3 && (scale_a || scale_b)) return GE_ERR_DTYPE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||
+        !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
+        return GE_ERR_ALIGN;
+    const size_t need = h->ws_c + h->ws_partial + h->ws_counters;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GE_ERR_WORKSPACE;
+    if (test_fail_launch()) return GE_ERR_HIP;
+    if (d.m == 0 || d.n == 0) return GE_OK;   // empty output: nothing to compute
+
+    KernelArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = A;
+    a.B = B;
+    a.bias = bias;
+    a.D = D;
+    a.aux = (uint32_t*)aux;
+    a.scale_a = scale_a;
+    a.scale_b = scale_b;
+    a.m = (int32_t)d.m;
+    a.n = (int32_t)d.n;
+    a.k = (int32_t)d.k;
+    a.epilog = h->epilog;
+    a.axis = h->axis;
+    a.ldaux = (int32_t)h->ldaux;
+    a.lda = d.lda;
+    a.ldb = d.ldb;
+    a.ldd = d.ldd;
+    a.tiles_m = h->tiles_m;
+    a.tiles_n = h->tiles_n;
+    a.group_m = h->group_m;
+    a.split_k = h->split_k;
+    a.k_per_split = h->k_per_split;
+    uint8_t* ws = (uint8_t*)workspace;
+    if (h->split_k > 1) {
+        a.partial = (float*)(ws + h->ws_c);
+        a.counters = (uint32_t*)(ws + h->ws_c + h->ws_partial);
+        if (hipMemsetAsync(a.counters, 0, h->ws_counters, (hipStream_t)stream) != hipSuccess) return GE_ERR_HIP;
+    }
+
+    KernelArgs k1 = a;
+    if (h->unfused) {
+        // kernel 1: the plain product, rounded to d_type, into the workspace
+        k1.epilog = GE_EPILOG_NONE;
+        k1.bias = nullptr;
+        k1.aux = nullptr;
+        k1.ldaux = 0;
+        k1.D = ws;
+    }
+    int err;
+    if (h->path == PATH_SMALLM)
+        err = launch_smallm(d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
+    else
+        err = launch_tile(h->tile_id, d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
+    if (err != 0) return GE_ERR_HIP;
+    if (h->unfused) {
+        // kernel 2: D = act(C + bias) (+ mask)
+        err = launch_elementwise(d.d_type, a, ws, stream);
+        if (err != 0) return GE_ERR_HIP;
+    }
+    return GE_OK;
+}
+
+int gemm_epilog_free(ge_handle h) {
+    delete h;
+    return GE_OK;
+}
+
+const char* gemm_epilog_status_string(int s) {
+    switch (s) {
+    case GE_OK: return "GE_OK: success";
+    case GE_ERR_NULL: return "GE_ERR_NULL: a required pointer is NULL";
+    case GE_ERR_SHAPE: return "GE_ERR_SHAPE: invalid dimension, leading dimension or plan option";
+    case GE_ERR_DTYPE: return "GE_ERR_DTYPE: unsupported or mismatched dtypes";
+    case GE_ERR_EPILOG: return "GE_ERR_EPILOG: invalid epilogue, bias axis or aux buffer";
+    case GE_ERR_ALIGN: return "GE_ERR_ALIGN: pointer or row stride not 16-byte aligned";
+    case GE_ERR_STATE: return "GE_ERR_STATE: handle not planned";
+    case GE_ERR_WORKSPACE: return "GE_ERR_WORKSPACE: workspace missing or too small";
+    case GE_ERR_HIP: return "GE_ERR_HIP: kernel launch failed";
+    case GE_ERR_ALLOC: return "GE_ERR_ALLOC: host allocation failed";
+    }
+    return "unknown status";
+}
+
+int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
+    if (!h || !buf) return GE_ERR_NULL;
+    if (cap == 0) return GE_OK;
+    const ge_desc& d = h->d;
+    if (!h->planned) {
+        snprintf(buf, cap, "m=%lld n=%lld k=%lld unplanned", (long long)d.m, (long long)d.n, (long long)d.k);
+        return GE_OK;
+    }
+    const TileShape* t = find_tile(h->tile_id);
+    snprintf(buf, cap,
+             "m=%lld n=%lld k=%lld a=%d d=%d op_b=%d epilog=%d axis=%d path=%s tile=%dx%d waves=%dx%d "
+             "grid=%u group_m=%d split_k=%d unfused=%d workspace=%zu ldaux_words=%lld",
+             (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
+             h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
+             t ? t->wn : 8, h->grid, h->group_m, h->split_k, h->unfused,
+             h->ws_c + h->ws_partial + h->ws_counters, (long long)h->ldaux);
+    return GE_OK;
+}
+
+}  // extern "C"

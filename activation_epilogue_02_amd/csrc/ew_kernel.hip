@@ -1,0 +1,84 @@
+// ew_kernel.hip -- the second kernel of the unfused pair: D = act(C + bias)
+// (+ ReLU sign mask), reading back the product C that the first kernel (the
+// tile or small-m kernel with no epilogue) stored in D's dtype.
+//
+// This is the separate elementwise pass that epilogue fusion removes (epilog
+// page, first body paragraph: the two-kernel form writes the intermediate to
+// memory and reads it back).  It exists to measure the fusion gain and to
+// cross-check the fused kernels.  HBM-bound: one thread per 32 columns of a
+// row (one mask word), 16-byte loads and stores.
+#include "ge_device.h"
+
+namespace ge {
+
+template <int DT>
+__global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int words = p.ldaux > 0 ? p.ldaux : (p.n + 31) / 32;   // work items per row
+    const int64_t row = t / words;
+    const int w = (int)(t - row * words);
+    if (row >= p.m) return;
+    const int n0 = w * 32;
+    const int ep = p.epilog;
+    const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+    if (n0 >= p.n) {
+        if (want_aux) p.aux[row * p.ldaux + w] = 0u;   // row padding
+        return;
+    }
+    const bool row_bias = p.axis == GE_BIAS_ROW;
+    const float brow = row_bias ? load_scalar<DT>(p.bias, row) : 0.0f;
+    uint32_t bits = 0;
+    const int64_t base = row * p.ldd;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int nc = n0 + 8 * g;
+        if (nc >= p.n) break;
+        const bool full = nc + 8 <= p.n;
+        float x[8], b[8];
+        if (full) {
+            load8<DT>(c, base + nc, x);
+            if (!row_bias) load8<DT>(p.bias, nc, b);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x[j] = (nc + j < p.n) ? load_scalar<DT>(c, base + nc + j) : 0.0f;
+                b[j] = (!row_bias && nc + j < p.n) ? load_scalar<DT>(p.bias, nc + j) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float pre = x[j] + (row_bias ? brow : b[j]);
+            if (want_aux && pre > 0.0f && nc + j < p.n) bits |= 1u << (8 * g + j);
+            x[j] = activate(ep, pre);
+        }
+        if (full) store8<DT>(p.D, base + nc, x);
+        else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (nc + j < p.n) store_one<DT>(p.D, base + nc + j, x[j]);
+        }
+    }
+    if (want_aux) p.aux[row * p.ldaux + w] = bits;
+}
+
+int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* stream) {
+    const int words = args.ldaux > 0 ? args.ldaux : (args.n + 31) / 32;
+    const int64_t items = (int64_t)args.m * words;
+    const unsigned grid = (unsigned)((items + 255) / 256);
+    switch (d_type) {
+    case GE_F32:
+        hipLaunchKernelGGL(ge_ew_kernel<GE_F32>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        break;
+    case GE_F16:
+        hipLaunchKernelGGL(ge_ew_kernel<GE_F16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        break;
+    case GE_BF16:
+        hipLaunchKernelGGL(ge_ew_kernel<GE_BF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        break;
+    default:
+        return (int)hipErrorInvalidDeviceFunction;
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace ge

@@ -1,0 +1,149 @@
+// ge_device.h -- device-side helpers shared by the gfx950 kernels: vector
+// types, element-type traits, output conversion and the epilogue activations.
+//
+// Pages cited: see include/gemm_epilog.h for the page list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ge_params.h"
+
+namespace ge {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Element-type traits, indexed by the ABI's ge_dtype value.
+template <int DT> struct Elem;
+template <> struct Elem<GE_F32>     { typedef float    T; static constexpr int size = 4; };
+template <> struct Elem<GE_F16>     { typedef uint16_t T; static constexpr int size = 2; };
+template <> struct Elem<GE_BF16>    { typedef uint16_t T; static constexpr int size = 2; };
+template <> struct Elem<GE_F8_E4M3> { typedef uint8_t  T; static constexpr int size = 1; };
+
+// ---- reading scalars of an output-typed vector (bias) ----------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+    _Float16 h;
+    uint16_t s = (uint16_t)b;
+    __builtin_memcpy(&h, &s, 2);
+    return (float)h;
+}
+
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
+    if constexpr (DT == GE_F32) return ((const float*)p)[i];
+    else if constexpr (DT == GE_BF16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+    else return f16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+// ---- fp32 -> output conversion, round to nearest even -----------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 b = (__bf16)x;  // gfx950: hardware RNE conversion
+    uint16_t r;
+    __builtin_memcpy(&r, &b, 2);
+    return r;
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;  // RNE (default rounding mode)
+    uint16_t r;
+    __builtin_memcpy(&r, &h, 2);
+    return r;
+}
+
+// Pack 8 fp32 values into 16 bytes of 16-bit outputs.
+template <int DT>
+__device__ __forceinline__ u32x4 pack8_16bit(const float* v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo, hi;
+        if constexpr (DT == GE_BF16) {
+            lo = f32_to_bf16_bits(v[2 * i]);
+            hi = f32_to_bf16_bits(v[2 * i + 1]);
+        } else {
+            lo = f32_to_f16_bits(v[2 * i]);
+            hi = f32_to_f16_bits(v[2 * i + 1]);
+        }
+        r[i] = lo | (hi << 16);
+    }
+    return r;
+}
+
+// Store one converted element.
+template <int DT>
+__device__ __forceinline__ void store_one(void* D, int64_t idx, float v) {
+    if constexpr (DT == GE_F32) ((float*)D)[idx] = v;
+    else if constexpr (DT == GE_BF16) ((uint16_t*)D)[idx] = f32_to_bf16_bits(v);
+    else ((uint16_t*)D)[idx] = f32_to_f16_bits(v);
+}
+
+// Store 8 consecutive converted elements (16-byte aligned for 16-bit types,
+// 32-byte span for fp32).
+template <int DT>
+__device__ __forceinline__ void store8(void* D, int64_t idx, const float* v) {
+    if constexpr (DT == GE_F32) {
+        u32x4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { a[i] = __float_as_uint(v[i]); b[i] = __float_as_uint(v[4 + i]); }
+        u32x4* p = (u32x4*)((float*)D + idx);
+        p[0] = a;
+        p[1] = b;
+    } else {
+        *(u32x4*)((uint16_t*)D + idx) = pack8_16bit<DT>(v);
+    }
+}
+
+// Load 8 consecutive bias values (aligned as store8).
+template <int DT>
+__device__ __forceinline__ void load8(const void* p, int64_t idx, float* v) {
+    if constexpr (DT == GE_F32) {
+        const u32x4* q = (const u32x4*)((const float*)p + idx);
+        u32x4 a = q[0], b = q[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(a[i]); v[4 + i] = __uint_as_float(b[i]); }
+    } else {
+        u32x4 a = *(const u32x4*)((const uint16_t*)p + idx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == GE_BF16) {
+                v[2 * i] = bf16_bits_to_f32(a[i] & 0xffffu);
+                v[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+            } else {
+                v[2 * i] = f16_bits_to_f32(a[i] & 0xffffu);
+                v[2 * i + 1] = f16_bits_to_f32(a[i] >> 16);
+            }
+        }
+    }
+}
+
+// ---- activations -------------------------------------------------------------
+// GELU in its tanh form, 0.5 x (1 + tanh(u)) with u = sqrt(2/pi)(x + 0.044715 x^3).
+// Since 0.5 (1 + tanh u) = 1 / (1 + e^{-2u}), this is x / (1 + 2^{-2u log2 e}),
+// evaluated with the hardware base-2 exponential and reciprocal (v_exp_f32,
+// v_rcp_f32).  Large |u| saturates correctly: e^{-2u} -> inf gives -0/+0,
+// e^{-2u} -> 0 gives x.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k0 = 0.7978845608028654f;          // sqrt(2/pi)
+    const float k1 = 0.044715f;
+    const float m2log2e = -2.0f * 1.4426950408889634f;
+    float u = k0 * (x + k1 * x * x * x);
+    float e = __builtin_amdgcn_exp2f(m2log2e * u);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Apply the activation of an epilogue to a pre-activation value.
+__device__ __forceinline__ float activate(int epilog, float x) {
+    if (epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS) return x > 0.0f ? x : 0.0f;
+    if (epilog == GE_EPILOG_GELU_BIAS) return gelu_tanh(x);
+    return x;
+}
+
+}  // namespace ge

@@ -1,0 +1,60 @@
+// ge_params.h -- kernel argument block and launch-table interface shared by
+// the C-ABI front end (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gemm_epilog.h"
+
+namespace ge {
+
+// Everything a kernel needs, passed by value as the kernel argument.
+struct KernelArgs {
+    const void* A;
+    const void* B;
+    const void* bias;      // NULL for GE_EPILOG_NONE
+    void* D;
+    uint32_t* aux;         // NULL unless RELU_AUX_BIAS
+    const float* scale_a;  // NULL = 1.0
+    const float* scale_b;  // NULL = 1.0
+    float* partial;        // split-K fp32 partials (small-m path), or NULL
+    uint32_t* counters;    // split-K arrival counters (small-m path), or NULL
+    int32_t m, n, k;
+    int32_t epilog, axis;
+    int32_t ldaux;         // mask row stride in 32-bit words
+    int64_t lda, ldb, ldd;
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;       // tile-rows per group in the launch order
+    int32_t split_k;       // K slices (small-m path)
+    int32_t k_per_split;   // K elements per slice, multiple of the k step
+};
+
+// Kernel families.
+enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
+
+// Tile shapes of the MFMA tile kernel: block tile BM x BN, waves WM x WN.
+struct TileShape {
+    int32_t id, bm, bn, wm, wn;
+};
+constexpr int kNumTiles = 4;
+constexpr TileShape kTiles[kNumTiles] = {
+    {1, 64, 64, 2, 2},     // 4 waves, 32 x 32 per wave
+    {2, 128, 128, 2, 2},   // 4 waves, 64 x 64 per wave
+    {3, 256, 256, 2, 2},   // 4 waves, 128 x 128 per wave
+    {4, 256, 128, 2, 2},   // 4 waves, 128 x 64 per wave
+};
+
+// Launch one fused (or NONE-epilogue) tile-kernel GEMM.  Returns a hipError_t.
+int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs& args,
+                unsigned grid, void* stream);
+
+// Launch the small-m streaming kernel.
+int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid,
+                  void* stream);
+
+// Launch the unfused pair's elementwise kernel: D = act(C + bias) (+ mask),
+// reading C (d_type, leading dimension ldd) from `c`.
+int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* stream);
+
+}  // namespace ge

@@ -1,0 +1,186 @@
+// smallm_kernel.hip -- fused GEMM + epilogue for small batches (m <= 16),
+// the bandwidth-bound Linear shape y = act(x W^T + b) with W given n x k.
+//
+// At m <= 16 every weight element is used at most 16 times, so the kernel is
+// bound by streaming W from HBM once; the epilogue is fused as in the tile
+// kernel (the small-batch, latency-sensitive case the nvmath page's
+// paragraph on the BIAS epilog singles out; the NVGEMM page's
+// Linear(4096,4096)+GELU example at batch 16).
+//
+// Design:
+//  * One workgroup per 16 output columns (16 rows of W) and K slice; its
+//    waves split the slice further.  Lane (r = lane % 16, q = lane / 16)
+//    streams 16-byte chunks of W row n0 + r straight from global memory into
+//    the A operand of v_mfma_f32_16x16x32_{f16,bf16}; the matching chunk of
+//    x row r (L2-resident, read by every workgroup) is the B operand.  Each
+//    lane's chunks for one MFMA step cover 32 consecutive K values of its row
+//    together with the other three q lanes, so each step reads 64 contiguous
+//    bytes per W row.
+//  * Loads are issued `kUnroll` steps ahead of the MFMAs that consume them to
+//    keep enough bytes in flight per CU.
+//  * The waves' partial 16 x 16 blocks are reduced in LDS in a fixed order.
+//    With split_k > 1 the per-slice sums go to an fp32 workspace and the last
+//    workgroup to arrive for a column block (arrival counter, then a device-
+//    scope fence) adds the slices in slice order, so results are
+//    deterministic; it re-arms the counter for the next launch.  The bias,
+//    activation, mask and the single store run once, after the full K sum.
+#include "ge_device.h"
+
+namespace ge {
+
+constexpr int kSmWaves = 8;
+constexpr int kUnroll = 8;
+
+template <int DIN, int DOUT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (DIN == GE_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 16-byte chunk of 8 16-bit elements at (row, col) with bounds (nrows, ncols).
+__device__ __forceinline__ u32x4 sm_load(const uint16_t* base, int64_t ld, int row, int nrows, int col,
+                                         int ncols) {
+    if (row >= nrows || col >= ncols) return u32x4{0, 0, 0, 0};
+    const uint16_t* p = base + (int64_t)row * ld + col;
+    if (col + 8 <= ncols) return __builtin_nontemporal_load((const u32x4*)p);
+    uint16_t t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (col + e < ncols) ? p[e] : (uint16_t)0;
+    u32x4 r;
+    __builtin_memcpy(&r, t, 16);
+    return r;
+}
+
+template <int DIN, int DOUT>
+__global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) {
+    __shared__ f32x4 red[kSmWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int nblk = blockIdx.x % p.tiles_n;   // column block
+    const int slice = blockIdx.x / p.tiles_n;  // K slice
+    const int n0 = nblk * 16;
+    const int M = p.m, N = p.n, K = p.k;
+    const uint16_t* W = (const uint16_t*)p.B;
+    const uint16_t* X = (const uint16_t*)p.A;
+
+    // this wave's K range: the slice split evenly over the waves, in steps of 32
+    const int ks = slice * p.k_per_split;
+    const int ke = min(K, ks + p.k_per_split);
+    const int steps_total = (ke - ks + 31) / 32;
+    const int per_wave = (steps_total + kSmWaves - 1) / kSmWaves;
+    const int s_begin = wave * per_wave;
+    const int s_end = min(steps_total, s_begin + per_wave);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = s_begin; s0 < s_end; s0 += kUnroll) {
+        u32x4 wv[kUnroll], xv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int kc = ks + (s0 + u) * 32 + q * 8;
+            const bool ok = s0 + u < s_end;
+            wv[u] = ok ? sm_load(W, p.ldb, n0 + r, N, kc, ke) : u32x4{0, 0, 0, 0};
+            xv[u] = ok ? sm_load(X, p.lda, r, M, kc, ke) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc = mfma16<DIN, DOUT>(wv[u], xv[u], acc);
+    }
+    // acc: lane holds rows n0 + 4q + i (i = 0..3) of column m = r of y^T
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kSmWaves; ++w) sum += red[w][lane];
+
+    if (p.split_k > 1) {
+        // publish this slice's partial, then let the last arriver finish
+        float* part = p.partial + ((int64_t)slice * p.tiles_n + nblk) * 256;
+        *(f32x4*)(part + lane * 4) = sum;
+        __threadfence();
+        int prev = 0;
+        if (lane == 0) prev = (int)atomicAdd(&p.counters[nblk], 1u);
+        prev = __shfl(prev, 0);
+        if (prev != p.split_k - 1) return;
+        __threadfence();
+        sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sl = 0; sl < p.split_k; ++sl) {
+            const float* ps = p.partial + ((int64_t)sl * p.tiles_n + nblk) * 256 + lane * 4;
+            sum += __builtin_nontemporal_load((const f32x4*)ps);
+        }
+        if (lane == 0) p.counters[nblk] = 0u;   // re-arm for the next launch
+    }
+
+    float s = 1.0f;
+    const int ep = p.epilog;
+    const bool has_bias = ep != GE_EPILOG_NONE;
+    const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+    const int m = r;
+    const bool mok = m < M;
+    float v[4];
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 4 * q + i;
+        float b = 0.0f;
+        if (has_bias && n < N && (p.axis == GE_BIAS_COL)) b = load_scalar<DOUT>(p.bias, n);
+        if (has_bias && p.axis == GE_BIAS_ROW && mok) b = load_scalar<DOUT>(p.bias, m);
+        const float x = sum[i] * s + b;
+        if (want_aux && x > 0.0f && n < N) bits |= 1u << (4 * q + i);
+        v[i] = activate(ep, x);
+    }
+    if (mok) {
+        const int n = n0 + 4 * q;
+        const int64_t idx = (int64_t)m * p.ldd + n;
+        if (n + 4 <= N) {
+            if constexpr (DOUT == GE_F32) {
+                *(f32x4*)((float*)p.D + idx) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+                uint32_t lo, hi;
+                if constexpr (DOUT == GE_BF16) {
+                    lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+                    hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+                } else {
+                    lo = f32_to_f16_bits(v[0]) | ((uint32_t)f32_to_f16_bits(v[1]) << 16);
+                    hi = f32_to_f16_bits(v[2]) | ((uint32_t)f32_to_f16_bits(v[3]) << 16);
+                }
+                *(u32x2*)((uint16_t*)p.D + idx) = u32x2{lo, hi};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n + i < N) store_one<DOUT>(p.D, idx + i, v[i]);
+        }
+    }
+    if (want_aux) {
+        // 16 bits per row per column block: one half-word of the mask row
+        bits |= (uint32_t)__shfl_xor((int)bits, 16);
+        bits |= (uint32_t)__shfl_xor((int)bits, 32);
+        uint16_t* aux16 = (uint16_t*)p.aux;
+        const int64_t row_hw = (int64_t)p.ldaux * 2;   // half-words per mask row
+        if (q == 0 && mok) aux16[(int64_t)m * row_hw + nblk] = (uint16_t)bits;
+        // the last column block also clears the row's padding half-words
+        if (nblk == p.tiles_n - 1 && q == 0 && mok) {
+            for (int64_t hw = nblk + 1; hw < row_hw; ++hw) aux16[(int64_t)m * row_hw + hw] = 0;
+        }
+    }
+}
+
+typedef void (*SmFn)(KernelArgs);
+
+int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid, void* stream) {
+    if (op_b != GE_OP_T) return (int)hipErrorInvalidDeviceFunction;
+    SmFn fn = nullptr;
+    if (a_type == GE_F16 && d_type == GE_F16) fn = ge_smallm_kernel<GE_F16, GE_F16>;
+    else if (a_type == GE_F16 && d_type == GE_F32) fn = ge_smallm_kernel<GE_F16, GE_F32>;
+    else if (a_type == GE_BF16 && d_type == GE_BF16) fn = ge_smallm_kernel<GE_BF16, GE_BF16>;
+    else if (a_type == GE_BF16 && d_type == GE_F32) fn = ge_smallm_kernel<GE_BF16, GE_F32>;
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSmWaves * 64), 0, (hipStream_t)stream, args);
+    return (int)hipGetLastError();
+}
+
+}  // namespace ge

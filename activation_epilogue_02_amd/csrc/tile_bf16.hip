@@ -1,0 +1,12 @@
+// tile_bf16.hip -- instantiations of the MFMA tile kernel for bf16 inputs.
+#include "tile_kernel.h"
+
+namespace ge {
+
+TileFn pick_tile_bf16(int d_type, int op_b, int tile_id) {
+    if (d_type == GE_BF16) return pick_op<GE_BF16, GE_BF16>(op_b, tile_id);
+    if (d_type == GE_F32) return pick_op<GE_BF16, GE_F32>(op_b, tile_id);
+    return nullptr;
+}
+
+}  // namespace ge

@@ -1,0 +1,210 @@
+/*
+ * gemm_epilog.h -- fused GEMM + bias/activation epilogue for AMD MI355X (gfx950).
+ *
+ *   D = epilogue(scale_a*scale_b * A*B + bias)
+ *
+ * computed in ONE kernel: the bias broadcast-add, the activation (ReLU or
+ * GELU) and the optional ReLU sign-mask output are applied to the fp32
+ * accumulators while they are still in registers, so the pre-activation
+ * matrix is never written to memory and read back.
+ *
+ * Pages cited:
+ *   [cuBLASLt page] "PyTorch inference: cuBLASLt bias fusion optimization"
+ *                   (blog.hotdry.top, 2025-09-22)
+ *   [nvmath page]   "nvmath-python cuBLASLt bias fusion for PyTorch inference"
+ *                   (blog.hotdry.top, 2025-09-22)
+ *   [epilog page]   "Explaining how nvmath-python's epilog mechanism
+ *                   configures parameters to fuse the bias add into the
+ *                   cuBLASLt matmul kernel" (blog.hotdry.top, 2025-09-22)
+ *   [NVGEMM page]   "PyTorch 2.14 NVGEMM epilogue fusion" (zdabc.icu)
+ *
+ * Life cycle (the stateful create -> plan -> execute -> free object of the
+ * nvmath page, paragraph on the workflow, and of the epilog page, paragraphs
+ * on Matmul.plan's epilog and epilog_inputs arguments):
+ *
+ *   gemm_epilog_create   describe the problem (shapes, dtypes, layouts)
+ *   gemm_epilog_plan     choose the epilogue and bias axis; the planner picks
+ *                        the kernel, tile and launch shape (host-only work,
+ *                        done once, kept apart from the steady-state calls)
+ *   gemm_epilog_execute  launch asynchronously on a HIP stream (any number of
+ *                        times, from any thread, on any stream)
+ *   gemm_epilog_free     release the host-side plan
+ *
+ * Conventions, all calls:
+ *   - Matrices are row-major.  A is m x k with leading dimension lda.  B is
+ *     k x n (op_b = GE_OP_N, ldb >= n) or, for a Linear layer's weight, n x k
+ *     (op_b = GE_OP_T, ldb >= k).  D is m x n with leading dimension ldd.
+ *     Leading dimensions are in elements.
+ *   - Every buffer passed to execute is a DEVICE pointer owned by the caller.
+ *     The library never allocates, frees, copies or synchronises.
+ *   - Status codes are returned, never thrown; a call that fails leaves no
+ *     state behind and launches nothing.  All validation happens before any
+ *     HIP runtime call.
+ *   - A planned handle is immutable: concurrent executes on different
+ *     streams are safe.  free() touches only host memory and is safe while
+ *     kernels launched from the handle are still running.
+ */
+#ifndef GEMM_EPILOG_H
+#define GEMM_EPILOG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+enum {
+    GE_OK = 0,
+    GE_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    GE_ERR_SHAPE = 2,     /* m, n or k < 0, a leading dimension too small, a
+                             dimension beyond 2^31-1, or an unknown plan option */
+    GE_ERR_DTYPE = 3,     /* unsupported or mismatched dtype combination        */
+    GE_ERR_EPILOG = 4,    /* unknown epilogue / axis, or aux buffer missing for
+                             RELU_AUX_BIAS / given for any other epilogue, or
+                             bias missing when the epilogue needs one           */
+    GE_ERR_ALIGN = 5,     /* a pointer or a row stride is not 16-byte aligned   */
+    GE_ERR_STATE = 6,     /* execute on a handle that has not been planned      */
+    GE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than workspace_size      */
+    GE_ERR_HIP = 8,       /* the kernel launch failed (HIP error)               */
+    GE_ERR_ALLOC = 9      /* host memory for the handle could not be allocated  */
+};
+
+/* ---- element types ---------------------------------------------------------
+ * fp16 = IEEE binary16; bf16 = bfloat16; e4m3 = OCP 8-bit float E4M3 (max
+ * 448, no infinities), the fp8 format of gfx950's matrix cores.  All products
+ * accumulate in fp32 (the 32-bit compute type of the cuBLASLt page,
+ * paragraph 3). */
+typedef enum { GE_F32 = 0, GE_F16 = 1, GE_BF16 = 2, GE_F8_E4M3 = 3 } ge_dtype;
+
+typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op;
+
+/* Epilogues, as the epilog page's paragraph on the epilog enum lists them
+ * (BIAS, RELU_BIAS, RELU_AUX_BIAS), plus NONE and GELU_BIAS (GELU is named
+ * as a fused activation on the cuBLASLt page, paragraph 2, and in the NVGEMM
+ * page's section on why epilogue fusion matters).  With P the pre-activation
+ * (the scaled product plus bias):
+ *   NONE           D = s*A*B                        (no bias read)
+ *   BIAS           D = P
+ *   RELU_BIAS      D = max(P, 0)
+ *   RELU_AUX_BIAS  D = max(P, 0), and aux bit (i,j) = (P[i][j] > 0)
+ *   GELU_BIAS      D = 0.5 P (1 + tanh(sqrt(2/pi) (P + 0.044715 P^3)))
+ * Conversion of the fp32 result to D's dtype rounds to nearest even. */
+typedef enum {
+    GE_EPILOG_NONE = 0,
+    GE_EPILOG_BIAS = 1,
+    GE_EPILOG_RELU_BIAS = 2,
+    GE_EPILOG_RELU_AUX_BIAS = 3,
+    GE_EPILOG_GELU_BIAS = 4
+} ge_epilog;
+
+/* Bias broadcast axis.
+ * ROW: m values (shape (m,) or (m,1)); bias[i] is added to every column of
+ *      row i -- the epilog page's paragraph on epilog_inputs.
+ * COL: n values (shape (1,n)); bias[j] is added to every row of column j --
+ *      the nvmath page's paragraph on shape constraints; a Linear layer. */
+typedef enum { GE_BIAS_ROW = 0, GE_BIAS_COL = 1 } ge_bias_axis;
+
+/* Problem description.  Supported dtype combinations (a_type == b_type):
+ *   F32  inputs -> d_type F32
+ *   F16  inputs -> d_type F16 or F32
+ *   BF16 inputs -> d_type BF16 or F32
+ *   E4M3 inputs -> d_type BF16, F16 or F32
+ * bias_type must equal d_type (for every epilogue): there is no implicit
+ * conversion (nvmath page, paragraph on dtype agreement). */
+typedef struct {
+    int64_t m, n, k;
+    int32_t a_type, b_type, d_type, bias_type; /* ge_dtype */
+    int32_t op_b;                              /* ge_op (op_a is always N) */
+    int32_t reserved;                          /* must be 0 */
+    int64_t lda, ldb, ldd;                     /* in elements */
+} ge_desc;
+
+/* Planner preferences (all 0 = automatic).
+ * path:    0 auto, 1 tile kernel, 2 small-m (batch <= 16) streaming kernel
+ * unfused: 1 = run the unfused pair instead of the fused kernel: the GEMM
+ *          with no epilogue writes the product, rounded to d_type, into the
+ *          workspace; a second, elementwise kernel reads it back, adds the
+ *          bias, applies the activation and writes D (and the mask).  This is
+ *          the two-kernel sequence that fusion removes (epilog page, first
+ *          body paragraph), kept for measurement and cross-checking.
+ * tile:    0 auto, else a tile id from gemm_epilog_describe's list
+ * split_k: 0 auto, else the number of K slices (small-m path only) */
+typedef struct {
+    int32_t path;
+    int32_t unfused;
+    int32_t tile;
+    int32_t split_k;
+} ge_pref;
+
+typedef struct ge_plan_s* ge_handle;
+
+/* Create a handle for a problem.  Degenerate sizes are valid: m == 0 or
+ * n == 0 makes execute a validated no-op; k == 0 gives D = act(bias) (the
+ * product of empty operands is zero).  Validates shapes (m, n, k >= 0; lda >= k;
+ * ldb >= n for N or >= k for T; ldd >= n), dtypes, and that every row
+ * stride is a multiple of 16 bytes (epilog page, paragraph on epilog_inputs:
+ * tensors must be 16-byte aligned).  On success *h owns host memory only.
+ * Errors: GE_ERR_NULL, GE_ERR_SHAPE, GE_ERR_DTYPE, GE_ERR_ALIGN,
+ * GE_ERR_ALLOC. */
+int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
+
+/* Choose the epilogue and bias axis and plan the launch (kernel, tile, grid,
+ * workspace).  p may be NULL.  May be called again to re-plan.
+ * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis),
+ * GE_ERR_SHAPE (an unknown tile id or split in p). */
+int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* p);
+
+/* Bytes of device workspace execute() needs (0 for the fused paths; m*ldd
+ * elements of d_type, rounded up to 256 bytes, for the unfused pair).
+ * Errors: GE_ERR_NULL, GE_ERR_STATE (not planned). */
+int gemm_epilog_workspace_size(ge_handle h, size_t* bytes);
+
+/* Row stride of the aux mask in bits: round_up(n, 128), so each row starts
+ * 16-byte aligned.  The mask is a row-major bit matrix of m rows: bit (i,j)
+ * is bit j%32 of the little-endian 32-bit word at word index
+ * i*(ld_bits/32) + j/32.  Bits j >= n of a row are written as 0.  The
+ * buffer must hold m*ld_bits/8 bytes.  Errors: GE_ERR_NULL. */
+int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits);
+
+/* Launch the planned computation on `stream` (a hipStream_t; NULL = the
+ * null stream).  Asynchronous: returns once the kernel(s) are queued.
+ *   A, B     device operands (see ge_desc)
+ *   bias     device vector of m (ROW) or n (COL) bias_type values; NULL
+ *            only for GE_EPILOG_NONE
+ *   D        device output, m x n with leading dimension ldd
+ *   aux      device mask buffer (see gemm_epilog_aux_ld); required for
+ *            RELU_AUX_BIAS, must be NULL otherwise
+ *   scale_a, scale_b
+ *            device pointers to one fp32 each, the per-tensor dequantisation
+ *            factors of fp8 inputs (D uses scale_a*scale_b*A*B); NULL means
+ *            1.0.  Must be NULL for non-fp8 inputs.
+ *   workspace, workspace_bytes
+ *            device scratch of at least gemm_epilog_workspace_size bytes
+ *            (may be NULL/0 when that size is 0)
+ * A pointer may be NULL only when its buffer holds no elements (e.g. A and B
+ * when k == 0).  Every non-NULL pointer must be 16-byte aligned (scales:
+ * 4-byte).  The
+ * output and aux buffers must not overlap the inputs.
+ * Errors: GE_ERR_NULL, GE_ERR_STATE, GE_ERR_EPILOG, GE_ERR_DTYPE (scales
+ * given for non-fp8 inputs), GE_ERR_ALIGN, GE_ERR_WORKSPACE, GE_ERR_HIP. */
+int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* bias,
+                        void* D, void* aux, const float* scale_a, const float* scale_b,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release the handle (NULL is accepted).  Host-only. */
+int gemm_epilog_free(ge_handle h);
+
+/* Human-readable text for a status code (static storage). */
+const char* gemm_epilog_status_string(int status);
+
+/* Write a one-line description of the plan (path, tile, grid, workspace)
+ * into buf (always NUL-terminated when cap > 0).  Errors: GE_ERR_NULL. */
+int gemm_epilog_describe(ge_handle h, char* buf, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPILOG_H */

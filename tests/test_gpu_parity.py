@@ -1,0 +1,152 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle,
+element by element, on seeded inputs.  Sizes span several tiles with ragged
+tails; every dtype combination, epilogue, bias axis and B layout; padded
+leading dimensions with NaN-poisoned padding (it must never be read, and D's
+padding must never be written); the small-m path with and without split-K;
+the unfused pair; integer-exact inputs (bit-exact); determinism.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import check_full, codes, decode_output, rel_fro, run_library, tolerance
+
+pytestmark = pytest.mark.gpu
+
+COMBOS = [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
+          ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
+EPILOGS = ["none", "bias", "relu_bias", "relu_aux_bias", "gelu_bias"]
+
+
+def wl(m, n, k, a, d, ep, axis="row", op_b=0, seed=7, **kw):
+    base = synth.Workload("t", "test", m, n, k, a, d, ep, axis, op_b, seed,
+                          ("normal", 1.0), ("normal", 1.0), ("normal", 1.0))
+    return synth.scaled(base, **kw) if kw else base
+
+
+def case_id(*a):
+    return "-".join(str(x) for x in a)
+
+
+@pytest.mark.parametrize("a,d", COMBOS, ids=[f"{a}->{d}" for a, d in COMBOS])
+@pytest.mark.parametrize("ep", EPILOGS)
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_tile_all_combos_ragged(a, d, ep, axis, op_b):
+    # 150 x 200 x 136: three 64-row tiles, four 64-column tiles, ragged tails
+    w = wl(150, 200, 136, a, d, ep, axis, op_b)
+    inp = synth.make_inputs(w)
+    r = run_library(w, inp, pad=1, path=1)
+    check_full(w, r)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("a,d", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("e4m3", "bf16")])
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_every_tile_shape(tile, a, d, op_b):
+    # several 256-wide tiles plus tails in m, n and k
+    w = wl(300, 520, 200, a, d, "relu_aux_bias", "row", op_b, seed=11)
+    inp = synth.make_inputs(w)
+    r = run_library(w, inp, pad=2, path=1, tile=tile)
+    check_full(w, r)
+
+
+@pytest.mark.parametrize("k", [1, 5, 37, 64, 65, 127])
+@pytest.mark.parametrize("a", ["bf16", "f32", "e4m3"])
+def test_ragged_k_with_poisoned_padding(k, a):
+    d = "bf16" if a == "e4m3" else a
+    for op_b in (0, 1):
+        w = wl(70, 90, k, a, d, "gelu_bias", "col", op_b, seed=k)
+        r = run_library(w, synth.make_inputs(w), pad=1, path=1)
+        check_full(w, r)
+
+
+def test_zero_k_gives_activated_bias():
+    w = wl(40, 72, 0, "bf16", "f32", "gelu_bias", "col")
+    inp = synth.make_inputs(w)
+    r = run_library(w, inp, path=1, lda=8, ldb=72)
+    check_full(w, r)
+
+
+def test_empty_output_is_noop():
+    w = wl(0, 64, 32, "bf16", "bf16", "bias", "row")
+    inp = synth.make_inputs(w)
+    r = run_library(w, inp, path=1)
+    assert r.D.numel() == 0
+
+
+@pytest.mark.parametrize("m", [1, 3, 16])
+@pytest.mark.parametrize("n,k", [(48, 40), (1000, 1000), (272, 4096)])
+@pytest.mark.parametrize("a,d", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
+@pytest.mark.parametrize("split", [0, 3])
+def test_smallm_path(m, n, k, a, d, split):
+    for ep in ("gelu_bias", "relu_aux_bias"):
+        for axis in ("col", "row"):
+            w = wl(m, n, k, a, d, ep, axis, op_b=1, seed=m * 1000 + n)
+            r = run_library(w, synth.make_inputs(w), pad=1, path=2, split_k=split)
+            assert "path=smallm" in r.desc
+            check_full(w, r)
+
+
+@pytest.mark.parametrize("a,d", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("e4m3", "bf16")])
+@pytest.mark.parametrize("ep", ["bias", "relu_aux_bias", "gelu_bias"])
+def test_unfused_pair_matches_oracle_and_fused(a, d, ep):
+    w = wl(260, 300, 96, a, d, ep, "row", 0, seed=5)
+    inp = synth.make_inputs(w)
+    ru = run_library(w, inp, pad=1, unfused=1)
+    check_full(w, ru)
+    rf = run_library(w, inp, pad=1)
+    Du, Df = decode_output(w, ru), decode_output(w, rf)
+    # the unfused pair rounds the product to D's dtype before the bias add,
+    # so the two paths agree to about two output roundings
+    assert rel_fro(Du, Df) <= 2 * tolerance(a, d)
+
+
+def test_unfused_smallm():
+    w = wl(16, 512, 1024, "f16", "f16", "gelu_bias", "col", 1)
+    r = run_library(w, synth.make_inputs(w), path=2, unfused=1)
+    check_full(w, r)
+
+
+@pytest.mark.parametrize("a,d", [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("tile", [1, 3])
+def test_integer_inputs_bit_exact(a, d, tile):
+    """Small integers make every fp32 partial sum exact, so D must equal the
+    RNE encoding of the exact result bit for bit, whatever the order."""
+    m, n, k = 512, 384, 1024
+    w = wl(m, n, k, a, d, "relu_bias", "row", 0)
+    inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    if a == "e4m3":   # keep codes exact: unit scales
+        inp.A = torch.clamp(torch.randint(-4, 5, (m, k), generator=torch.Generator().manual_seed(1)).float(),
+                            -4, 4).to(torch.float8_e4m3fn)
+        inp.B = torch.randint(-4, 5, (k, n), generator=torch.Generator().manual_seed(2)).float().to(
+            torch.float8_e4m3fn)
+        inp.scale_a = torch.ones(1)
+        inp.scale_b = torch.ones(1)
+    r = run_library(w, inp, path=1, tile=tile)
+    from parity import oracle_full
+    Y, P, _ = oracle_full(w, r)
+    got = codes(r.D)[:, :n]
+    if d == "f32":
+        want = Y.astype(np.float32)
+    else:
+        want = oracle.encode(Y, d).reshape(Y.shape)
+    assert np.array_equal(got, want)
+
+
+def test_deterministic_bitwise():
+    w = wl(700, 650, 520, "bf16", "bf16", "relu_aux_bias", "row", 0, seed=3)
+    inp = synth.make_inputs(w)
+    r1 = run_library(w, inp)
+    r2 = run_library(w, inp)
+    assert torch.equal(r1.D.view(torch.int16), r2.D.view(torch.int16))
+    assert torch.equal(r1.aux, r2.aux)
+    w2 = wl(16, 4096, 4096, "f16", "f16", "gelu_bias", "col", 1, seed=3)
+    inp2 = synth.make_inputs(w2)
+    r3 = run_library(w2, inp2, split_k=4, path=2)
+    r4 = run_library(w2, inp2, split_k=4, path=2)
+    assert torch.equal(r3.D.view(torch.int16), r4.D.view(torch.int16))
