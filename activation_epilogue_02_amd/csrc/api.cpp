@@ -70,14 +70,27 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // two tiles (256 CUs); below that, the shape with the most tiles.  Large
 // tiles halve the L2 -> LDS traffic per flop; small problems need the
 // parallelism more than the reuse.
-int choose_tile(int64_t m, int64_t n) {
+int choose_tile(int64_t m, int64_t n, int a_type) {
     const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
     const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    if (a_type == GE_F16 || a_type == GE_BF16) {
+        // the pipelined direct-to-LDS kernel
+        if (t256 >= 512) return 5;
+        if (t128 >= 512) return 8;
+        if (t256 >= 256 && t128 < 256) return 5;
+        if (t128 >= 256) return 8;
+        return 1;
+    }
     if (t256 >= 512) return 3;
     if (t128 >= 512) return 2;
     if (t256 >= 256 && t128 < 256) return 3;
     if (t128 >= 256) return 2;
     return 1;
+}
+
+// The pipelined kernel takes 16-bit inputs only.
+bool tile_supports(const TileShape* t, int a_type) {
+    return t->kernel == 1 || a_type == GE_F16 || a_type == GE_BF16;
 }
 
 bool smallm_supported(const ge_desc& d) {
@@ -160,8 +173,9 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         }
     } else {
         if (pr.split_k > 1) return GE_ERR_SHAPE;
-        q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n);
+        q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n, d.a_type);
         const TileShape* t = find_tile(q.tile_id);
+        if (!tile_supports(t, d.a_type)) return GE_ERR_SHAPE;
         const int64_t tm = ceil_div(d.m, t->bm), tn = ceil_div(d.n, t->bn);
         if (tm * tn > INT32_MAX) return GE_ERR_SHAPE;
         q.tiles_m = (int32_t)tm;
@@ -296,10 +310,12 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
     const TileShape* t = find_tile(h->tile_id);
     snprintf(buf, cap,
              "m=%lld n=%lld k=%lld a=%d d=%d op_b=%d epilog=%d axis=%d path=%s tile=%dx%d waves=%dx%d "
-             "grid=%u group_m=%d split_k=%d unfused=%d workspace=%zu ldaux_words=%lld",
+             "tile_id=%d kernel=%d stages=%d grid=%u group_m=%d split_k=%d unfused=%d workspace=%zu "
+             "ldaux_words=%lld",
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
              h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
-             t ? t->wn : 8, h->grid, h->group_m, h->split_k, h->unfused,
+             t ? t->wn : 8, h->tile_id, t ? t->kernel : 0, t ? t->stages : 0, h->grid, h->group_m, h->split_k,
+             h->unfused,
              h->ws_c + h->ws_partial + h->ws_counters, (long long)h->ldaux);
     return GE_OK;
 }

@@ -33,16 +33,23 @@ struct KernelArgs {
 // Kernel families.
 enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 
-// Tile shapes of the MFMA tile kernel: block tile BM x BN, waves WM x WN.
+// Tile shapes of the MFMA tile kernels: block tile BM x BN, waves WM x WN.
+// Kernel 1 (tile_kernel.h): register-staged, two LDS stages, every dtype.
+// Kernel 2 (tile2_kernel.h): direct-to-LDS copies through `stages` LDS
+// stages, 16-bit inputs only.
 struct TileShape {
-    int32_t id, bm, bn, wm, wn;
+    int32_t id, bm, bn, wm, wn, kernel, stages;
 };
-constexpr int kNumTiles = 4;
+constexpr int kNumTiles = 8;
 constexpr TileShape kTiles[kNumTiles] = {
-    {1, 64, 64, 2, 2},     // 4 waves, 32 x 32 per wave
-    {2, 128, 128, 2, 2},   // 4 waves, 64 x 64 per wave
-    {3, 256, 256, 2, 2},   // 4 waves, 128 x 128 per wave
-    {4, 256, 128, 2, 2},   // 4 waves, 128 x 64 per wave
+    {1, 64, 64, 2, 2, 1, 2},     // 4 waves, 32 x 32 per wave
+    {2, 128, 128, 2, 2, 1, 2},   // 4 waves, 64 x 64 per wave
+    {3, 256, 256, 2, 2, 1, 2},   // 4 waves, 128 x 128 per wave
+    {4, 256, 128, 2, 2, 1, 2},   // 4 waves, 128 x 64 per wave
+    {5, 256, 256, 2, 2, 2, 4},   // 4 waves, 128 x 128 per wave
+    {6, 256, 256, 2, 4, 2, 4},   // 8 waves, 128 x 64 per wave
+    {7, 256, 128, 2, 2, 2, 4},   // 4 waves, 128 x 64 per wave
+    {8, 128, 128, 2, 2, 2, 4},   // 4 waves, 64 x 64 per wave
 };
 
 // Launch one fused (or NONE-epilogue) tile-kernel GEMM.  Returns a hipError_t.

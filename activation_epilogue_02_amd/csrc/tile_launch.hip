@@ -1,21 +1,28 @@
 // tile_launch.hip -- launch table of the MFMA tile kernel.
-#include "tile_kernel.h"
+#include "tile2_kernel.h"
 
 namespace ge {
 
 int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid,
                 void* stream) {
+    const TileShape* t = nullptr;
+    for (int i = 0; i < kNumTiles; ++i)
+        if (kTiles[i].id == tile_id) t = &kTiles[i];
+    if (!t) return (int)hipErrorInvalidDeviceFunction;
     TileFn fn = nullptr;
-    switch (a_type) {
-    case GE_F32: fn = pick_tile_f32(d_type, op_b, tile_id); break;
-    case GE_F16: fn = pick_tile_f16(d_type, op_b, tile_id); break;
-    case GE_BF16: fn = pick_tile_bf16(d_type, op_b, tile_id); break;
-    case GE_F8_E4M3: fn = pick_tile_f8(d_type, op_b, tile_id); break;
+    if (t->kernel == 2) {
+        if (a_type == GE_F16) fn = pick_tile2_f16(d_type, op_b, tile_id);
+        else if (a_type == GE_BF16) fn = pick_tile2_bf16(d_type, op_b, tile_id);
+    } else {
+        switch (a_type) {
+        case GE_F32: fn = pick_tile_f32(d_type, op_b, tile_id); break;
+        case GE_F16: fn = pick_tile_f16(d_type, op_b, tile_id); break;
+        case GE_BF16: fn = pick_tile_bf16(d_type, op_b, tile_id); break;
+        case GE_F8_E4M3: fn = pick_tile_f8(d_type, op_b, tile_id); break;
+        }
     }
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
-    int threads = 0;
-    for (int i = 0; i < kNumTiles; ++i)
-        if (kTiles[i].id == tile_id) threads = kTiles[i].wm * kTiles[i].wn * 64;
+    const int threads = t->wm * t->wn * 64;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, (hipStream_t)stream, args);
     return (int)hipGetLastError();
 }

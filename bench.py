@@ -25,7 +25,11 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["tile_kernel.h", "smallm_kernel.hip", "ge_device.h", "ge_params.h"]
+CSRC = os.path.join(ROOT, "activation_epilogue_02_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# HBM-traffic counters: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+# scaled by what it reads for a plain device copy of known size
+COPY_MIB = 1024
 
 
 def parse():
@@ -42,30 +46,154 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead: run a plain device copy of MIB MiB (counter calibration)")
+    p.add_argument("--digest", default=None, metavar="DIR",
+                   help="instead: summarise the rocprofv3 runs under DIR for --workload into "
+                        "profiles/ (no GPU needed)")
     return p.parse_args()
 
 
 def kernel_src_hash() -> str:
+    """Hash of every kernel and launch source: counters taken on other
+    sources do not describe the kernel being timed."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "activation_epilogue_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str, launches_bytes_alg: float):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_for(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources;
+    else None."""
+    path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         t = json.load(open(path)).get(workload)
-    except Exception:
+    except (OSError, ValueError):
         return None
     if not t or t.get("kernel_src_hash") != kernel_src_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+# ---- profile digest (host only) ------------------------------------------------------
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d {d}/prof_{wl}_trace -o run --output-format csv "
+             "-- python3 bench.py --workload {wl} --steps {steps} --warmup 2 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_{wl}_fetch -o run --output-format csv "
+             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_{wl}_write -o run --output-format csv "
+             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_copy_fetch -o run --output-format csv "
+                  "-- python3 bench.py --copy-calibration 1024 --steps 3",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_copy_write -o run --output-format csv "
+                  "-- python3 bench.py --copy-calibration 1024 --steps 3",
+}
+FUSED_KERNEL = {"C3": "ge_smallm_kernel"}   # others: the tile kernel
+
+
+def _csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _counter_avg(dirpath, name_part, counter):
+    rows = [r for r in _csv(os.path.join(dirpath, "run_counter_collection.csv"))
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit(f"digest: no {counter} rows for {name_part} in {dirpath}")
+    vals = [float(r["Counter_Value"]) for r in rows]
+    return sum(vals) / len(vals), len(vals), rows[0]["Kernel_Name"]
+
+
+def _last_json(path):
+    line = None
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("{"):
+                line = ln
+    return json.loads(line) if line else None
+
+
+def digest(d: str, wl: str):
+    """Turn the rocprofv3 CSVs of one workload (kernel trace + stats, a
+    FETCH_SIZE and a WRITE_SIZE pass) and of the copy calibration into a
+    short text summary under profiles/ and the traffic figure bench.py
+    reports.  The kernel-source hash comes from the profiled run's own bench
+    line, so the figure is dropped once the kernel changes."""
+    import synth
+    w = synth.WORKLOADS[wl]
+    part = FUSED_KERNEL.get(wl, "ge_tile_kernel")
+    stats = _csv(os.path.join(d, f"prof_{wl.lower()}_trace", "run_kernel_stats.csv"))
+    run = _last_json(os.path.join(d, f"prof_{wl.lower()}_trace.log"))
+    if run is None:
+        raise SystemExit("digest: the traced bench run printed no JSON line")
+    fused = [r for r in stats if part in r["Name"]]
+    if not fused:
+        raise SystemExit(f"digest: {part} not in the kernel stats")
+    k = fused[0]
+    avg_ns = float(k["AverageNs"])
+    fetch_kib, nf, kname = _counter_avg(os.path.join(d, f"prof_{wl.lower()}_fetch"), part, "FETCH_SIZE")
+    write_kib, nw, _ = _counter_avg(os.path.join(d, f"prof_{wl.lower()}_write"), part, "WRITE_SIZE")
+    cf, _, _ = _counter_avg(os.path.join(d, "prof_copy_fetch"), "copyBuffer", "FETCH_SIZE")
+    cw, _, _ = _counter_avg(os.path.join(d, "prof_copy_write"), "copyBuffer", "WRITE_SIZE")
+    copy_kib = COPY_MIB * 1024.0
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    read_b = fetch_kib * 1024 * f_scale
+    write_b = write_kib * 1024 * w_scale
+    traffic = read_b + write_b
+    alg = w.algorithmic_bytes()
+    steps = run.get("steps", 10)
+    cmds = {key: c.format(d="gpurun_out", wl=wl.lower() if "{wl}_" in c else wl, steps=steps)
+            for key, c in PROFILE_COMMANDS.items()}
+    cmds = {key: c.replace(f"prof_{wl}_", f"prof_{wl.lower()}_") for key, c in cmds.items()}
+    name = f"{part}_{wl}"
+    lines = [
+        f"# {part} on {w.name}",
+        "",
+        f"kernel-source hash: {run.get('kernel_src_hash')}   plan: {run['config']['plan']}",
+        "",
+        "Commands (run from the repository root on an MI355X, rocprofv3 "
+        "output under gpurun_out/):",
+        "",
+    ] + [f"    {c}" for c in cmds.values()] + [
+        "",
+        "## Kernel trace statistics (rocprofv3 --stats), kernels above 0.5% of GPU time",
+        "",
+        "| kernel | calls | average ns | % time |",
+        "|---|---|---|---|",
+    ] + [f"| {r['Name'][:100]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['Percentage']} |"
+         for r in stats if float(r["Percentage"]) > 0.5] + [
+        "",
+        f"Dominant kernel average duration: {avg_ns / 1e3:.3f} us "
+        f"(bench.py HIP-event average in the same run: {run['roofline']['kernel_ms'] * 1e3:.3f} us).",
+        "",
+        "## HBM traffic per launch (rocprofv3 --pmc, one counter per run)",
+        "",
+        f"- FETCH_SIZE {fetch_kib:.1f} KiB/dispatch (mean of {nf}); the copy of {COPY_MIB} MiB reads "
+        f"{cf:.1f} KiB -> scale {f_scale:.4f} -> {read_b / 1e9:.4f} GB read",
+        f"- WRITE_SIZE {write_kib:.1f} KiB/dispatch (mean of {nw}); the copy writes {cw:.1f} KiB -> "
+        f"scale {w_scale:.4f} -> {write_b / 1e9:.4f} GB written",
+        f"- traffic {traffic / 1e9:.4f} GB per launch; algorithmic bytes {alg / 1e9:.4f} GB "
+        f"(ratio {traffic / alg:.2f})",
+        f"- at the traced average duration: {traffic / (avg_ns * 1e-9) / 1e9:.1f} GB/s of traffic",
+        "",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, name + ".md"), "w") as fh:
+        fh.write("\n".join(lines))
+    tpath = os.path.join(PROFILES, "traffic.json")
+    table = json.load(open(tpath)) if os.path.exists(tpath) else {}
+    table[wl] = {"kernel": kname, "kernel_src_hash": run.get("kernel_src_hash"),
+                 "hbm_bytes_per_launch": round(traffic), "read_bytes": round(read_b),
+                 "write_bytes": round(write_b), "fetch_scale": round(f_scale, 4),
+                 "write_scale": round(w_scale, 4), "avg_kernel_ns": round(avg_ns)}
+    with open(tpath, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 def copy_calibration(mib: int, steps: int):
@@ -103,18 +231,21 @@ def cpu_baseline(w, inp, seconds: float, unit: str):
     sa = float(inp.scale_a.item()) if inp.scale_a is not None else 1.0
     sb = float(inp.scale_b.item()) if inp.scale_b is not None else 1.0
     rows = max(1, min(w.m, threads))
-    done, t_total = 0, 0.0
-    while done < w.m and t_total < seconds:
-        rows = min(rows, w.m - done)
-        A_rows = raw(inp.A[done:done + rows])
+    done, t_total, start = 0, 0.0, 0
+    # whole rows of D, cycling through the rows of A (again from row 0 once
+    # all are done) until about `seconds` of oracle time has been spent
+    while t_total < seconds:
+        rows = min(rows, w.m - start)
+        A_rows = raw(inp.A[start:start + rows])
         t0 = time.perf_counter()
         C = oracle.gemm(A_rows, w.in_dtype, Bc, w.in_dtype, w.op_b, sa, sb)
-        b = bias[done:done + rows] if w.axis == "row" else bias
+        b = bias[start:start + rows] if w.axis == "row" else bias
         P = oracle.bias_pass(C, b, w.out_dtype, w.axis)
         oracle.act_pass(P, w.epilog)
         dt = time.perf_counter() - t0
         t_total += dt
         done += rows
+        start = (start + rows) % w.m
         if dt < seconds / 4:
             rows *= 2
     es, eo = synth.ELEM_SIZE[w.in_dtype], synth.ELEM_SIZE[w.out_dtype]
@@ -122,8 +253,9 @@ def cpu_baseline(w, inp, seconds: float, unit: str):
     nbytes = done * w.k * es + w.k * w.n * es + done * w.n * eo
     value = flops / t_total / 1e12 if unit == "TFLOP/s" else nbytes / t_total / 1e9
     return {"value": round(value, 6), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.m} rows of D ({done}x{w.n} outputs, full K={w.k}) through the "
-                      f"oracle's fp64 GEMM, bias and activation passes in {t_total:.1f} s"}
+            "sample": f"{done} rows of D (of {w.m}; {done}x{w.n} outputs, full K={w.k}, rows taken "
+                      f"in order and again from row 0 once all are done) through the oracle's fp64 "
+                      f"GEMM, bias and activation passes in {t_total:.1f} s"}
 
 
 def main():
@@ -133,6 +265,9 @@ def main():
               f"(the op shards by rows of A or columns of B with no exchange step; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.digest:
+        digest(args.digest, args.workload)
+        return
     import torch
 
     if args.copy_calibration:
@@ -190,6 +325,8 @@ def main():
         durs = [a.elapsed_time(b) for a, b in ev]
         return wall, durs
 
+    # the timed run: K steps between two synchronisations; the HIP events
+    # on the launch stream give the kernel's own average duration
     wall, durs = timed(step)
     ms_per_step = wall * 1e3 / args.steps
     kern_ms = sum(durs) / len(durs)
@@ -200,13 +337,14 @@ def main():
         gu.plan(w.epilog, w.axis, unfused=1)
         outs_u = [gu.alloc_outputs(dev) for _ in range(rot)]
         wall_u, durs_u = timed(lambda i: step(i, gu, outs_u))
-        # interleave once more with the fused kernel to be fair to clocks
-        wall2, durs2 = timed(step)
-        kern_ms = min(kern_ms, sum(durs2) / len(durs2))
-        ms_per_step = min(ms_per_step, wall2 * 1e3 / args.steps)
+        # the fused kernel once more after the pair, so that the comparison
+        # brackets the pair in time (clocks and temperature drift)
+        _, durs2 = timed(step)
+        kf = 0.5 * (kern_ms + sum(durs2) / len(durs2))
         ku = sum(durs_u) / len(durs_u)
         unfused = {"ms_per_step": round(wall_u * 1e3 / args.steps, 4), "kernel_pair_ms": round(ku, 4),
-                   "fused_speedup": round(ku / kern_ms, 4), "plan": gu.describe()}
+                   "fused_kernel_ms": round(kf, 4), "fused_speedup": round(ku / kf, 4),
+                   "plan": gu.describe()}
         del outs_u
         gu.free()
 
@@ -224,7 +362,7 @@ def main():
         peak = PEAK_TFLOPS[w.in_dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-    roof["traffic"] = traffic_for(args.workload, alg_bytes)
+    roof["traffic"] = traffic_for(args.workload)
     roof["kernel_ms"] = round(kern_ms, 4)
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = w.flops
@@ -255,6 +393,7 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
         "hip": torch.version.hip,
+        "kernel_src_hash": kernel_src_hash(),
     }
     print(json.dumps(out), flush=True)
     g.free()

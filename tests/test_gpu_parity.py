@@ -55,6 +55,48 @@ def test_every_tile_shape(tile, a, d, op_b):
     check_full(w, r)
 
 
+PIPELINED = [5, 6, 7, 8]
+COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32")]
+
+
+@pytest.mark.parametrize("tile", PIPELINED)
+@pytest.mark.parametrize("a,d", COMBOS16, ids=[f"{a}->{d}" for a, d in COMBOS16])
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_pipelined_tiles_ragged(tile, a, d, op_b):
+    # the direct-to-LDS kernel: ragged m and n (clamped copies), k = 200 (six
+    # full 32-deep steps plus a register-loaded tail of 8), padded leading
+    # dimensions with NaN padding, both bias axes
+    for ep, axis in (("relu_aux_bias", "row"), ("gelu_bias", "col")):
+        w = wl(300, 520, 200, a, d, ep, axis, op_b, seed=tile * 10 + op_b)
+        r = run_library(w, synth.make_inputs(w), pad=2, path=1, tile=tile)
+        assert f"tile_id={tile} kernel=2" in r.desc
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129])
+@pytest.mark.parametrize("tile", [5, 8])
+def test_pipelined_short_and_ragged_k(k, tile):
+    # fewer K steps than pipeline stages, exact multiples and one-element tails
+    for op_b in (0, 1):
+        w = wl(130, 136, k, "bf16", "bf16", "bias", "row", op_b, seed=k)
+        r = run_library(w, synth.make_inputs(w), pad=1, path=1, tile=tile)
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("tile", PIPELINED)
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_pipelined_integer_bit_exact(tile, op_b):
+    """Integer inputs: every fp32 partial sum is exact, so the pipelined
+    kernel must reproduce the RNE encoding of the exact result bit for bit."""
+    m, n, k = 512, 384, 1056
+    w = wl(m, n, k, "bf16", "bf16", "relu_bias", "col", op_b)
+    inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    r = run_library(w, inp, path=1, tile=tile)
+    from parity import oracle_full
+    Y, P, _ = oracle_full(w, r)
+    assert np.array_equal(codes(r.D)[:, :n], oracle.encode(Y, "bf16").reshape(Y.shape))
+
+
 @pytest.mark.parametrize("k", [1, 5, 37, 64, 65, 127])
 @pytest.mark.parametrize("a", ["bf16", "f32", "e4m3"])
 def test_ragged_k_with_poisoned_padding(k, a):
