@@ -74,10 +74,12 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
     const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
     const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
     if (a_type == GE_F16 || a_type == GE_BF16) {
-        // the pipelined direct-to-LDS kernel
-        if (t256 >= 512) return 5;
+        // the pipelined direct-to-LDS kernel; at 256 x 256 the 8-wave
+        // layout (two waves per SIMD fill each other's barrier and copy
+        // gaps) measures faster than 4 waves
+        if (t256 >= 512) return 6;
         if (t128 >= 512) return 8;
-        if (t256 >= 256 && t128 < 256) return 5;
+        if (t256 >= 256 && t128 < 256) return 6;
         if (t128 >= 256) return 8;
         return 1;
     }
@@ -252,7 +254,7 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     if (h->split_k > 1) {
         a.partial = (float*)(ws + h->ws_c);
         a.counters = (uint32_t*)(ws + h->ws_c + h->ws_partial);
-        if (hipMemsetAsync(a.counters, 0, h->ws_counters, (hipStream_t)stream) != hipSuccess) return GE_ERR_HIP;
+        if (launch_clear_counters(a.counters, h->tiles_n, stream) != 0) return GE_ERR_HIP;
     }
 
     KernelArgs k1 = a;

@@ -60,6 +60,9 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
 int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid,
                   void* stream);
 
+// Zero n split-K arrival counters on `stream` (a kernel, graph-capturable).
+int launch_clear_counters(uint32_t* p, int n, void* stream);
+
 // Launch the unfused pair's elementwise kernel: D = act(C + bias) (+ mask),
 // reading C (d_type, leading dimension ldd) from `c`.
 int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* stream);

@@ -16,8 +16,9 @@
 //    lane's chunks for one MFMA step cover 32 consecutive K values of its row
 //    together with the other three q lanes, so each step reads 64 contiguous
 //    bytes per W row.
-//  * Loads are issued `kUnroll` steps ahead of the MFMAs that consume them to
-//    keep enough bytes in flight per CU.
+//  * Loads are issued `kUnroll` steps ahead of the MFMAs that consume them
+//    (all of a wave's share of W at the batch-16 Linear shape), so the HBM
+//    latency is paid once rather than once per batch.
 //  * The waves' partial 16 x 16 blocks are reduced in LDS in a fixed order.
 //    With split_k > 1 the per-slice sums go to an fp32 workspace and the last
 //    workgroup to arrive for a column block (arrival counter, then a device-
@@ -29,7 +30,7 @@
 namespace ge {
 
 constexpr int kSmWaves = 8;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 template <int DIN, int DOUT>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -41,15 +42,14 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// 16-byte chunk of 8 16-bit elements at (row, col) with bounds (nrows, ncols).
-__device__ __forceinline__ u32x4 sm_load(const uint16_t* base, int64_t ld, int row, int nrows, int col,
-                                         int ncols) {
-    if (row >= nrows || col >= ncols) return u32x4{0, 0, 0, 0};
-    const uint16_t* p = base + (int64_t)row * ld + col;
-    if (col + 8 <= ncols) return __builtin_nontemporal_load((const u32x4*)p);
+// 16-byte chunk of 8 16-bit elements starting at column `col` of a row,
+// elements at col + e >= ncols read as zero (the ragged K step only).
+__device__ __forceinline__ u32x4 sm_load_masked(const uint16_t* row, int col, int ncols) {
+    if (col >= ncols) return u32x4{0, 0, 0, 0};
+    if (col + 8 <= ncols) return *(const u32x4*)(row + col);
     uint16_t t[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = (col + e < ncols) ? p[e] : (uint16_t)0;
+    for (int e = 0; e < 8; ++e) t[e] = (col + e < ncols) ? row[col + e] : (uint16_t)0;
     u32x4 r;
     __builtin_memcpy(&r, t, 16);
     return r;
@@ -64,29 +64,51 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
     const int slice = blockIdx.x / p.tiles_n;  // K slice
     const int n0 = nblk * 16;
     const int M = p.m, N = p.n, K = p.k;
-    const uint16_t* W = (const uint16_t*)p.B;
-    const uint16_t* X = (const uint16_t*)p.A;
 
     // this wave's K range: the slice split evenly over the waves, in steps of 32
     const int ks = slice * p.k_per_split;
     const int ke = min(K, ks + p.k_per_split);
     const int steps_total = (ke - ks + 31) / 32;
     const int per_wave = (steps_total + kSmWaves - 1) / kSmWaves;
-    const int s_begin = wave * per_wave;
+    const int s_begin = min(steps_total, wave * per_wave);
     const int s_end = min(steps_total, s_begin + per_wave);
+    const int s_full = min(s_end, (ke - ks) / 32);   // steps lying wholly below ke
+
+    // Rows beyond n (of W) or m (of x) only feed outputs that are never
+    // stored, so their addresses are clamped to the last valid row: the
+    // full steps then need no bounds checks at all.
+    const uint16_t* wrow = (const uint16_t*)p.B + (int64_t)min(n0 + r, N - 1) * p.ldb + ks + q * 8;
+    const uint16_t* xrow = (const uint16_t*)p.A + (int64_t)min(r, M - 1) * p.lda + ks + q * 8;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = s_begin; s0 < s_end; s0 += kUnroll) {
+    int s0 = s_begin;
+    for (; s0 + kUnroll <= s_full; s0 += kUnroll) {
         u32x4 wv[kUnroll], xv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int kc = ks + (s0 + u) * 32 + q * 8;
-            const bool ok = s0 + u < s_end;
-            wv[u] = ok ? sm_load(W, p.ldb, n0 + r, N, kc, ke) : u32x4{0, 0, 0, 0};
-            xv[u] = ok ? sm_load(X, p.lda, r, M, kc, ke) : u32x4{0, 0, 0, 0};
+            wv[u] = __builtin_nontemporal_load((const u32x4*)(wrow + (s0 + u) * 32));
+            xv[u] = *(const u32x4*)(xrow + (s0 + u) * 32);
         }
+        // keep the whole batch of loads ahead of the MFMAs (the scheduler
+        // would otherwise trickle them out two per MFMA)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc = mfma16<DIN, DOUT>(wv[u], xv[u], acc);
+    }
+    for (; s0 < s_full; ++s0) {
+        const u32x4 wv = __builtin_nontemporal_load((const u32x4*)(wrow + s0 * 32));
+        const u32x4 xv = *(const u32x4*)(xrow + s0 * 32);
+        acc = mfma16<DIN, DOUT>(wv, xv, acc);
+    }
+    if (s_full >= s_begin && s_full < s_end) {
+        // the ragged last step of the slice, if it falls in this wave's
+        // range: elements at k >= ke are zero in both operands (0 * NaN
+        // would not vanish)
+        const int col = s_full * 32;
+        const int lim = ke - ks - q * 8;
+        const u32x4 wv = sm_load_masked(wrow, col, lim);
+        const u32x4 xv = sm_load_masked(xrow, col, lim);
+        acc = mfma16<DIN, DOUT>(wv, xv, acc);
     }
     // acc: lane holds rows n0 + 4q + i (i = 0..3) of column m = r of y^T
     red[wave][lane] = acc;
@@ -167,6 +189,19 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
             for (int64_t hw = nblk + 1; hw < row_hw; ++hw) aux16[(int64_t)m * row_hw + hw] = 0;
         }
     }
+}
+
+// Clear the split-K arrival counters before a launch.  A kernel rather than
+// hipMemsetAsync, so that a caller may capture execute() into a HIP graph.
+__global__ void __launch_bounds__(256) ge_clear_u32(uint32_t* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+int launch_clear_counters(uint32_t* p, int n, void* stream) {
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(ge_clear_u32, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, p, n);
+    return (int)hipGetLastError();
 }
 
 typedef void (*SmFn)(KernelArgs);

@@ -240,70 +240,89 @@ ge_tile2_kernel(KernelArgs p) {
         }
     }
 
-    auto compute = [&](int stage) {
+    // fragments of one k16 sub-step (kk) of the step held in `stage`
+    auto load_frags = [&](int stage, int kk, u32x4 (&af)[C::FM], u32x4 (&bfr)[C::FN]) {
         const uint8_t* st = smem + stage * C::STAGE;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            u32x4 af[C::FM], bfr[C::FN];
-#pragma unroll
-            for (int f = 0; f < C::FM; ++f) af[f] = *(const u32x4*)(st + offA[f][kk]);
-#pragma unroll
-            for (int f = 0; f < C::FN; ++f) {
-                if constexpr (OPB == GE_OP_T) {
-                    bfr[f] = *(const u32x4*)(st + offB[f][kk][0]);
-                } else {
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][1])));
-                    bfr[f] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                                   (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                                   (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                                   (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-                }
+        for (int f = 0; f < C::FN; ++f) {
+            if constexpr (OPB == GE_OP_T) {
+                bfr[f] = *(const u32x4*)(st + offB[f][kk][0]);
+            } else {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][1])));
+                bfr[f] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
             }
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j) {
-                    if constexpr (DIN == GE_BF16)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, bfr[i]), __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0,
-                            0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0,
-                            0, 0);
-                }
         }
+#pragma unroll
+        for (int f = 0; f < C::FM; ++f) af[f] = *(const u32x4*)(st + offA[f][kk]);
     };
-
-    // ---- main loop: S stages, S-1 steps in flight ----
+    auto mfmas = [&](const u32x4 (&af)[C::FM], const u32x4 (&bfr)[C::FN]) {
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-        if (t < KT) issue(t);
-    for (int kt = 0; kt < KT; ++kt) {
-        // this wave's copies of step kt are done when at most the copies of
-        // the (up to S-2) later steps already issued are outstanding
-        const int later = min(S - 2, KT - 1 - kt);
-        if constexpr (S >= 4) {
-            if (later >= 2) wait_vm<2 * C::VM_PER_STEP>();
-            else if (later == 1) wait_vm<C::VM_PER_STEP>();
-            else wait_vm<0>();
-        } else if constexpr (S == 3) {
-            if (later >= 1) wait_vm<C::VM_PER_STEP>();
-            else wait_vm<0>();
-        } else {
-            wait_vm<0>();
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): tail-step LDS writes done
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) {
+                if constexpr (DIN == GE_BF16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, bfr[i]), __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0, 0, 0);
+            }
+    };
+    // Wait until this wave's copies of step t are done, given that the
+    // copies of steps t+1 .. last_issued were issued after them.
+    auto wait_step = [&](int later) {
+        static_assert(S <= 5, "wait ladder covers up to 4 later steps");
+        if (later >= 4) wait_vm<(4 * C::VM_PER_STEP < 64 ? 4 * C::VM_PER_STEP : 63)>();
+        else if (later == 3) wait_vm<(3 * C::VM_PER_STEP < 64 ? 3 * C::VM_PER_STEP : 63)>();
+        else if (later == 2) wait_vm<2 * C::VM_PER_STEP>();
+        else if (later == 1) wait_vm<C::VM_PER_STEP>();
+        else wait_vm<0>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads and tail writes done
         // workgroup barrier without a memory fence (a fence would wait for
         // every copy in flight); the clobber keeps LDS accesses on their side
         asm volatile("s_barrier" ::: "memory");
-        // stage (kt + S - 1) % S was last read in step kt - 1, which every
-        // wave has finished (its reads returned before its MFMAs issued)
-        if (kt + S - 1 < KT) issue(kt + S - 1);
-        compute(kt % S);
+    };
+
+    // ---- main loop ----
+    // All S stages start filling at once; afterwards the copy of step
+    // kt + S goes into the stage step kt used, as soon as every wave has
+    // read its last fragments from it.  The barrier sits between the two
+    // k16 halves of a step, so the first fragments of step kt + 1 are read
+    // while the matrix cores still work on step kt.
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+        if (t < KT) issue(t);
+    u32x4 a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    if (KT > 0) {
+        wait_step(min(S - 1, KT - 1));
+        load_frags(0, 0, a0, b0);
+    }
+    // (the last step is peeled off so that the loop body always passes the
+    // barrier: a merged path would make the compiler's wait analysis hold
+    // the second-half MFMAs until the next step's fragment reads return)
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        // each group of fragment reads is issued ahead of the MFMAs that do
+        // not need it (the scheduler would otherwise sink the last reads to
+        // the end of the block and stall the next MFMAs on them)
+        load_frags(kt % S, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a0, b0);
+        wait_step(min(S - 2, KT - 2 - kt));
+        if (kt + S < KT) issue(kt + S);
+        load_frags((kt + 1) % S, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a1, b1);
+    }
+    if (KT > 0) {
+        load_frags((KT - 1) % S, 1, a1, b1);
+        mfmas(a0, b0);
+        mfmas(a1, b1);
     }
 
     // ---- fused epilogue on the accumulators (as in tile_kernel.h) ----

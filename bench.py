@@ -44,6 +44,13 @@ def parse():
                    help="copies of the operands cycled through (defeats the 256 MiB MALL "
                         "for HBM-bound workloads); default 16 for the batch-16 Linear, else 1")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--tile", type=int, default=0,
+                   help="force a tile id of the planner (0 = its own choice)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch each step from Python instead of replaying the K steps as one "
+                        "captured HIP graph (then host launch latency shows in the timings)")
+    p.add_argument("--split-k", type=int, default=0,
+                   help="force the K split of the small-m path (0 = the planner's choice)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead: run a plain device copy of MIB MiB (counter calibration)")
     p.add_argument("--digest", default=None, metavar="DIR",
@@ -295,7 +302,7 @@ def main():
 
     t0 = time.perf_counter()
     g = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-    g.plan(w.epilog, w.axis)
+    g.plan(w.epilog, w.axis, tile=args.tile, split_k=args.split_k)
     plan_us = (time.perf_counter() - t0) * 1e6
     desc = g.describe()
     outs = [g.alloc_outputs(dev) for _ in range(rot)]
@@ -305,25 +312,48 @@ def main():
     def step(i, h=g, outputs=outs):
         c = copies[i % rot]
         D, aux, ws = outputs[i % rot]
+        # the stream current at call time: the capture stream while a graph
+        # is being recorded
         B.gemm_epilog_execute(h.h, c.A, c.B, bias[i % rot], D, aux, c.scale_a, c.scale_b, ws,
-                              None if ws is None else ws.numel(), stream.cuda_stream)
+                              None if ws is None else ws.numel(),
+                              torch.cuda.current_stream().cuda_stream)
 
     def timed(fn):
+        """W eager warm-up steps, then exactly K timed steps between two
+        synchronisations.  By default the K steps are captured once as a HIP
+        graph (replayed once untimed, to load it) and the timed region is one
+        replay: the kernels then run back to back instead of waiting for
+        Python to launch each one.  Returns (wall seconds, [mean ms per step
+        from HIP events on the launch stream])."""
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.no_graph:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for i in range(args.steps):
+                ev[i][0].record(stream)
+                fn(i)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_start
+            return wall, [a.elapsed_time(b) for a, b in ev]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                fn(i)
+        graph.replay()
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        for i in range(args.steps):
-            ev[i][0].record(stream)
-            fn(i)
-            ev[i][1].record(stream)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
-        durs = [a.elapsed_time(b) for a, b in ev]
-        return wall, durs
+        return wall, [e0.elapsed_time(e1) / args.steps]
 
     # the timed run: K steps between two synchronisations; the HIP events
     # on the launch stream give the kernel's own average duration
@@ -334,7 +364,7 @@ def main():
     unfused = None
     if not args.no_unfused and w.epilog != "none":
         gu = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-        gu.plan(w.epilog, w.axis, unfused=1)
+        gu.plan(w.epilog, w.axis, unfused=1, tile=args.tile, split_k=args.split_k)
         outs_u = [gu.alloc_outputs(dev) for _ in range(rot)]
         wall_u, durs_u = timed(lambda i: step(i, gu, outs_u))
         # the fused kernel once more after the pair, so that the comparison
@@ -384,6 +414,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.in_dtype,
         "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "timing": "eager launches, HIP events per step" if args.no_graph else
+                  "K steps replayed as one captured HIP graph, HIP events around the replay",
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "epilog": w.epilog,
                    "bias_axis": w.axis, "op_b": w.op_b, "out_dtype": w.out_dtype,
                    "operand_copies": rot, "plan": desc, "plan_us": round(plan_us, 1)},
