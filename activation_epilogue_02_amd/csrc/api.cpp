@@ -73,6 +73,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int choose_tile(int64_t m, int64_t n, int a_type) {
     const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
     const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    if (a_type == GE_F8_E4M3) {
+        // fp8 rows are 128 bytes per step: a 256 x 256 stage is 64 KiB, so
+        // only two stages fit and the registers spill; 256 x 128 keeps three
+        // stages and measures faster
+        const int64_t t2x1 = ceil_div(m, 256) * ceil_div(n, 128);
+        if (t2x1 >= 512) return 7;
+        if (t128 >= 256) return 8;
+        return 1;
+    }
     if (a_type == GE_F16 || a_type == GE_BF16) {
         // the pipelined direct-to-LDS kernel; at 256 x 256 the 8-wave
         // layout (two waves per SIMD fill each other's barrier and copy
@@ -90,9 +99,9 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
     return 1;
 }
 
-// The pipelined kernel takes 16-bit inputs only.
+// The pipelined kernel takes 16-bit and fp8 inputs.
 bool tile_supports(const TileShape* t, int a_type) {
-    return t->kernel == 1 || a_type == GE_F16 || a_type == GE_BF16;
+    return t->kernel == 1 || a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
 }
 
 bool smallm_supported(const ge_desc& d) {
@@ -316,7 +325,9 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
              "ldaux_words=%lld",
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
              h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
-             t ? t->wn : 8, h->tile_id, t ? t->kernel : 0, t ? t->stages : 0, h->grid, h->group_m, h->split_k,
+             t ? t->wn : 8, h->tile_id, t ? t->kernel : 0,
+             t ? (t->kernel == 2 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
+             h->split_k,
              h->unfused,
              h->ws_c + h->ws_partial + h->ws_counters, (long long)h->ldaux);
     return GE_OK;

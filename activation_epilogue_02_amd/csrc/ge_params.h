@@ -35,8 +35,8 @@ enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 
 // Tile shapes of the MFMA tile kernels: block tile BM x BN, waves WM x WN.
 // Kernel 1 (tile_kernel.h): register-staged, two LDS stages, every dtype.
-// Kernel 2 (tile2_kernel.h): direct-to-LDS copies through `stages` LDS
-// stages, 16-bit inputs only.
+// Kernel 2 (tile2_kernel.h): direct-to-LDS copies through up to `stages`
+// LDS stages (as many as fit in 160 KiB), fp16/bf16/fp8 inputs.
 struct TileShape {
     int32_t id, bm, bn, wm, wn, kernel, stages;
 };
@@ -51,6 +51,13 @@ constexpr TileShape kTiles[kNumTiles] = {
     {7, 256, 128, 2, 2, 2, 4},   // 4 waves, 128 x 64 per wave
     {8, 128, 128, 2, 2, 2, 4},   // 4 waves, 64 x 64 per wave
 };
+
+// LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64
+// bytes (16-bit inputs) or 128 bytes (fp8); at most 160 KiB in total.
+constexpr int tile2_stages(const TileShape& t, int elem_size) {
+    const int stage = (t.bm + t.bn) * (elem_size == 1 ? 128 : 64);
+    return t.stages * stage <= 160 * 1024 ? t.stages : (160 * 1024) / stage;
+}
 
 // Launch one fused (or NONE-epilogue) tile-kernel GEMM.  Returns a hipError_t.
 int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs& args,

@@ -70,7 +70,12 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
     const int ke = min(K, ks + p.k_per_split);
     const int steps_total = (ke - ks + 31) / 32;
     const int per_wave = (steps_total + kSmWaves - 1) / kSmWaves;
-    const int s_begin = min(steps_total, wave * per_wave);
+    // Every workgroup reads all of x, so the waves of different workgroups
+    // take the K sub-ranges in a rotated order: at any moment neighbouring
+    // workgroups read different parts of x rather than all hitting the same
+    // L2 lines.  Each output column's summation order is still fixed.
+    const int wslot = (wave + nblk) % kSmWaves;
+    const int s_begin = min(steps_total, wslot * per_wave);
     const int s_end = min(steps_total, s_begin + per_wave);
     const int s_full = min(s_end, (ke - ks) / 32);   // steps lying wholly below ke
 
@@ -79,6 +84,24 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
     // full steps then need no bounds checks at all.
     const uint16_t* wrow = (const uint16_t*)p.B + (int64_t)min(n0 + r, N - 1) * p.ldb + ks + q * 8;
     const uint16_t* xrow = (const uint16_t*)p.A + (int64_t)min(r, M - 1) * p.lda + ks + q * 8;
+
+    // the epilogue's bias values (wave 0 runs the epilogue): fetched now so
+    // that their latency hides under the W stream instead of adding to the
+    // end of the kernel
+    const int ep = p.epilog;
+    const bool has_bias = ep != GE_EPILOG_NONE;
+    float bpre[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0 && has_bias) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + 4 * q + i;
+            if (p.axis == GE_BIAS_COL) {
+                if (n < N) bpre[i] = load_scalar<DOUT>(p.bias, n);
+            } else if (r < M) {
+                bpre[i] = load_scalar<DOUT>(p.bias, r);
+            }
+        }
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int s0 = s_begin;
@@ -136,9 +159,6 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
         if (lane == 0) p.counters[nblk] = 0u;   // re-arm for the next launch
     }
 
-    float s = 1.0f;
-    const int ep = p.epilog;
-    const bool has_bias = ep != GE_EPILOG_NONE;
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
     const int m = r;
     const bool mok = m < M;
@@ -147,10 +167,7 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = n0 + 4 * q + i;
-        float b = 0.0f;
-        if (has_bias && n < N && (p.axis == GE_BIAS_COL)) b = load_scalar<DOUT>(p.bias, n);
-        if (has_bias && p.axis == GE_BIAS_ROW && mok) b = load_scalar<DOUT>(p.bias, m);
-        const float x = sum[i] * s + b;
+        const float x = sum[i] + bpre[i];
         if (want_aux && x > 0.0f && n < N) bits |= 1u << (4 * q + i);
         v[i] = activate(ep, x);
     }

@@ -1,5 +1,5 @@
 // tile2_kernel.h -- the pipelined fused GEMM + epilogue tile kernel for
-// 16-bit inputs (fp16, bf16) on gfx950.
+// 16-bit (fp16, bf16) and 8-bit (OCP E4M3) inputs on gfx950.
 //
 // Computes the same thing as the baseline tile kernel (tile_kernel.h):
 // D = act(A*B + bias) (+ ReLU sign mask), one workgroup per BM x BN tile,
@@ -7,8 +7,9 @@
 // once (cuBLASLt page, paragraph 2; NVGEMM page, section "What NVGEMM
 // changes").  What differs is how A and B reach the matrix cores:
 //
-//  * K is consumed 32 elements (64 bytes of a row) per step, through S LDS
-//    stages.  Full steps are copied global -> LDS by the direct-to-LDS loads
+//  * K is consumed 64 bytes of a row per step for 16-bit inputs (32
+//    elements) and 128 bytes for fp8 (128 elements), through as many LDS
+//    stages as fit (up to S).  Full steps are copied global -> LDS by the direct-to-LDS loads
 //    of gfx950 (global_load_lds_dwordx4: each lane's 16 bytes land at
 //    M0 + 16*lane), so the copy costs no VGPRs and no VALU, and S-1 steps are
 //    in flight while the matrix cores work on the current one.  A wave waits
@@ -23,18 +24,23 @@
 //    natural [k][n] layout in LDS and is read with the transposing LDS load
 //    of gfx950 (ds_read_b64_tr_b16): in each 16-lane group, lanes 4r..4r+3
 //    address the four 8-byte pieces of row r of a 4 x 16 block and lane i
-//    receives column i, i.e. 4 consecutive k values of one n.  No transpose
-//    in registers.
+//    receives column i, i.e. 4 consecutive k values of one n.  For fp8 the
+//    byte form (ds_read_b64_tr_b8) does the same on an 8 x 16-byte block:
+//    lanes 2r, 2r+1 address the halves of row r, lane i receives 8
+//    consecutive k values of column i.  No transpose in registers.
 //  * Tails: rows of A beyond m and columns of B beyond n only feed outputs
 //    that are never stored, so their addresses are clamped to the last valid
 //    row / 16-byte chunk (memory safety only).  A ragged last K step is
 //    loaded through registers with the elements beyond k zeroed (in both A
 //    and B, since 0 * NaN would not vanish) and written to the same LDS
 //    positions.
-//  * MFMA 32x32x16 with swapped operands and the epilogue exactly as in
+//  * MFMA 32x32x16 (16-bit) or 32x32x64 (fp8, per-tensor scales applied to
+//    the accumulator) with swapped operands and the epilogue exactly as in
 //    tile_kernel.h: after a lane-half swap each lane owns 8 consecutive
 //    columns of one row of D and stores them with one 16-byte store.
 #pragma once
+#include <type_traits>
+
 #include "tile_kernel.h"
 
 namespace ge {
@@ -83,36 +89,68 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// XOR swizzle of the chunks of a [k][n] LDS row of 8-bit B (given k x n),
+// indexed by k mod 8.  The transposing byte reads take 8 consecutive k rows
+// and one 16-byte chunk per 16-lane group (two adjacent chunks per 32
+// lanes); with 256-byte rows the table keeps both the chunk index mod 8 and
+// its upper three bits distinct over the 8 rows, with 128-byte rows (where
+// the rows alternate between bank halves) the identity does.
+__device__ __forceinline__ int swz_kn8(int k, int cpr) {
+    const int r = k & 7;
+    return cpr == 16 ? 2 * r + (r >> 2) : r;
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S>
 struct Tile2Cfg {
     static constexpr int NW = WM * WN, NT = NW * 64;
-    static constexpr int BK = 32;                    // elements per K step
-    static constexpr int ROWB = 64;                  // bytes per LDS row (A, B n x k)
+    static constexpr int ESZ = Elem<DIN>::size;
+    static constexpr int ROWB = ESZ == 1 ? 128 : 64;  // bytes of an A (or n x k B) row per K step
+    static constexpr int BK = ROWB / ESZ;             // K elements per step: 32 (16-bit) or 128 (fp8)
+    static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row: 4 or 8
+    static constexpr int RPC = 1024 / ROWB;           // rows per 1 KiB copy
+    static constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
     static constexpr int A_BYTES = BM * ROWB;
-    static constexpr int B_BYTES = BK * BN * 2;      // same for both B layouts
+    static constexpr int B_BYTES = BK * BN * ESZ;     // same for both B layouts
     static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int SE = S * STAGE <= 160 * 1024 ? S : (160 * 1024) / STAGE;   // stages that fit
     static constexpr int A_INS = A_BYTES / 1024 / NW;   // 1 KiB copies per wave per step
     static constexpr int B_INS = B_BYTES / 1024 / NW;
     static constexpr int VM_PER_STEP = A_INS + B_INS;
-    static constexpr int KN_ROWB = BN * 2;           // bytes per [k][n] LDS row
-    static constexpr int KN_CPR = BN / 8;            // 16-byte chunks per [k][n] row
-    static constexpr int KN_RPI = 1024 / KN_ROWB;    // [k][n] rows per 1 KiB copy
+    static constexpr int KN_ROWB = BN * ESZ;          // bytes per [k][n] LDS row
+    static constexpr int KN_CPR = KN_ROWB / 16;       // 16-byte chunks per [k][n] row
+    static constexpr int KN_RPI = 1024 / KN_ROWB;     // [k][n] rows per 1 KiB copy
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
-    static_assert(DIN == GE_F16 || DIN == GE_BF16, "16-bit inputs only");
+    // LDS reads per fragment and k sub-step: 16-bit A 1 x 16 B; fp8 A 2 x 16 B;
+    // k x n B: 2 transposing 16-bit reads or 4 transposing byte reads
+    static constexpr int NRA = ESZ == 1 ? 2 : 1;
+    static constexpr int NRB = OPB == GE_OP_T ? NRA : (ESZ == 1 ? 4 : 2);
+    static_assert(DIN == GE_F16 || DIN == GE_BF16 || DIN == GE_F8_E4M3, "16-bit or fp8 inputs");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole copies per wave");
-    static_assert(KN_CPR >= 16 && KN_ROWB <= 1024, "[k][n] swizzle needs 16..64 chunks per row");
+    static_assert(OPB == GE_OP_T || (ESZ == 2 ? (KN_CPR >= 16 && KN_CPR <= 64) : (KN_CPR == 8 || KN_CPR == 16)),
+                  "[k][n] swizzle tables cover 256..1024-byte (16-bit) or 128/256-byte (fp8) rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
-    static_assert((S - 2) * VM_PER_STEP < 64, "vmcnt range");
+    static_assert(SE >= 2, "LDS budget");
+    static_assert((SE - 1) * VM_PER_STEP < 64, "vmcnt range");
 };
+
+// swizzle of the chunks of a ROWB-byte row (A, or B given n x k)
+template <int ROWB>
+__device__ __forceinline__ int swz_row(int row) {
+    if constexpr (ROWB == 64) return swz64(row);
+    else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
+}
 
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S>
 __global__ void __launch_bounds__(WM* WN * 64)
 ge_tile2_kernel(KernelArgs p) {
     using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S>;
-    constexpr int BK = C::BK;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * C::STAGE];
+    constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
+    using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SE * C::STAGE];
 
     int tm, tn;
     tile_coords<DIN, DOUT, OPB, BM, BN, WM, WN>(p, tm, tn);
@@ -129,47 +167,48 @@ ge_tile2_kernel(KernelArgs p) {
     const int KF = K / BK;                  // full K steps (direct copies)
 
     // ---- per-lane sources of this wave's 1 KiB copies, at K step 0 ----
-    // A: copy i covers LDS rows R = (wave*A_INS + i)*16 + lane/4, slot lane%4
+    // A: copy i covers LDS rows R = (wave*A_INS + i)*RPC + lane/CPR, slot lane%CPR
     const uint8_t* srcA[C::A_INS];
     int rowA_cp[C::A_INS], chA_cp[C::A_INS];
 #pragma unroll
     for (int i = 0; i < C::A_INS; ++i) {
-        const int R = (wave * C::A_INS + i) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz64(R);
+        const int R = (wave * C::A_INS + i) * C::RPC + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ swz_row<C::ROWB>(R);
         const int gm = min(m0 + R, max(M - 1, 0));
         rowA_cp[i] = m0 + R;
         chA_cp[i] = c;
-        srcA[i] = gA + ((int64_t)gm * p.lda + c * 8) * 2;
+        srcA[i] = gA + ((int64_t)gm * p.lda + c * EPC) * ESZ;
     }
     const uint8_t* srcB[C::B_INS];
     int rowB_cp[C::B_INS], chB_cp[C::B_INS];
-    const int nlast = N > 0 ? ((N - 1) / 8) * 8 : 0;   // start of the last chunk holding valid columns
+    const int nlast = N > 0 ? ((N - 1) / EPC) * EPC : 0;   // start of the last chunk holding valid columns
 #pragma unroll
     for (int i = 0; i < C::B_INS; ++i) {
         if constexpr (OPB == GE_OP_T) {
-            const int R = (wave * C::B_INS + i) * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ swz64(R);
+            const int R = (wave * C::B_INS + i) * C::RPC + lane / C::CPR;
+            const int c = (lane % C::CPR) ^ swz_row<C::ROWB>(R);
             const int gn = min(n0 + R, max(N - 1, 0));
             rowB_cp[i] = n0 + R;
             chB_cp[i] = c;
-            srcB[i] = gB + ((int64_t)gn * p.ldb + c * 8) * 2;
+            srcB[i] = gB + ((int64_t)gn * p.ldb + c * EPC) * ESZ;
         } else {
             const int kr = (wave * C::B_INS + i) * C::KN_RPI + lane / C::KN_CPR;
-            const int c = (lane % C::KN_CPR) ^ swz_kn(kr);
-            const int gn = min(n0 + c * 8, nlast);
+            const int c = (lane % C::KN_CPR) ^ (ESZ == 1 ? swz_kn8(kr, C::KN_CPR) : swz_kn(kr));
+            const int gn = min(n0 + c * EPC, nlast);
             rowB_cp[i] = kr;
-            chB_cp[i] = n0 + c * 8;
-            srcB[i] = gB + ((int64_t)kr * p.ldb + gn) * 2;
+            chB_cp[i] = n0 + c * EPC;
+            srcB[i] = gB + ((int64_t)kr * p.ldb + gn) * ESZ;
         }
     }
-    const int64_t stepB = (OPB == GE_OP_T) ? (int64_t)BK * 2 : (int64_t)BK * p.ldb * 2;
+    const int64_t stepA = (int64_t)BK * ESZ;
+    const int64_t stepB = (OPB == GE_OP_T) ? (int64_t)BK * ESZ : (int64_t)BK * p.ldb * ESZ;
 
-    // issue the direct copies of full K step t into stage t % S
+    // issue the direct copies of full K step t into stage t % SE
     auto issue_direct = [&](int t) {
-        uint8_t* st = smem + (t % S) * C::STAGE;
+        uint8_t* st = smem + (t % SE) * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::A_INS; ++i)
-            copy_to_lds16(srcA[i] + (int64_t)t * BK * 2, lds_addr(st + (wave * C::A_INS + i) * 1024));
+            copy_to_lds16(srcA[i] + (int64_t)t * stepA, lds_addr(st + (wave * C::A_INS + i) * 1024));
 #pragma unroll
         for (int i = 0; i < C::B_INS; ++i)
             copy_to_lds16(srcB[i] + (int64_t)t * stepB, lds_addr(st + C::A_BYTES + (wave * C::B_INS + i) * 1024));
@@ -177,18 +216,18 @@ ge_tile2_kernel(KernelArgs p) {
 
     // the ragged last K step t: through registers, elements at k >= K zeroed
     auto issue_tail = [&](int t) {
-        uint8_t* st = smem + (t % S) * C::STAGE;
+        uint8_t* st = smem + (t % SE) * C::STAGE;
         const int k0 = t * BK;
         u32x4 va[C::A_INS], vb[C::B_INS];
 #pragma unroll
         for (int i = 0; i < C::A_INS; ++i)
-            va[i] = load_chunk<2>(gA, p.lda, min(rowA_cp[i], max(M - 1, 0)), M, k0 + chA_cp[i] * 8, K);
+            va[i] = load_chunk<ESZ>(gA, p.lda, min(rowA_cp[i], max(M - 1, 0)), M, k0 + chA_cp[i] * EPC, K);
 #pragma unroll
         for (int i = 0; i < C::B_INS; ++i) {
             if constexpr (OPB == GE_OP_T)
-                vb[i] = load_chunk<2>(gB, p.ldb, min(rowB_cp[i], max(N - 1, 0)), N, k0 + chB_cp[i] * 8, K);
+                vb[i] = load_chunk<ESZ>(gB, p.ldb, min(rowB_cp[i], max(N - 1, 0)), N, k0 + chB_cp[i] * EPC, K);
             else
-                vb[i] = load_chunk<2>(gB, p.ldb, k0 + rowB_cp[i], K, min(chB_cp[i], nlast), N);
+                vb[i] = load_chunk<ESZ>(gB, p.ldb, k0 + rowB_cp[i], K, min(chB_cp[i], nlast), N);
         }
 #pragma unroll
         for (int i = 0; i < C::A_INS; ++i) *(u32x4*)(st + (wave * C::A_INS + i) * 1024 + lane * 16) = va[i];
@@ -208,46 +247,68 @@ ge_tile2_kernel(KernelArgs p) {
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
 
-    // per-lane LDS read offsets within a stage
-    int offA[C::FM][2];
+    // Per-lane LDS read offsets within a stage.  Any assignment of K values
+    // to (lane half, operand element) is valid as long as A and B use the
+    // same one.  16-bit: sub-step kk, lane half h reads k 16kk + 8h .. +7.
+    // fp8: sub-step kk, lane half h reads k 64kk + 32h .. +31.
+    int offA[C::FM][2][C::NRA];
 #pragma unroll
     for (int f = 0; f < C::FM; ++f) {
         const int row = wm * C::TM + f * 32 + r32;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) offA[f][kk] = row * C::ROWB + (((2 * kk + h) ^ swz64(row)) << 4);
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < C::NRA; ++e) {
+                const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
+                offA[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
+            }
     }
-    // B given n x k: as A.  B given k x n: two transposing reads per fragment
-    // and k16 sub-step; lane (group G, i): k = 16kk + 8(G/2) + 4*half + i/4,
-    // n = wave col + 32f + 16(G%2) + 4(i%4).
-    int offB[C::FN][2][2];
+    // B given n x k: as A.  B given k x n, transposing reads:
+    //  16-bit, read e of 2: group G, lane i: k = 16kk + 8(G/2) + 4e + i/4,
+    //          n = wave col + 32f + 16(G%2) + 4(i%4);
+    //  fp8, read e of 4:    group G, lane i: k = 64kk + 32(G/2) + 8e + i/2,
+    //          n = wave col + 32f + 16(G%2) + 8(i%2).
+    int offB[C::FN][2][C::NRB];
 #pragma unroll
     for (int f = 0; f < C::FN; ++f) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
+            for (int e = 0; e < C::NRB; ++e) {
                 if constexpr (OPB == GE_OP_T) {
                     const int row = wn * C::TN + f * 32 + r32;
-                    offB[f][kk][hf] = C::A_BYTES + row * C::ROWB + (((2 * kk + h) ^ swz64(row)) << 4);
+                    const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
+                    offB[f][kk][e] = C::A_BYTES + row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
+                } else if constexpr (ESZ == 2) {
+                    const int G = lane >> 4, i = lane & 15;
+                    const int k = 16 * kk + 8 * (G >> 1) + 4 * e + (i >> 2);
+                    const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 4 * (i & 3);
+                    offB[f][kk][e] =
+                        C::A_BYTES + k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k)) << 4) + ((n & 4) << 1);
                 } else {
                     const int G = lane >> 4, i = lane & 15;
-                    const int k = 16 * kk + 8 * (G >> 1) + 4 * hf + (i >> 2);
-                    const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 4 * (i & 3);
-                    offB[f][kk][hf] =
-                        C::A_BYTES + k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k)) << 4) + ((n & 4) << 1);
+                    const int k = 64 * kk + 32 * (G >> 1) + 8 * e + (i >> 1);
+                    const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 8 * (i & 1);
+                    offB[f][kk][e] = C::A_BYTES + k * C::KN_ROWB +
+                                     (((n >> 4) ^ swz_kn8(k, C::KN_CPR)) << 4) + (n & 8);
                 }
             }
         }
     }
 
-    // fragments of one k16 sub-step (kk) of the step held in `stage`
-    auto load_frags = [&](int stage, int kk, u32x4 (&af)[C::FM], u32x4 (&bfr)[C::FN]) {
+    auto read16 = [&](const uint8_t* a) { return *(const u32x4*)a; };
+    // fragments of one k sub-step (kk) of the step held in `stage`
+    auto load_frags = [&](int stage, int kk, Frag (&af)[C::FM], Frag (&bfr)[C::FN]) {
         const uint8_t* st = smem + stage * C::STAGE;
 #pragma unroll
         for (int f = 0; f < C::FN; ++f) {
-            if constexpr (OPB == GE_OP_T) {
-                bfr[f] = *(const u32x4*)(st + offB[f][kk][0]);
-            } else {
+            if constexpr (OPB == GE_OP_T && ESZ == 2) {
+                bfr[f] = read16(st + offB[f][kk][0]);
+            } else if constexpr (OPB == GE_OP_T) {
+                const u32x4 lo = read16(st + offB[f][kk][0]), hi = read16(st + offB[f][kk][1]);
+                bfr[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else if constexpr (ESZ == 2) {
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -256,12 +317,27 @@ ge_tile2_kernel(KernelArgs p) {
                                (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                                (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
                                (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+            } else {
+                i32x2 v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_i32x2_t*)((lds_void_t*)(st + offB[f][kk][e])));
+                bfr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
             }
         }
 #pragma unroll
-        for (int f = 0; f < C::FM; ++f) af[f] = *(const u32x4*)(st + offA[f][kk]);
+        for (int f = 0; f < C::FM; ++f) {
+            if constexpr (ESZ == 2) {
+                af[f] = read16(st + offA[f][kk][0]);
+            } else {
+                const u32x4 lo = read16(st + offA[f][kk][0]), hi = read16(st + offA[f][kk][1]);
+                af[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
     };
-    auto mfmas = [&](const u32x4 (&af)[C::FM], const u32x4 (&bfr)[C::FN]) {
+    auto mfmas = [&](const Frag (&af)[C::FM], const Frag (&bfr)[C::FN]) {
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -269,18 +345,21 @@ ge_tile2_kernel(KernelArgs p) {
                 if constexpr (DIN == GE_BF16)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, bfr[i]), __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0, 0, 0);
-                else
+                else if constexpr (DIN == GE_F16)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0, 0, 0);
+                else   // OCP E4M3 operands (format code 0 for both), no block scales
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[i], af[j], acc[i][j], 0, 0,
+                                                                                 0, 0, 0, 0);
             }
     };
     // Wait until this wave's copies of step t are done, given that the
-    // copies of steps t+1 .. last_issued were issued after them.
+    // copies of `later` further steps were issued after them.
     auto wait_step = [&](int later) {
-        static_assert(S <= 5, "wait ladder covers up to 4 later steps");
+        static_assert(SE <= 5, "wait ladder covers up to 4 later steps");
         if (later >= 4) wait_vm<(4 * C::VM_PER_STEP < 64 ? 4 * C::VM_PER_STEP : 63)>();
         else if (later == 3) wait_vm<(3 * C::VM_PER_STEP < 64 ? 3 * C::VM_PER_STEP : 63)>();
-        else if (later == 2) wait_vm<2 * C::VM_PER_STEP>();
+        else if (later == 2) wait_vm<(2 * C::VM_PER_STEP < 64 ? 2 * C::VM_PER_STEP : 63)>();
         else if (later == 1) wait_vm<C::VM_PER_STEP>();
         else wait_vm<0>();
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads and tail writes done
@@ -290,17 +369,17 @@ ge_tile2_kernel(KernelArgs p) {
     };
 
     // ---- main loop ----
-    // All S stages start filling at once; afterwards the copy of step
-    // kt + S goes into the stage step kt used, as soon as every wave has
+    // All SE stages start filling at once; afterwards the copy of step
+    // kt + SE goes into the stage step kt used, as soon as every wave has
     // read its last fragments from it.  The barrier sits between the two
-    // k16 halves of a step, so the first fragments of step kt + 1 are read
+    // k sub-steps of a step, so the first fragments of step kt + 1 are read
     // while the matrix cores still work on step kt.
 #pragma unroll
-    for (int t = 0; t < S; ++t)
+    for (int t = 0; t < SE; ++t)
         if (t < KT) issue(t);
-    u32x4 a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    Frag a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
     if (KT > 0) {
-        wait_step(min(S - 1, KT - 1));
+        wait_step(min(SE - 1, KT - 1));
         load_frags(0, 0, a0, b0);
     }
     // (the last step is peeled off so that the loop body always passes the
@@ -310,22 +389,27 @@ ge_tile2_kernel(KernelArgs p) {
         // each group of fragment reads is issued ahead of the MFMAs that do
         // not need it (the scheduler would otherwise sink the last reads to
         // the end of the block and stall the next MFMAs on them)
-        load_frags(kt % S, 1, a1, b1);
+        load_frags(kt % SE, 1, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
         mfmas(a0, b0);
-        wait_step(min(S - 2, KT - 2 - kt));
-        if (kt + S < KT) issue(kt + S);
-        load_frags((kt + 1) % S, 0, a0, b0);
+        wait_step(min(SE - 2, KT - 2 - kt));
+        if (kt + SE < KT) issue(kt + SE);
+        load_frags((kt + 1) % SE, 0, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
         mfmas(a1, b1);
     }
     if (KT > 0) {
-        load_frags((KT - 1) % S, 1, a1, b1);
+        load_frags((KT - 1) % SE, 1, a1, b1);
         mfmas(a0, b0);
         mfmas(a1, b1);
     }
 
     // ---- fused epilogue on the accumulators (as in tile_kernel.h) ----
+    float s = 1.0f;   // per-tensor dequantisation of fp8 operands
+    if constexpr (DIN == GE_F8_E4M3) {
+        if (p.scale_a) s *= *p.scale_a;
+        if (p.scale_b) s *= *p.scale_b;
+    }
     const int ep = p.epilog;
     const bool has_bias = ep != GE_EPILOG_NONE;
     const bool row_bias = p.axis == GE_BIAS_ROW;
@@ -369,7 +453,7 @@ ge_tile2_kernel(KernelArgs p) {
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float x = v[g][j] + bc[j];
+                    const float x = v[g][j] * s + bc[j];
                     if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
                     v[g][j] = activate(ep, x);
                 }

@@ -430,5 +430,6 @@ TileFn pick_tile_bf16(int d_type, int op_b, int tile_id);
 TileFn pick_tile_f8(int d_type, int op_b, int tile_id);
 TileFn pick_tile2_f16(int d_type, int op_b, int tile_id);
 TileFn pick_tile2_bf16(int d_type, int op_b, int tile_id);
+TileFn pick_tile2_f8(int d_type, int op_b, int tile_id);
 
 }  // namespace ge

@@ -56,41 +56,53 @@ def test_every_tile_shape(tile, a, d, op_b):
 
 
 PIPELINED = [5, 6, 7, 8]
-COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32")]
+COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
+            ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
 
 
 @pytest.mark.parametrize("tile", PIPELINED)
 @pytest.mark.parametrize("a,d", COMBOS16, ids=[f"{a}->{d}" for a, d in COMBOS16])
 @pytest.mark.parametrize("op_b", [0, 1])
 def test_pipelined_tiles_ragged(tile, a, d, op_b):
-    # the direct-to-LDS kernel: ragged m and n (clamped copies), k = 200 (six
-    # full 32-deep steps plus a register-loaded tail of 8), padded leading
-    # dimensions with NaN padding, both bias axes
+    # the direct-to-LDS kernel: ragged m and n (clamped copies), k = 200 for
+    # 16-bit inputs (six full 32-deep steps plus a register-loaded tail of 8)
+    # and 456 for fp8 (three full 128-deep steps plus a tail of 72), padded
+    # leading dimensions with NaN padding, both bias axes
+    k = 456 if a == "e4m3" else 200
     for ep, axis in (("relu_aux_bias", "row"), ("gelu_bias", "col")):
-        w = wl(300, 520, 200, a, d, ep, axis, op_b, seed=tile * 10 + op_b)
+        w = wl(300, 520, k, a, d, ep, axis, op_b, seed=tile * 10 + op_b)
         r = run_library(w, synth.make_inputs(w), pad=2, path=1, tile=tile)
         assert f"tile_id={tile} kernel=2" in r.desc
         check_full(w, r)
 
 
-@pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129])
-@pytest.mark.parametrize("tile", [5, 8])
-def test_pipelined_short_and_ragged_k(k, tile):
+@pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129, 256, 385, 512])
+@pytest.mark.parametrize("tile", [5, 6, 8])
+@pytest.mark.parametrize("a", ["bf16", "e4m3"])
+def test_pipelined_short_and_ragged_k(k, tile, a):
     # fewer K steps than pipeline stages, exact multiples and one-element tails
     for op_b in (0, 1):
-        w = wl(130, 136, k, "bf16", "bf16", "bias", "row", op_b, seed=k)
+        w = wl(130, 136, k, a, "bf16", "bias", "row", op_b, seed=k)
         r = run_library(w, synth.make_inputs(w), pad=1, path=1, tile=tile)
         check_full(w, r)
 
 
 @pytest.mark.parametrize("tile", PIPELINED)
 @pytest.mark.parametrize("op_b", [0, 1])
-def test_pipelined_integer_bit_exact(tile, op_b):
+@pytest.mark.parametrize("a", ["bf16", "e4m3"])
+def test_pipelined_integer_bit_exact(tile, op_b, a):
     """Integer inputs: every fp32 partial sum is exact, so the pipelined
-    kernel must reproduce the RNE encoding of the exact result bit for bit."""
+    kernel must reproduce the RNE encoding of the exact result bit for bit
+    (fp8: small integers are exact E4M3 codes, unit scales)."""
     m, n, k = 512, 384, 1056
-    w = wl(m, n, k, "bf16", "bf16", "relu_bias", "col", op_b)
+    w = wl(m, n, k, a, "bf16", "relu_bias", "col", op_b)
     inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    if a == "e4m3":
+        g = torch.Generator().manual_seed(5)
+        inp.A = torch.randint(-4, 5, (m, k), generator=g).float().to(torch.float8_e4m3fn)
+        inp.B = torch.randint(-4, 5, (n, k) if op_b else (k, n), generator=g).float().to(torch.float8_e4m3fn)
+        inp.scale_a = torch.ones(1)
+        inp.scale_b = torch.ones(1)
     r = run_library(w, inp, path=1, tile=tile)
     from parity import oracle_full
     Y, P, _ = oracle_full(w, r)
