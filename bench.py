@@ -87,18 +87,28 @@ def traffic_for(workload: str):
 
 # ---- profile digest (host only) ------------------------------------------------------
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -d {d}/prof_{wl}_trace -o run --output-format csv "
+    "trace": "rocprofv3 --kernel-trace --stats -d {d}/prof_{wll}_trace -o run --output-format csv "
              "-- python3 bench.py --workload {wl} --steps {steps} --warmup 2 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_{wl}_fetch -o run --output-format csv "
-             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused",
-    "write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_{wl}_write -o run --output-format csv "
-             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_{wll}_fetch -o run --output-format csv "
+             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused "
+             "--no-graph",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_{wll}_write -o run --output-format csv "
+             "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused "
+             "--no-graph",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_copy_fetch -o run --output-format csv "
                   "-- python3 bench.py --copy-calibration 1024 --steps 3",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_copy_write -o run --output-format csv "
                   "-- python3 bench.py --copy-calibration 1024 --steps 3",
 }
-FUSED_KERNEL = {"C3": "ge_smallm_kernel"}   # others: the tile kernel
+
+def _dominant(stats):
+    """The fused kernel: the library kernel (ge::ge_*, not the unfused pair's
+    elementwise pass or the counter clear) with the most GPU time."""
+    cands = [r for r in stats if "ge::ge_" in r["Name"] and "ge_ew_kernel" not in r["Name"]
+             and "ge_clear" not in r["Name"]]
+    if not cands:
+        raise SystemExit("digest: no fused library kernel in the kernel stats")
+    return max(cands, key=lambda r: float(r["TotalDurationNs"]))
 
 
 def _csv(path):
@@ -133,15 +143,12 @@ def digest(d: str, wl: str):
     line, so the figure is dropped once the kernel changes."""
     import synth
     w = synth.WORKLOADS[wl]
-    part = FUSED_KERNEL.get(wl, "ge_tile_kernel")
     stats = _csv(os.path.join(d, f"prof_{wl.lower()}_trace", "run_kernel_stats.csv"))
     run = _last_json(os.path.join(d, f"prof_{wl.lower()}_trace.log"))
     if run is None:
         raise SystemExit("digest: the traced bench run printed no JSON line")
-    fused = [r for r in stats if part in r["Name"]]
-    if not fused:
-        raise SystemExit(f"digest: {part} not in the kernel stats")
-    k = fused[0]
+    k = _dominant(stats)
+    part = k["Name"].split("(")[0].replace("void ", "")   # template name with arguments
     avg_ns = float(k["AverageNs"])
     fetch_kib, nf, kname = _counter_avg(os.path.join(d, f"prof_{wl.lower()}_fetch"), part, "FETCH_SIZE")
     write_kib, nw, _ = _counter_avg(os.path.join(d, f"prof_{wl.lower()}_write"), part, "WRITE_SIZE")
@@ -154,10 +161,9 @@ def digest(d: str, wl: str):
     traffic = read_b + write_b
     alg = w.algorithmic_bytes()
     steps = run.get("steps", 10)
-    cmds = {key: c.format(d="gpurun_out", wl=wl.lower() if "{wl}_" in c else wl, steps=steps)
+    cmds = {key: c.format(d="gpurun_out", wl=wl, wll=wl.lower(), steps=steps)
             for key, c in PROFILE_COMMANDS.items()}
-    cmds = {key: c.replace(f"prof_{wl}_", f"prof_{wl.lower()}_") for key, c in cmds.items()}
-    name = f"{part}_{wl}"
+    name = part.replace("ge::", "").split("<")[0] + "_" + wl
     lines = [
         f"# {part} on {w.name}",
         "",
