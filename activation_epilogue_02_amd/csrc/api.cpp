@@ -85,10 +85,11 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
     if (a_type == GE_F16 || a_type == GE_BF16) {
         // the pipelined direct-to-LDS kernel; at 256 x 256 the 8-wave
         // layout (two waves per SIMD fill each other's barrier and copy
-        // gaps) measures faster than 4 waves
-        if (t256 >= 512) return 6;
+        // gaps) with 128-byte K steps (full-line A requests, half the
+        // barriers) measures fastest
+        if (t256 >= 512) return 11;
         if (t128 >= 512) return 8;
-        if (t256 >= 256 && t128 < 256) return 6;
+        if (t256 >= 256 && t128 < 256) return 11;
         if (t128 >= 256) return 8;
         return 1;
     }
@@ -326,7 +327,7 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
              h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
              t ? t->wn : 8, h->tile_id, t ? t->kernel : 0,
-             t ? (t->kernel == 2 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
+             t ? (t->kernel == 2 || t->kernel == 4 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
              h->split_k,
              h->unfused,
              h->ws_c + h->ws_partial + h->ws_counters, (long long)h->ldaux);

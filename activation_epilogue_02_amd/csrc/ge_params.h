@@ -37,10 +37,14 @@ enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 // Kernel 1 (tile_kernel.h): register-staged, two LDS stages, every dtype.
 // Kernel 2 (tile2_kernel.h): direct-to-LDS copies through up to `stages`
 // LDS stages (as many as fit in 160 KiB), fp16/bf16/fp8 inputs.
+// Kernel 3: the same kernel with register-staged copies (global loads two
+// steps ahead into registers, then LDS writes; two LDS stages).
+// Kernel 4: the same kernel with 128-byte K steps for 16-bit inputs (64 k
+// per step, four MFMA sub-steps, two 64 KiB stages at 256 x 256).
 struct TileShape {
     int32_t id, bm, bn, wm, wn, kernel, stages;
 };
-constexpr int kNumTiles = 8;
+constexpr int kNumTiles = 12;
 constexpr TileShape kTiles[kNumTiles] = {
     {1, 64, 64, 2, 2, 1, 2},     // 4 waves, 32 x 32 per wave
     {2, 128, 128, 2, 2, 1, 2},   // 4 waves, 64 x 64 per wave
@@ -50,12 +54,16 @@ constexpr TileShape kTiles[kNumTiles] = {
     {6, 256, 256, 2, 4, 2, 4},   // 8 waves, 128 x 64 per wave
     {7, 256, 128, 2, 2, 2, 4},   // 4 waves, 128 x 64 per wave
     {8, 128, 128, 2, 2, 2, 4},   // 4 waves, 64 x 64 per wave
+    {9, 256, 256, 2, 4, 3, 2},   // register-staged copies: 8 waves
+    {10, 256, 256, 2, 2, 3, 2},  // register-staged copies: 4 waves
+    {11, 256, 256, 2, 4, 4, 2},  // 128-byte K steps for 16-bit inputs: 8 waves
+    {12, 256, 256, 2, 2, 4, 2},  // 128-byte K steps for 16-bit inputs: 4 waves
 };
 
 // LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64
 // bytes (16-bit inputs) or 128 bytes (fp8); at most 160 KiB in total.
 constexpr int tile2_stages(const TileShape& t, int elem_size) {
-    const int stage = (t.bm + t.bn) * (elem_size == 1 ? 128 : 64);
+    const int stage = (t.bm + t.bn) * (elem_size == 1 || t.kernel == 4 ? 128 : 64);
     return t.stages * stage <= 160 * 1024 ? t.stages : (160 * 1024) / stage;
 }
 

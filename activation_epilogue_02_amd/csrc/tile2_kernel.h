@@ -103,19 +103,22 @@ __device__ __forceinline__ int swz_kn8(int k, int cpr) {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S>
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB>
 struct Tile2Cfg {
     static constexpr int NW = WM * WN, NT = NW * 64;
     static constexpr int ESZ = Elem<DIN>::size;
-    static constexpr int ROWB = ESZ == 1 ? 128 : 64;  // bytes of an A (or n x k B) row per K step
-    static constexpr int BK = ROWB / ESZ;             // K elements per step: 32 (16-bit) or 128 (fp8)
+    static constexpr int ROWB = ESZ == 1 ? 128 : RB;  // bytes of an A (or n x k B) row per K step
+    static constexpr int BK = ROWB / ESZ;             // K elements per step: 32/64 (16-bit) or 128 (fp8)
+    static constexpr int NKK = ESZ == 1 ? 2 : ROWB / 32;   // MFMA k sub-steps per step (even)
     static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row: 4 or 8
     static constexpr int RPC = 1024 / ROWB;           // rows per 1 KiB copy
     static constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
     static constexpr int A_BYTES = BM * ROWB;
     static constexpr int B_BYTES = BK * BN * ESZ;     // same for both B layouts
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int SE = S * STAGE <= 160 * 1024 ? S : (160 * 1024) / STAGE;   // stages that fit
+    // stages that fit; the register-staged copy uses two (its lookahead is
+    // in registers)
+    static constexpr int SE = REG ? 2 : (S * STAGE <= 160 * 1024 ? S : (160 * 1024) / STAGE);
     static constexpr int A_INS = A_BYTES / 1024 / NW;   // 1 KiB copies per wave per step
     static constexpr int B_INS = B_BYTES / 1024 / NW;
     static constexpr int VM_PER_STEP = A_INS + B_INS;
@@ -134,6 +137,8 @@ struct Tile2Cfg {
                   "[k][n] swizzle tables cover 256..1024-byte (16-bit) or 128/256-byte (fp8) rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(SE >= 2, "LDS budget");
+    static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
+    static_assert(NKK % 2 == 0, "fragment sets alternate over an even number of sub-steps");
     static_assert((SE - 1) * VM_PER_STEP < 64, "vmcnt range");
 };
 
@@ -144,10 +149,10 @@ __device__ __forceinline__ int swz_row(int row) {
     else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
 }
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S>
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB>
 __global__ void __launch_bounds__(WM* WN * 64)
 ge_tile2_kernel(KernelArgs p) {
-    using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S>;
+    using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB>;
     constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
     using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SE * C::STAGE];
@@ -251,12 +256,12 @@ ge_tile2_kernel(KernelArgs p) {
     // to (lane half, operand element) is valid as long as A and B use the
     // same one.  16-bit: sub-step kk, lane half h reads k 16kk + 8h .. +7.
     // fp8: sub-step kk, lane half h reads k 64kk + 32h .. +31.
-    int offA[C::FM][2][C::NRA];
+    int offA[C::FM][C::NKK][C::NRA];
 #pragma unroll
     for (int f = 0; f < C::FM; ++f) {
         const int row = wm * C::TM + f * 32 + r32;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
             for (int e = 0; e < C::NRA; ++e) {
                 const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
@@ -268,11 +273,11 @@ ge_tile2_kernel(KernelArgs p) {
     //          n = wave col + 32f + 16(G%2) + 4(i%4);
     //  fp8, read e of 4:    group G, lane i: k = 64kk + 32(G/2) + 8e + i/2,
     //          n = wave col + 32f + 16(G%2) + 8(i%2).
-    int offB[C::FN][2][C::NRB];
+    int offB[C::FN][C::NKK][C::NRB];
 #pragma unroll
     for (int f = 0; f < C::FN; ++f) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < C::NKK; ++kk) {
 #pragma unroll
             for (int e = 0; e < C::NRB; ++e) {
                 if constexpr (OPB == GE_OP_T) {
@@ -368,6 +373,86 @@ ge_tile2_kernel(KernelArgs p) {
         asm volatile("s_barrier" ::: "memory");
     };
 
+    if constexpr (REG) {
+        static_assert(C::NKK == 2, "the register-staged loop takes two sub-steps per step");
+        // ---- main loop, register-staged copies ----
+        // Step t is fetched from global memory into register set t % 2 two
+        // steps before it is written to LDS stage t % 2, right after the
+        // barrier that frees that stage; it is read after the next barrier.
+        // The compiler tracks these loads itself (no hand-counted waits).
+        u32x4 ra0[C::A_INS], rb0[C::B_INS], ra1[C::A_INS], rb1[C::B_INS];
+        auto fetch = [&](int t, u32x4 (&ra)[C::A_INS], u32x4 (&rb)[C::B_INS]) {
+            if (t >= KT) return;
+            if (t < KF) {
+#pragma unroll
+                for (int i = 0; i < C::A_INS; ++i) ra[i] = *(const u32x4*)(srcA[i] + (int64_t)t * stepA);
+#pragma unroll
+                for (int i = 0; i < C::B_INS; ++i) rb[i] = *(const u32x4*)(srcB[i] + (int64_t)t * stepB);
+            } else {
+                const int k0 = t * BK;
+#pragma unroll
+                for (int i = 0; i < C::A_INS; ++i)
+                    ra[i] = load_chunk<ESZ>(gA, p.lda, min(rowA_cp[i], max(M - 1, 0)), M, k0 + chA_cp[i] * EPC, K);
+#pragma unroll
+                for (int i = 0; i < C::B_INS; ++i) {
+                    if constexpr (OPB == GE_OP_T)
+                        rb[i] = load_chunk<ESZ>(gB, p.ldb, min(rowB_cp[i], max(N - 1, 0)), N,
+                                                k0 + chB_cp[i] * EPC, K);
+                    else
+                        rb[i] = load_chunk<ESZ>(gB, p.ldb, k0 + rowB_cp[i], K, min(chB_cp[i], nlast), N);
+                }
+            }
+        };
+        auto commit = [&](int t, const u32x4 (&ra)[C::A_INS], const u32x4 (&rb)[C::B_INS]) {
+            if (t >= KT) return;
+            uint8_t* st = smem + (t % 2) * C::STAGE;
+#pragma unroll
+            for (int i = 0; i < C::A_INS; ++i) *(u32x4*)(st + (wave * C::A_INS + i) * 1024 + lane * 16) = ra[i];
+#pragma unroll
+            for (int i = 0; i < C::B_INS; ++i)
+                *(u32x4*)(st + C::A_BYTES + (wave * C::B_INS + i) * 1024 + lane * 16) = rb[i];
+        };
+        auto barrier = [&]() {
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads and writes done
+            asm volatile("s_barrier" ::: "memory");
+        };
+        fetch(0, ra0, rb0);
+        fetch(1, ra1, rb1);
+        commit(0, ra0, rb0);
+        commit(1, ra1, rb1);
+        fetch(2, ra0, rb0);
+        fetch(3, ra1, rb1);
+        Frag a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+        if (KT > 0) {
+            barrier();
+            load_frags(0, 0, a0, b0);
+        }
+        auto body = [&](int kt, u32x4 (&ra)[C::A_INS], u32x4 (&rb)[C::B_INS]) {
+            load_frags(kt % 2, 1, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(a0, b0);
+            barrier();
+            commit(kt + 2, ra, rb);   // into stage kt % 2, free since the barrier
+            fetch(kt + 4, ra, rb);
+            load_frags((kt + 1) % 2, 0, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(a1, b1);
+        };
+        int kt = 0;
+        for (; kt + 2 <= KT - 1; kt += 2) {
+            body(kt, ra0, rb0);
+            body(kt + 1, ra1, rb1);
+        }
+        if (kt < KT - 1) {
+            body(kt, ra0, rb0);
+            ++kt;
+        }
+        if (KT > 0) {
+            load_frags((KT - 1) % 2, 1, a1, b1);
+            mfmas(a0, b0);
+            mfmas(a1, b1);
+        }
+    } else {
     // ---- main loop ----
     // All SE stages start filling at once; afterwards the copy of step
     // kt + SE goes into the stage step kt used, as soon as every wave has
@@ -385,24 +470,38 @@ ge_tile2_kernel(KernelArgs p) {
     // (the last step is peeled off so that the loop body always passes the
     // barrier: a merged path would make the compiler's wait analysis hold
     // the second-half MFMAs until the next step's fragment reads return)
+    // sub-steps kk = 0 .. NKK-2 of step kt: the fragments of sub-step kk+1
+    // are read (into the other register set) ahead of the MFMAs of kk
+    auto inner = [&](int stage) {
+#pragma unroll
+        for (int kk = 0; kk < C::NKK - 1; ++kk) {
+            // each group of fragment reads is issued ahead of the MFMAs that
+            // do not need it (the scheduler would otherwise sink the last
+            // reads to the end of the block and stall the next MFMAs on them)
+            if (kk % 2 == 0) {
+                load_frags(stage, kk + 1, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(a0, b0);
+            } else {
+                load_frags(stage, kk + 1, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(a1, b1);
+            }
+        }
+    };
     for (int kt = 0; kt < KT - 1; ++kt) {
-        // each group of fragment reads is issued ahead of the MFMAs that do
-        // not need it (the scheduler would otherwise sink the last reads to
-        // the end of the block and stall the next MFMAs on them)
-        load_frags(kt % SE, 1, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(a0, b0);
+        inner(kt % SE);
         wait_step(min(SE - 2, KT - 2 - kt));
         if (kt + SE < KT) issue(kt + SE);
         load_frags((kt + 1) % SE, 0, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(a1, b1);
+        mfmas(a1, b1);   // the last sub-step (NKK - 1 is odd)
     }
     if (KT > 0) {
-        load_frags((KT - 1) % SE, 1, a1, b1);
-        mfmas(a0, b0);
+        inner((KT - 1) % SE);
         mfmas(a1, b1);
     }
+    }   // copy mode
 
     // ---- fused epilogue on the accumulators (as in tile_kernel.h) ----
     float s = 1.0f;   // per-tensor dequantisation of fp8 operands
@@ -488,10 +587,14 @@ ge_tile2_kernel(KernelArgs p) {
 template <int DIN, int DOUT, int OPB>
 TileFn pick_tile2(int tile_id) {
     switch (tile_id) {
-    case 5: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 4>;
-    case 6: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 4>;
-    case 7: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 128, 2, 2, 4>;
-    case 8: return ge_tile2_kernel<DIN, DOUT, OPB, 128, 128, 2, 2, 4>;
+    case 5: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 4, false, 64>;
+    case 6: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 4, false, 64>;
+    case 7: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 128, 2, 2, 4, false, 64>;
+    case 8: return ge_tile2_kernel<DIN, DOUT, OPB, 128, 128, 2, 2, 4, false, 64>;
+    case 9: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 2, true, 64>;
+    case 10: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 2, true, 64>;
+    case 11: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 2, false, 128>;
+    case 12: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 2, false, 128>;
     }
     return nullptr;
 }

@@ -10,7 +10,7 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
         if (kTiles[i].id == tile_id) t = &kTiles[i];
     if (!t) return (int)hipErrorInvalidDeviceFunction;
     TileFn fn = nullptr;
-    if (t->kernel == 2) {
+    if (t->kernel >= 2) {
         if (a_type == GE_F16) fn = pick_tile2_f16(d_type, op_b, tile_id);
         else if (a_type == GE_BF16) fn = pick_tile2_bf16(d_type, op_b, tile_id);
         else if (a_type == GE_F8_E4M3) fn = pick_tile2_f8(d_type, op_b, tile_id);

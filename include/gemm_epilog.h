@@ -132,8 +132,11 @@ typedef struct {
  * tile:    0 auto, else a tile id: 1..4 the register-staged kernel (any
  *          dtype; 64x64, 128x128, 256x256, 256x128), 5..8 the pipelined
  *          direct-to-LDS kernel (fp16/bf16/fp8 inputs, not fp32; 256x256
- *          with 4 waves, 256x256 with 8 waves, 256x128, 128x128).  An id
- *          the input dtype does not support gives GE_ERR_SHAPE.
+ *          with 4 waves, 256x256 with 8 waves, 256x128, 128x128), 9..10
+ *          the same kernel with register-staged copies (256x256 with 8 or
+ *          4 waves), 11..12 with 128-byte K steps (256x256 with 8 or 4
+ *          waves).  An id the input dtype does not support gives
+ *          GE_ERR_SHAPE.
  * split_k: 0 auto, else the number of K slices (small-m path only) */
 typedef struct {
     int32_t path;

@@ -55,7 +55,7 @@ def test_every_tile_shape(tile, a, d, op_b):
     check_full(w, r)
 
 
-PIPELINED = [5, 6, 7, 8]
+PIPELINED = [5, 6, 7, 8, 9, 10, 11, 12]
 COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
             ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
 
@@ -72,12 +72,12 @@ def test_pipelined_tiles_ragged(tile, a, d, op_b):
     for ep, axis in (("relu_aux_bias", "row"), ("gelu_bias", "col")):
         w = wl(300, 520, k, a, d, ep, axis, op_b, seed=tile * 10 + op_b)
         r = run_library(w, synth.make_inputs(w), pad=2, path=1, tile=tile)
-        assert f"tile_id={tile} kernel=2" in r.desc
+        assert f"tile_id={tile} kernel={ {9: 3, 10: 3, 11: 4, 12: 4}.get(tile, 2)}" in r.desc
         check_full(w, r)
 
 
 @pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129, 256, 385, 512])
-@pytest.mark.parametrize("tile", [5, 6, 8])
+@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11])
 @pytest.mark.parametrize("a", ["bf16", "e4m3"])
 def test_pipelined_short_and_ragged_k(k, tile, a):
     # fewer K steps than pipeline stages, exact multiples and one-element tails
