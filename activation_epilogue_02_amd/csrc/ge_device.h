@@ -124,6 +124,36 @@ __device__ __forceinline__ void load8(const void* p, int64_t idx, float* v) {
     }
 }
 
+// ---- direct global -> LDS copies ---------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// LDS byte address lds + 16*l (lds must be the same for the whole wave; it
+// goes to M0, and one wait state separates the M0 write from its use).
+// Written as inline assembly on purpose: the compiler's wait-count pass
+// would otherwise make every later LDS read wait for all copies in flight,
+// which defeats the pipeline.  Completion is tracked by hand instead
+// (wait_vm + barrier).  The compiler's own vmcnt waits for ordinary loads
+// stay correct: copies it does not count only make them wait longer.
+__device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (the other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- activations -------------------------------------------------------------
 // GELU in its tanh form, 0.5 x (1 + tanh(u)) with u = sqrt(2/pi)(x + 0.044715 x^3).
 // Since 0.5 (1 + tanh u) = 1 / (1 + e^{-2u}), this is x / (1 + 2^{-2u log2 e}),
