@@ -91,7 +91,7 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
         if (t128 >= 512) return 8;
         if (t256 >= 256 && t128 < 256) return 11;
         if (t128 >= 256) return 8;
-        return 1;
+        return 13;   // small problems: 64 x 64 tiles, four deep stages
     }
     if (t256 >= 512) return 3;
     if (t128 >= 512) return 2;
@@ -100,9 +100,12 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
     return 1;
 }
 
-// The pipelined kernel takes 16-bit and fp8 inputs.
+// The pipelined kernel takes 16-bit and fp8 inputs (its 64 x 64 tile only
+// 16-bit ones).
 bool tile_supports(const TileShape* t, int a_type) {
-    return t->kernel == 1 || a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
+    if (t->kernel == 1) return true;
+    if (t->id == 13) return a_type == GE_F16 || a_type == GE_BF16;
+    return a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
 }
 
 bool smallm_supported(const ge_desc& d) {

@@ -44,7 +44,7 @@ enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 struct TileShape {
     int32_t id, bm, bn, wm, wn, kernel, stages;
 };
-constexpr int kNumTiles = 12;
+constexpr int kNumTiles = 13;
 constexpr TileShape kTiles[kNumTiles] = {
     {1, 64, 64, 2, 2, 1, 2},     // 4 waves, 32 x 32 per wave
     {2, 128, 128, 2, 2, 1, 2},   // 4 waves, 64 x 64 per wave
@@ -58,6 +58,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {10, 256, 256, 2, 2, 3, 2},  // register-staged copies: 4 waves
     {11, 256, 256, 2, 4, 4, 2},  // 128-byte K steps for 16-bit inputs: 8 waves
     {12, 256, 256, 2, 2, 4, 2},  // 128-byte K steps for 16-bit inputs: 4 waves
+    {13, 64, 64, 2, 2, 4, 4},    // 128-byte K steps, 16-bit inputs only: 4 waves, 32 x 32 per wave
 };
 
 // LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64

@@ -53,10 +53,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // distinct banks (64-byte rows repeat the bank pattern every 2 or 4 rows).
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// XOR swizzle of the chunks of a [k][n] LDS row (B given k x n), indexed by
-// k mod 4: the transposing reads of four consecutive k rows then cover
-// distinct banks whether a pass serves 16 or 32 lanes.
-__device__ __forceinline__ int swz_kn(int k) {
+// XOR swizzle of the chunks of a [k][n] LDS row of 16-bit B (given k x n),
+// indexed by k mod 4: the transposing reads of four consecutive k rows then
+// cover distinct banks whether a pass serves 16 or 32 lanes.  Rows of 256
+// bytes or more use the table; 128-byte rows (which alternate between the
+// halves of a 256-byte bank window) use 2 * (k mod 4).
+__device__ __forceinline__ int swz_kn(int k, int cpr) {
+    if (cpr == 8) return 2 * (k & 3);
     constexpr int t = (0 << 0) | (4 << 5) | (10 << 10) | (14 << 15);
     return (t >> (5 * (k & 3))) & 31;
 }
@@ -106,8 +109,8 @@ struct Tile2Cfg {
     static constexpr int NRB = OPB == GE_OP_T ? NRA : (ESZ == 1 ? 4 : 2);
     static_assert(DIN == GE_F16 || DIN == GE_BF16 || DIN == GE_F8_E4M3, "16-bit or fp8 inputs");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole copies per wave");
-    static_assert(OPB == GE_OP_T || (ESZ == 2 ? (KN_CPR >= 16 && KN_CPR <= 64) : (KN_CPR == 8 || KN_CPR == 16)),
-                  "[k][n] swizzle tables cover 256..1024-byte (16-bit) or 128/256-byte (fp8) rows");
+    static_assert(OPB == GE_OP_T || (ESZ == 2 ? (KN_CPR >= 8 && KN_CPR <= 64) : (KN_CPR == 8 || KN_CPR == 16)),
+                  "[k][n] swizzles cover 128..1024-byte (16-bit) or 128/256-byte (fp8) rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(SE >= 2, "LDS budget");
     static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
@@ -171,7 +174,7 @@ ge_tile2_kernel(KernelArgs p) {
             srcB[i] = gB + ((int64_t)gn * p.ldb + c * EPC) * ESZ;
         } else {
             const int kr = (wave * C::B_INS + i) * C::KN_RPI + lane / C::KN_CPR;
-            const int c = (lane % C::KN_CPR) ^ (ESZ == 1 ? swz_kn8(kr, C::KN_CPR) : swz_kn(kr));
+            const int c = (lane % C::KN_CPR) ^ (ESZ == 1 ? swz_kn8(kr, C::KN_CPR) : swz_kn(kr, C::KN_CPR));
             const int gn = min(n0 + c * EPC, nlast);
             rowB_cp[i] = kr;
             chB_cp[i] = n0 + c * EPC;
@@ -262,7 +265,7 @@ ge_tile2_kernel(KernelArgs p) {
                     const int k = 16 * kk + 8 * (G >> 1) + 4 * e + (i >> 2);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 4 * (i & 3);
                     offB[f][kk][e] =
-                        C::A_BYTES + k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k)) << 4) + ((n & 4) << 1);
+                        C::A_BYTES + k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k, C::KN_CPR)) << 4) + ((n & 4) << 1);
                 } else {
                     const int G = lane >> 4, i = lane & 15;
                     const int k = 64 * kk + 32 * (G >> 1) + 8 * e + (i >> 1);
@@ -568,6 +571,9 @@ TileFn pick_tile2(int tile_id) {
     case 10: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 2, true, 64>;
     case 11: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 2, false, 128>;
     case 12: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 2, false, 128>;
+    case 13:   // 16-bit inputs only (64-byte fp8 k rows have no swizzle here)
+        if constexpr (Elem<DIN>::size == 2) return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128>;
+        else return nullptr;
     }
     return nullptr;
 }

@@ -135,8 +135,8 @@ typedef struct {
  *          with 4 waves, 256x256 with 8 waves, 256x128, 128x128), 9..10
  *          the same kernel with register-staged copies (256x256 with 8 or
  *          4 waves), 11..12 with 128-byte K steps (256x256 with 8 or 4
- *          waves).  An id the input dtype does not support gives
- *          GE_ERR_SHAPE.
+ *          waves), 13 a 64x64 tile of it (fp16/bf16 only).  An id the input
+ *          dtype does not support gives GE_ERR_SHAPE.
  * split_k: 0 auto, else the number of K slices (small-m path only) */
 typedef struct {
     int32_t path;

@@ -174,7 +174,7 @@ def test_forced_launch_failure_hook(monkeypatch):
     (65536, 8192, 16384, 0, "bf16", "tile_id=11 kernel=4"),
     (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=2x2 tile_id=7 kernel=2 stages=3"),
     (4096, 1024, 4096, 1, "f16", "tile_id=8 kernel=2"),
-    (1024, 512, 2048, 0, "f16", "tile=64x64"),
+    (1024, 512, 2048, 0, "f16", "tile=64x64 waves=2x2 tile_id=13 kernel=4 stages=4"),
     (128, 64, 256, 0, "f32", "tile=64x64"),
 ])
 def test_planner_choices(m, n, k, op_b, a, expect):
@@ -187,11 +187,19 @@ def test_planner_choices(m, n, k, op_b, a, expect):
         B.gemm_epilog_free(h)
 
 
-@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12])
+@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13])
 def test_pipelined_tiles_reject_fp32_inputs(tile):
     h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "f32", "f32", 0))
     try:
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, tile, 0)) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_small_pipelined_tile_rejects_fp8():
+    h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "e4m3", "bf16", 0))
+    try:
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, 13, 0)) == B.GE_ERR_SHAPE
     finally:
         B.gemm_epilog_free(h)
 

@@ -55,15 +55,21 @@ def test_every_tile_shape(tile, a, d, op_b):
     check_full(w, r)
 
 
-PIPELINED = [5, 6, 7, 8, 9, 10, 11, 12]
+PIPELINED = [5, 6, 7, 8, 9, 10, 11, 12, 13]
 COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
             ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
+
+
+def skip_unsupported(tile, a):
+    if tile == 13 and a == "e4m3":
+        pytest.skip("the pipelined 64x64 tile takes 16-bit inputs only (planner rejects fp8)")
 
 
 @pytest.mark.parametrize("tile", PIPELINED)
 @pytest.mark.parametrize("a,d", COMBOS16, ids=[f"{a}->{d}" for a, d in COMBOS16])
 @pytest.mark.parametrize("op_b", [0, 1])
 def test_pipelined_tiles_ragged(tile, a, d, op_b):
+    skip_unsupported(tile, a)
     # the direct-to-LDS kernel: ragged m and n (clamped copies), k = 200 for
     # 16-bit inputs (six full 32-deep steps plus a register-loaded tail of 8)
     # and 456 for fp8 (three full 128-deep steps plus a tail of 72), padded
@@ -72,14 +78,15 @@ def test_pipelined_tiles_ragged(tile, a, d, op_b):
     for ep, axis in (("relu_aux_bias", "row"), ("gelu_bias", "col")):
         w = wl(300, 520, k, a, d, ep, axis, op_b, seed=tile * 10 + op_b)
         r = run_library(w, synth.make_inputs(w), pad=2, path=1, tile=tile)
-        assert f"tile_id={tile} kernel={ {9: 3, 10: 3, 11: 4, 12: 4}.get(tile, 2)}" in r.desc
+        assert f"tile_id={tile} kernel={ {9: 3, 10: 3, 11: 4, 12: 4, 13: 4}.get(tile, 2)}" in r.desc
         check_full(w, r)
 
 
 @pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129, 256, 385, 512])
-@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11])
+@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11, 13])
 @pytest.mark.parametrize("a", ["bf16", "e4m3"])
 def test_pipelined_short_and_ragged_k(k, tile, a):
+    skip_unsupported(tile, a)
     # fewer K steps than pipeline stages, exact multiples and one-element tails
     for op_b in (0, 1):
         w = wl(130, 136, k, a, "bf16", "bias", "row", op_b, seed=k)
@@ -94,6 +101,7 @@ def test_pipelined_integer_bit_exact(tile, op_b, a):
     """Integer inputs: every fp32 partial sum is exact, so the pipelined
     kernel must reproduce the RNE encoding of the exact result bit for bit
     (fp8: small integers are exact E4M3 codes, unit scales)."""
+    skip_unsupported(tile, a)
     m, n, k = 512, 384, 1056
     w = wl(m, n, k, a, "bf16", "relu_bias", "col", op_b)
     inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
