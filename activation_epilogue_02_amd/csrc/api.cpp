@@ -113,6 +113,20 @@ bool smallm_supported(const ge_desc& d) {
            (d.d_type == d.a_type || d.d_type == GE_F32);
 }
 
+// Automatic K split of the small-m path.  The kernel's register use leaves
+// room for one workgroup per CU (256 CUs), so a grid beyond 256 runs in a
+// second round that pays the whole load-latency chain again, and the
+// split's serial device-scope round trips (partial store, arrival count,
+// reload) only pay off when the column blocks alone leave CUs idle.  Hence:
+// the largest power of two that keeps the grid within one round and each of
+// the 8 waves at four or more 32-wide K steps.
+int smallm_auto_split(int64_t tiles_n, int64_t steps) {
+    constexpr int64_t kCUs = 256, kWaves = 8, kMinStepsPerWave = 4;
+    int split = 1;
+    while (tiles_n * split * 2 <= kCUs && steps >= split * 2 * kWaves * kMinStepsPerWave) split *= 2;
+    return split;
+}
+
 bool test_fail_launch() {
     const char* e = getenv("GE_TEST_FAIL_LAUNCH");
     return e && e[0] == '1';
@@ -172,8 +186,8 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.tile_id = 0;
         q.tiles_m = 1;
         q.tiles_n = (int32_t)ceil_div(d.n, 16);
-        int split = pr.split_k > 0 ? pr.split_k : 1;
         const int64_t steps = ceil_div(d.k, 32);
+        int split = pr.split_k > 0 ? pr.split_k : smallm_auto_split(q.tiles_n, steps);
         if (split > steps) split = steps > 0 ? (int)steps : 1;
         q.k_per_split = (int32_t)(ceil_div(steps, split) * 32);
         split = q.k_per_split > 0 ? (int)ceil_div(d.k, q.k_per_split) : 1;

@@ -25,6 +25,8 @@
 //    scope fence) adds the slices in slice order, so results are
 //    deterministic; it re-arms the counter for the next launch.  The bias,
 //    activation, mask and the single store run once, after the full K sum.
+#include <type_traits>
+
 #include "ge_device.h"
 
 namespace ge {
@@ -105,24 +107,28 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int s0 = s_begin;
-    for (; s0 + kUnroll <= s_full; s0 += kUnroll) {
-        u32x4 wv[kUnroll], xv[kUnroll];
+    // U steps at once: all loads first (the scheduler would otherwise
+    // trickle them out two per MFMA), then the MFMAs
+    auto batch = [&](auto u_const) {
+        constexpr int U = decltype(u_const)::value;
+        u32x4 wv[U], xv[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             wv[u] = __builtin_nontemporal_load((const u32x4*)(wrow + (s0 + u) * 32));
             xv[u] = *(const u32x4*)(xrow + (s0 + u) * 32);
         }
-        // keep the whole batch of loads ahead of the MFMAs (the scheduler
-        // would otherwise trickle them out two per MFMA)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc = mfma16<DIN, DOUT>(wv[u], xv[u], acc);
-    }
-    for (; s0 < s_full; ++s0) {
-        const u32x4 wv = __builtin_nontemporal_load((const u32x4*)(wrow + s0 * 32));
-        const u32x4 xv = *(const u32x4*)(xrow + s0 * 32);
-        acc = mfma16<DIN, DOUT>(wv, xv, acc);
-    }
+        for (int u = 0; u < U; ++u) acc = mfma16<DIN, DOUT>(wv[u], xv[u], acc);
+        s0 += U;
+    };
+    while (s0 + kUnroll <= s_full) batch(std::integral_constant<int, kUnroll>{});
+    // the rest in descending power-of-two batches, never one load at a time
+    // unless a single step is left
+    if (s0 + 8 <= s_full) batch(std::integral_constant<int, 8>{});
+    if (s0 + 4 <= s_full) batch(std::integral_constant<int, 4>{});
+    if (s0 + 2 <= s_full) batch(std::integral_constant<int, 2>{});
+    if (s0 < s_full) batch(std::integral_constant<int, 1>{});
     if (s_full >= s_begin && s_full < s_end) {
         // the ragged last step of the slice, if it falls in this wave's
         // range: elements at k >= ke are zero in both operands (0 * NaN
@@ -143,18 +149,35 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
 
     if (p.split_k > 1) {
         // publish this slice's partial, then let the last arriver finish
-        float* part = p.partial + ((int64_t)slice * p.tiles_n + nblk) * 256;
-        *(f32x4*)(part + lane * 4) = sum;
-        __threadfence();
+        // The partials are written and read with device-scope atomic
+        // accesses, which are coherent across the XCDs' separate L2s by
+        // themselves.  A device-scope fence would do instead, but on this
+        // chip it writes back and invalidates the whole L2 of the XCD, and
+        // every other workgroup there then re-fetches x from memory.
+        float* part = p.partial + ((int64_t)slice * p.tiles_n + nblk) * 256 + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(part + i, sum[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every lane's stores complete (performed at device scope) before
+        // the arrival is counted; the clobber keeps the compiler from
+        // moving either across the wait
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         int prev = 0;
-        if (lane == 0) prev = (int)atomicAdd(&p.counters[nblk], 1u);
+        if (lane == 0)
+            prev = (int)__hip_atomic_fetch_add(&p.counters[nblk], 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
         prev = __shfl(prev, 0);
         if (prev != p.split_k - 1) return;
-        __threadfence();
+        // the loads below depend on the counter's value, so they issue only
+        // after every other slice's stores have been performed (the clobber
+        // stops the compiler from hoisting them above the branch)
+        asm volatile("" ::: "memory");
         sum = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int sl = 0; sl < p.split_k; ++sl) {
-            const float* ps = p.partial + ((int64_t)sl * p.tiles_n + nblk) * 256 + lane * 4;
-            sum += __builtin_nontemporal_load((const f32x4*)ps);
+            float* ps = p.partial + ((int64_t)sl * p.tiles_n + nblk) * 256 + lane * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sum[i] += __hip_atomic_load(ps + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (lane == 0) p.counters[nblk] = 0u;   // re-arm for the next launch
     }

@@ -215,6 +215,34 @@ def test_smallm_split_workspace():
         B.gemm_epilog_free(h)
 
 
+@pytest.mark.parametrize("m,n,k,split", [
+    (16, 4096, 4096, 1),     # 256 column blocks already fill the 256 CUs
+    (16, 2048, 14336, 2),
+    (16, 1024, 16384, 4),
+    (16, 512, 8192, 8),
+    (16, 128, 65536, 32),
+    (4, 1024, 1024, 1),      # 32 K steps: 4 per wave leaves no room to split
+    (1, 1024, 2048, 2),
+])
+def test_smallm_auto_split(m, n, k, split):
+    """Without a preference the small-m path splits K while the grid stays
+    within one workgroup per CU and each wave keeps >= 4 K steps."""
+    h = B.gemm_epilog_create(B.make_desc(m, n, k, "bf16", "bf16", 1))
+    try:
+        B.gemm_epilog_plan(h, "bias", "col")
+        s = B.gemm_epilog_describe(h)
+        assert "path=smallm" in s and f"split_k={split} " in s, s
+        tiles_n = (n + 15) // 16
+        assert f"grid={tiles_n * split} " in s, s
+        ws = B.gemm_epilog_workspace_size(h)
+        assert ws == (0 if split == 1 else split * tiles_n * 1024 + ((tiles_n * 4 + 255) // 256) * 256)
+        # an explicit preference still wins
+        B.gemm_epilog_plan(h, "bias", "col", B.ge_pref(2, 0, 0, 1))
+        assert "split_k=1 " in B.gemm_epilog_describe(h)
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_status_strings():
     for s in range(10):
         assert B.gemm_epilog_status_string(s).startswith("GE_")

@@ -154,6 +154,33 @@ def test_smallm_path(m, n, k, a, d, split):
             check_full(w, r)
 
 
+@pytest.mark.parametrize("m,n,k,split", [(16, 130, 8200, 8), (4, 128, 65560, 32), (1, 1000, 4096, 4)])
+def test_smallm_auto_split_ragged(m, n, k, split):
+    """The planner's own K split (few column blocks, long K, a ragged last
+    slice and a ragged last step) against the oracle."""
+    for ep, axis in (("gelu_bias", "col"), ("relu_aux_bias", "row")):
+        w = wl(m, n, k, "bf16", "bf16", ep, axis, op_b=1, seed=n + k)
+        r = run_library(w, synth.make_inputs(w), pad=1)
+        assert "path=smallm" in r.desc and f"split_k={split} " in r.desc, r.desc
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("a,d", [("bf16", "bf16"), ("f16", "f32")])
+def test_smallm_split_integer_bit_exact(a, d):
+    """Integer inputs keep every partial and slice sum exact, so the split
+    reduction must reproduce the RNE encoding of the exact result."""
+    m, n, k = 16, 520, 8200
+    w = wl(m, n, k, a, d, "relu_bias", "col", 1)
+    inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    r = run_library(w, inp)
+    assert "split_k=4 " in r.desc, r.desc
+    from parity import oracle_full
+    Y, _, _ = oracle_full(w, r)
+    got = codes(r.D)[:, :n]
+    want = Y.astype(np.float32) if d == "f32" else oracle.encode(Y, d).reshape(Y.shape)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("a,d", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("e4m3", "bf16")])
 @pytest.mark.parametrize("ep", ["bias", "relu_aux_bias", "gelu_bias"])
 def test_unfused_pair_matches_oracle_and_fused(a, d, ep):
