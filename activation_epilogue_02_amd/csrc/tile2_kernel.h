@@ -184,15 +184,19 @@ ge_tile2_kernel(KernelArgs p) {
     const int64_t stepA = (int64_t)BK * ESZ;
     const int64_t stepB = (OPB == GE_OP_T) ? (int64_t)BK * ESZ : (int64_t)BK * p.ldb * ESZ;
 
+    // direct copy c (A copies first, then B) of full K step t into stage t % SE
+    auto copy_one = [&](int t, int c) {
+        uint8_t* st = smem + (t % SE) * C::STAGE;
+        if (c < C::A_INS)
+            copy_to_lds16(srcA[c] + (int64_t)t * stepA, lds_addr(st + (wave * C::A_INS + c) * 1024));
+        else
+            copy_to_lds16(srcB[c - C::A_INS] + (int64_t)t * stepB,
+                          lds_addr(st + C::A_BYTES + (wave * C::B_INS + c - C::A_INS) * 1024));
+    };
     // issue the direct copies of full K step t into stage t % SE
     auto issue_direct = [&](int t) {
-        uint8_t* st = smem + (t % SE) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < C::A_INS; ++i)
-            copy_to_lds16(srcA[i] + (int64_t)t * stepA, lds_addr(st + (wave * C::A_INS + i) * 1024));
-#pragma unroll
-        for (int i = 0; i < C::B_INS; ++i)
-            copy_to_lds16(srcB[i] + (int64_t)t * stepB, lds_addr(st + C::A_BYTES + (wave * C::B_INS + i) * 1024));
+        for (int c = 0; c < C::VM_PER_STEP; ++c) copy_one(t, c);
     };
 
     // the ragged last K step t: through registers, elements at k >= K zeroed
@@ -278,61 +282,83 @@ ge_tile2_kernel(KernelArgs p) {
     }
 
     auto read16 = [&](const uint8_t* a) { return *(const u32x4*)a; };
-    // fragments of one k sub-step (kk) of the step held in `stage`
-    auto load_frags = [&](int stage, int kk, Frag (&af)[C::FM], Frag (&bfr)[C::FN]) {
+    // fragment f of B (or of A) for k sub-step kk of the step held in `stage`
+    auto load_fragB = [&](int stage, int kk, int f, Frag (&bfr)[C::FN]) {
         const uint8_t* st = smem + stage * C::STAGE;
+        if constexpr (OPB == GE_OP_T && ESZ == 2) {
+            bfr[f] = read16(st + offB[f][kk][0]);
+        } else if constexpr (OPB == GE_OP_T) {
+            const u32x4 lo = read16(st + offB[f][kk][0]), hi = read16(st + offB[f][kk][1]);
+            bfr[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else if constexpr (ESZ == 2) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][1])));
+            bfr[f] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                           (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                           (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                           (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+        } else {
+            i32x2 v[4];
 #pragma unroll
-        for (int f = 0; f < C::FN; ++f) {
-            if constexpr (OPB == GE_OP_T && ESZ == 2) {
-                bfr[f] = read16(st + offB[f][kk][0]);
-            } else if constexpr (OPB == GE_OP_T) {
-                const u32x4 lo = read16(st + offB[f][kk][0]), hi = read16(st + offB[f][kk][1]);
-                bfr[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else if constexpr (ESZ == 2) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][1])));
-                bfr[f] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-            } else {
-                i32x2 v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (lds_i32x2_t*)((lds_void_t*)(st + offB[f][kk][e])));
-                bfr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
-            }
+            for (int e = 0; e < 4; ++e)
+                v[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_i32x2_t*)((lds_void_t*)(st + offB[f][kk][e])));
+            bfr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
         }
-#pragma unroll
-        for (int f = 0; f < C::FM; ++f) {
-            if constexpr (ESZ == 2) {
-                af[f] = read16(st + offA[f][kk][0]);
-            } else {
-                const u32x4 lo = read16(st + offA[f][kk][0]), hi = read16(st + offA[f][kk][1]);
-                af[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            }
+    };
+    auto load_fragA = [&](int stage, int kk, int f, Frag (&af)[C::FM]) {
+        const uint8_t* st = smem + stage * C::STAGE;
+        if constexpr (ESZ == 2) {
+            af[f] = read16(st + offA[f][kk][0]);
+        } else {
+            const u32x4 lo = read16(st + offA[f][kk][0]), hi = read16(st + offA[f][kk][1]);
+            af[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
+    };
+    // all fragments of one k sub-step (kk) of the step held in `stage`
+    auto load_frags = [&](int stage, int kk, Frag (&af)[C::FM], Frag (&bfr)[C::FN]) {
+#pragma unroll
+        for (int f = 0; f < C::FN; ++f) load_fragB(stage, kk, f, bfr);
+#pragma unroll
+        for (int f = 0; f < C::FM; ++f) load_fragA(stage, kk, f, af);
+    };
+    // MFMA number idx (B fragment idx / FM, A fragment idx % FM) of a sub-step
+    auto mfma_one = [&](int idx, const Frag (&af)[C::FM], const Frag (&bfr)[C::FN]) {
+        const int i = idx / C::FM, j = idx % C::FM;
+        if constexpr (DIN == GE_BF16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, bfr[i]), __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0, 0, 0);
+        else if constexpr (DIN == GE_F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0, 0, 0);
+        else   // OCP E4M3 operands (format code 0 for both), no block scales
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[i], af[j], acc[i][j], 0, 0, 0, 0,
+                                                                         0, 0);
     };
     auto mfmas = [&](const Frag (&af)[C::FM], const Frag (&bfr)[C::FN]) {
 #pragma unroll
-        for (int i = 0; i < C::FN; ++i)
+        for (int idx = 0; idx < C::FM * C::FN; ++idx) mfma_one(idx, af, bfr);
+    };
+    // Scheduling order for a region holding one sub-step's MFMAs and the
+    // next sub-step's fragment reads: LDS read and MFMA alternate, so the
+    // matrix core is never left waiting behind a burst of reads.  With fewer
+    // than four MFMAs per sub-step (the 64 x 64 tile) there is nothing to
+    // alternate with, and the reads simply go first.
+    auto interleave = [&]() {
+        constexpr int NMF = C::FM * C::FN;
+        constexpr int NDS = C::FM * C::NRA + C::FN * C::NRB;
+        if constexpr (NMF >= 4) {
 #pragma unroll
-            for (int j = 0; j < C::FM; ++j) {
-                if constexpr (DIN == GE_BF16)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, bfr[i]), __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0, 0, 0);
-                else if constexpr (DIN == GE_F16)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0, 0, 0);
-                else   // OCP E4M3 operands (format code 0 for both), no block scales
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[i], af[j], acc[i][j], 0, 0,
-                                                                                 0, 0, 0, 0);
+            for (int i = 0; i < (NMF > NDS ? NMF : NDS); ++i) {
+                if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                if (i < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     // Wait until this wave's copies of step t are done, given that the
     // copies of `later` further steps were issued after them.
@@ -448,6 +474,10 @@ ge_tile2_kernel(KernelArgs p) {
     // the second-half MFMAs until the next step's fragment reads return)
     // sub-steps kk = 0 .. NKK-2 of step kt: the fragments of sub-step kk+1
     // are read (into the other register set) ahead of the MFMAs of kk
+    // (small tiles: a fence between the reads and the MFMAs, as above)
+    auto reads_first = [&]() {
+        if constexpr (C::FM * C::FN < 4) __builtin_amdgcn_sched_barrier(0);
+    };
     auto inner = [&](int stage) {
 #pragma unroll
         for (int kk = 0; kk < C::NKK - 1; ++kk) {
@@ -456,22 +486,27 @@ ge_tile2_kernel(KernelArgs p) {
             // reads to the end of the block and stall the next MFMAs on them)
             if (kk % 2 == 0) {
                 load_frags(stage, kk + 1, a1, b1);
-                __builtin_amdgcn_sched_barrier(0);
+                reads_first();
                 mfmas(a0, b0);
             } else {
                 load_frags(stage, kk + 1, a0, b0);
-                __builtin_amdgcn_sched_barrier(0);
+                reads_first();
                 mfmas(a1, b1);
             }
+            interleave();
         }
     };
     for (int kt = 0; kt < KT - 1; ++kt) {
         inner(kt % SE);
         wait_step(min(SE - 2, KT - 2 - kt));
         if (kt + SE < KT) issue(kt + SE);
-        load_frags((kt + 1) % SE, 0, a0, b0);
+        // the copies stay ahead of the reads below; the last sub-step's
+        // MFMAs interleave with the reads of step kt + 1's first fragments
         __builtin_amdgcn_sched_barrier(0);
+        load_frags((kt + 1) % SE, 0, a0, b0);
+        reads_first();
         mfmas(a1, b1);   // the last sub-step (NKK - 1 is odd)
+        interleave();
     }
     if (KT > 0) {
         inner((KT - 1) % SE);
