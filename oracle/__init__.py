@@ -26,7 +26,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # Oracle-private codes (independent of the library's enums).
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 EPILOGS = {"none": 0, "bias": 1, "relu_bias": 2, "relu_aux_bias": 3,
-           "gelu_bias": 4, "gelu_erf": 5}
+           "gelu_bias": 4, "gelu_erf": 5, "gelu_aux_bias": 4}   # O5's Y is O3's GELU
 AXES = {"row": 0, "col": 1}
 _NP_CODE_TYPE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16,
                  "e4m3": np.uint8}
@@ -82,6 +82,10 @@ def lib():
                                        ctypes.c_int, vp, vp]
         L.orc_act.argtypes = [i64, ctypes.c_int, vp, vp]
         L.orc_mask.argtypes = [i64, i64, vp, i64, vp]
+        L.orc_gelu_deriv.restype = dbl
+        L.orc_gelu_deriv.argtypes = [dbl]
+        L.orc_drelu.argtypes = [i64, i64, vp, i64, vp, vp]
+        L.orc_dgelu.argtypes = [i64, i64, vp, ctypes.c_int, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -209,6 +213,35 @@ def mask_pass(P: np.ndarray, ldw: int) -> np.ndarray:
     W = np.empty((m, ldw), dtype=np.uint32)
     _check(lib().orc_mask(m, n, _ptr(P), ldw, _ptr(W)), "mask")
     return W
+
+
+def gelu_deriv(x: float) -> float:
+    """GELU'(x) of the tanh form (the derivative used by O7)."""
+    return lib().orc_gelu_deriv(float(x))
+
+
+def drelu_pass(C: np.ndarray, words: np.ndarray) -> np.ndarray:
+    """O6: D = C where the O4 mask bit is set, else 0.  words: uint32 (m, ldw)."""
+    C = np.ascontiguousarray(C, dtype=np.float64)
+    m, n = C.shape
+    W = np.ascontiguousarray(words, dtype=np.uint32)
+    if W.shape[0] != m:
+        raise ValueError("oracle drelu: mask rows differ from C's")
+    D = np.empty_like(C)
+    _check(lib().orc_drelu(m, n, _ptr(C), W.shape[1], _ptr(W), _ptr(D)), "drelu")
+    return D
+
+
+def dgelu_pass(C: np.ndarray, P: np.ndarray, tp: str) -> np.ndarray:
+    """O7: D = C * GELU'(P), P given as raw codes of dtype tp, shape (m, ldp)."""
+    C = np.ascontiguousarray(C, dtype=np.float64)
+    m, n = C.shape
+    Pc = _codes(P, tp)
+    if Pc.shape[0] != m:
+        raise ValueError("oracle dgelu: aux rows differ from C's")
+    D = np.empty_like(C)
+    _check(lib().orc_dgelu(m, n, _ptr(C), DTYPES[tp], _ptr(Pc), Pc.shape[1], _ptr(D)), "dgelu")
+    return D
 
 
 def reference(A, ta, B, tb, bias, tbias, epilog, axis, op_b=0, sa=1.0, sb=1.0,

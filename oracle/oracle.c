@@ -317,3 +317,53 @@ int orc_mask(int64_t m, int64_t n, const double* P, int64_t ldw, uint32_t* words
             if (P[i * n + j] > 0.0) words[i * ldw + j / 32] |= (1u << (j % 32));
     return 0;
 }
+
+/* ---- training-side epilogues ---------------------------------------------
+ * The pages tie the aux output to the backward pass: in training the backward
+ * pass needs the intermediate activation, and a ReLU epilogue with aux output
+ * returns the mask it needs ([nvmath page], paragraph on limitations); fusing
+ * GELU and the bias gradient into the epilogue is where they see the method
+ * going next ([nvmath page], closing paragraph).  Their plainest reading, as
+ * separate passes after O1 (O2 and O3 as above where a bias is involved):
+ *
+ *   O5  GELU with aux:  Y = GELU(P) (O3) and the aux output is P itself,
+ *                       the value GELU's backward needs (stored in D's dtype);
+ *   O6  DRELU:          D = C * ReLU'(P), ReLU'(P) = (P > 0) read from the O4
+ *                       bit matrix of a forward pass (no bias);
+ *   O7  DGELU:          D = C * GELU'(P), P read from an O5 aux output.
+ *
+ * GELU' is the derivative of the tanh form, by the product and chain rules:
+ *   d/dx [0.5 x (1 + tanh u(x))] = 0.5 (1 + tanh u) + 0.5 x (1 - tanh(u)^2) u'(x)
+ *   with u = sqrt(2/pi) (x + 0.044715 x^3), u' = sqrt(2/pi) (1 + 3 * 0.044715 x^2). */
+double orc_gelu_deriv(double x)
+{
+    const double c = sqrt(2.0 / M_PI);
+    const double u = c * (x + 0.044715 * x * x * x);
+    const double du = c * (1.0 + 3.0 * 0.044715 * x * x);
+    const double t = tanh(u);
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * du;
+}
+
+/* O6: D[i][j] = C[i][j] if bit (i,j) of the O4 layout (row stride ldw words)
+ * is set, else 0. */
+int orc_drelu(int64_t m, int64_t n, const double* C, int64_t ldw, const uint32_t* words, double* D)
+{
+    if (ldw * 32 < n) return -1;
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            const uint32_t bit = (words[i * ldw + j / 32] >> (j % 32)) & 1u;
+            D[i * n + j] = bit ? C[i * n + j] : 0.0;
+        }
+    return 0;
+}
+
+/* O7: D[i][j] = C[i][j] * GELU'(P[i][j]), P given as codes of dtype tp with
+ * row stride ldp elements, decoded exactly. */
+int orc_dgelu(int64_t m, int64_t n, const double* C, int tp, const void* P, int64_t ldp, double* D)
+{
+    if (ldp < n || tp < ORC_F32 || tp > ORC_E4M3) return -1;
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            D[i * n + j] = C[i * n + j] * orc_gelu_deriv(dec_at(tp, P, i * ldp + j));
+    return 0;
+}

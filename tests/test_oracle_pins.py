@@ -314,3 +314,65 @@ def test_p11_mask_layout_vs_packbits():
     bits[:, :n] = P > 0
     ref = np.packbits(bits, axis=1, bitorder="little").view("<u4")
     assert np.array_equal(W, ref)
+
+
+# ---- training-side epilogues (O5..O7) ----------------------------------------
+def test_gelu_deriv_matches_central_difference_of_gelu():
+    """GELU' against a central difference of the oracle's own GELU (pinned
+    above by its symmetry and limits): a dropped term of the product or chain
+    rule shows as an O(1) gap, far above the O(h^2) of the difference."""
+    h = 1e-5
+    for x in np.linspace(-6.0, 6.0, 241):
+        fd = (oracle.act1(x + h, "gelu_bias") - oracle.act1(x - h, "gelu_bias")) / (2 * h)
+        assert abs(oracle.gelu_deriv(x) - fd) < 1e-8, x
+
+
+def test_gelu_deriv_symmetry_and_limits():
+    """GELU(x) - GELU(-x) = x gives GELU'(x) + GELU'(-x) = 1; GELU'(0) = 1/2;
+    GELU' -> 1 as x -> +inf and -> 0 as x -> -inf."""
+    for x in np.linspace(0.0, 8.0, 81):
+        assert abs(oracle.gelu_deriv(x) + oracle.gelu_deriv(-x) - 1.0) < 1e-14
+    assert oracle.gelu_deriv(0.0) == 0.5
+    assert abs(oracle.gelu_deriv(10.0) - 1.0) < 1e-12
+    assert abs(oracle.gelu_deriv(-10.0)) < 1e-12
+    # GELU dips below zero for negative x, so its slope changes sign there
+    assert oracle.gelu_deriv(-1.0) < 0.0 < oracle.gelu_deriv(-0.5)
+
+
+def test_drelu_selects_by_mask_bits_vs_unpackbits():
+    """O6 reads the O4 layout: checked against numpy's own bit unpacking of a
+    random mask (little-endian bit order, 128-bit padded rows)."""
+    rng = np.random.default_rng(7)
+    m, n = 5, 200
+    ldw = ((n + 127) // 128) * 4
+    W = rng.integers(0, 2 ** 32, size=(m, ldw), dtype=np.uint64).astype(np.uint32)
+    C = rng.standard_normal((m, n))
+    D = oracle.drelu_pass(C, W)
+    bits = np.unpackbits(W.view(np.uint8), axis=1, bitorder="little")[:, :n].astype(bool)
+    assert np.array_equal(D, np.where(bits, C, 0.0))
+
+
+def test_drelu_after_forward_mask_is_relu_derivative():
+    """With C = 1, O6 applied to the O4 mask of P gives ReLU'(P) = (P > 0)."""
+    rng = np.random.default_rng(8)
+    P = rng.standard_normal((7, 130))
+    P[0, :5] = 0.0   # ReLU'(0) = 0
+    W = oracle.mask_pass(P, ((130 + 127) // 128) * 4)
+    D = oracle.drelu_pass(np.ones_like(P), W)
+    assert np.array_equal(D, (P > 0).astype(np.float64))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_dgelu_is_upstream_times_slope_of_gelu(dt):
+    """O7 with P given as codes (padded rows): compared with a central
+    difference of O3's GELU at the exactly decoded P, times C."""
+    rng = np.random.default_rng(9)
+    m, n, ld = 4, 50, 56
+    Pf = (rng.standard_normal((m, ld)) * 2).astype(np.float32)
+    codes = {"f32": lambda x: x, "f16": f16_codes, "bf16": bf16_codes}[dt](Pf)
+    Pd = oracle.decode(np.ascontiguousarray(codes), dt)[:, :n]
+    C = rng.standard_normal((m, n))
+    D = oracle.dgelu_pass(C, np.ascontiguousarray(codes), dt)
+    h = 1e-5
+    slope = (oracle.act_pass(Pd + h, "gelu_bias") - oracle.act_pass(Pd - h, "gelu_bias")) / (2 * h)
+    assert np.allclose(D, C * slope, rtol=0, atol=1e-8)
