@@ -23,14 +23,16 @@ GE_OK, GE_ERR_NULL, GE_ERR_SHAPE, GE_ERR_DTYPE, GE_ERR_EPILOG, GE_ERR_ALIGN, \
 GE_F32, GE_F16, GE_BF16, GE_F8_E4M3 = 0, 1, 2, 3
 GE_OP_N, GE_OP_T = 0, 1
 GE_EPILOG_NONE, GE_EPILOG_BIAS, GE_EPILOG_RELU_BIAS, GE_EPILOG_RELU_AUX_BIAS, \
-    GE_EPILOG_GELU_BIAS = range(5)
+    GE_EPILOG_GELU_BIAS, GE_EPILOG_GELU_AUX_BIAS, GE_EPILOG_DRELU, GE_EPILOG_DGELU = range(8)
 GE_BIAS_ROW, GE_BIAS_COL = 0, 1
 
 DTYPE_CODE = {"f32": GE_F32, "f16": GE_F16, "bf16": GE_BF16, "e4m3": GE_F8_E4M3,
               torch.float32: GE_F32, torch.float16: GE_F16, torch.bfloat16: GE_BF16,
               torch.float8_e4m3fn: GE_F8_E4M3}
 EPILOG_CODE = {"none": GE_EPILOG_NONE, "bias": GE_EPILOG_BIAS, "relu_bias": GE_EPILOG_RELU_BIAS,
-               "relu_aux_bias": GE_EPILOG_RELU_AUX_BIAS, "gelu_bias": GE_EPILOG_GELU_BIAS}
+               "relu_aux_bias": GE_EPILOG_RELU_AUX_BIAS, "gelu_bias": GE_EPILOG_GELU_BIAS,
+               "gelu_aux_bias": GE_EPILOG_GELU_AUX_BIAS, "drelu": GE_EPILOG_DRELU,
+               "dgelu": GE_EPILOG_DGELU}
 AXIS_CODE = {"row": GE_BIAS_ROW, "col": GE_BIAS_COL}
 TORCH_DTYPE = {GE_F32: torch.float32, GE_F16: torch.float16, GE_BF16: torch.bfloat16,
                GE_F8_E4M3: torch.float8_e4m3fn}
@@ -191,6 +193,11 @@ class GemmEpilog:
         aux = None
         if self.epilog == GE_EPILOG_RELU_AUX_BIAS:
             aux = torch.empty((d.m, self.aux_ld_bits // 32), dtype=torch.int32, device=device)
+        elif self.epilog == GE_EPILOG_GELU_AUX_BIAS:
+            # the pre-activation matrix, D's dtype, round_up(n, 128) columns
+            dt = TORCH_DTYPE[d.d_type]
+            aux = torch.empty((d.m, self.aux_ld_bits // torch.finfo(dt).bits), dtype=dt,
+                              device=device)
         ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device) if self.ws_bytes else None
         return D, aux, ws
 

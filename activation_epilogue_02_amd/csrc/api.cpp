@@ -56,6 +56,20 @@ bool dtype_combo_ok(int a, int b, int d) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Epilogues that add a bias (DRELU and DGELU read none).
+bool has_bias(int e) {
+    return e == GE_EPILOG_BIAS || e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_RELU_AUX_BIAS ||
+           e == GE_EPILOG_GELU_BIAS || e == GE_EPILOG_GELU_AUX_BIAS;
+}
+// Epilogues with an aux buffer: a bit mask (written by RELU_AUX_BIAS, read by
+// DRELU) or a pre-activation matrix in D's dtype (written by GELU_AUX_BIAS,
+// read by DGELU).
+bool has_aux(int e) {
+    return e == GE_EPILOG_RELU_AUX_BIAS || e == GE_EPILOG_DRELU || e == GE_EPILOG_GELU_AUX_BIAS ||
+           e == GE_EPILOG_DGELU;
+}
+bool aux_is_matrix(int e) { return e == GE_EPILOG_GELU_AUX_BIAS || e == GE_EPILOG_DGELU; }
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 const TileShape* find_tile(int id) {
@@ -159,7 +173,7 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
 
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* pref) {
     if (!h) return GE_ERR_NULL;
-    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_GELU_BIAS) return GE_ERR_EPILOG;
+    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_DGELU) return GE_ERR_EPILOG;
     if (bias_axis != GE_BIAS_ROW && bias_axis != GE_BIAS_COL) return GE_ERR_EPILOG;
     ge_pref pr = {0, 0, 0, 0};
     if (pref) pr = *pref;
@@ -173,12 +187,19 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     q.epilog = epilog;
     q.axis = bias_axis;
     q.unfused = (pr.unfused && epilog != GE_EPILOG_NONE) ? 1 : 0;
-    q.ldaux = (epilog == GE_EPILOG_RELU_AUX_BIAS) ? (int64_t)round_up((size_t)d.n, 128) / 32 : 0;
+    // aux row stride: round_up(n, 128) bits (mask, in 32-bit words) or
+    // elements (pre-activation matrix)
+    q.ldaux = !has_aux(epilog) ? 0
+              : aux_is_matrix(epilog) ? (int64_t)round_up((size_t)d.n, 128)
+                                      : (int64_t)round_up((size_t)d.n, 128) / 32;
     if (q.ldaux > INT32_MAX) return GE_ERR_SHAPE;
 
+    // the small-m kernel serves the inference epilogues only
+    const bool smallm_epilog = epilog <= GE_EPILOG_GELU_BIAS;
     int path = pr.path;
-    if (path == 0) path = smallm_supported(d) ? PATH_SMALLM : PATH_TILE;
+    if (path == 0) path = (smallm_supported(d) && smallm_epilog) ? PATH_SMALLM : PATH_TILE;
     if (path == PATH_SMALLM && !smallm_supported(d)) return GE_ERR_SHAPE;
+    if (path == PATH_SMALLM && !smallm_epilog) return GE_ERR_EPILOG;
     q.path = path;
     q.split_k = 1;
     q.ws_partial = q.ws_counters = 0;
@@ -228,7 +249,8 @@ int gemm_epilog_workspace_size(ge_handle h, size_t* bytes) {
 
 int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
     if (!h || !ld_bits) return GE_ERR_NULL;
-    *ld_bits = (int64_t)round_up((size_t)h->d.n, 128);
+    const int64_t ld = (int64_t)round_up((size_t)h->d.n, 128);
+    *ld_bits = (h->planned && aux_is_matrix(h->epilog)) ? ld * 8 * elem_size(h->d.d_type) : ld;
     return GE_OK;
 }
 
@@ -241,9 +263,9 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     // a pointer may be NULL only when its buffer holds no elements
     if ((!A && d.m * d.k > 0) || (!B && d.k * d.n > 0) || (!D && d.m * d.n > 0)) return GE_ERR_NULL;
     const int64_t bias_len = h->axis == GE_BIAS_ROW ? d.m : d.n;
-    if (h->epilog != GE_EPILOG_NONE && !bias && bias_len > 0) return GE_ERR_NULL;
-    const bool want_aux = h->epilog == GE_EPILOG_RELU_AUX_BIAS && d.m > 0;
-    if (aux && h->epilog != GE_EPILOG_RELU_AUX_BIAS) return GE_ERR_EPILOG;
+    if (has_bias(h->epilog) && !bias && bias_len > 0) return GE_ERR_NULL;
+    const bool want_aux = has_aux(h->epilog) && d.m > 0;
+    if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
     if (d.a_type != GE_F8_E4M3 && (scale_a || scale_b)) return GE_ERR_DTYPE;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||

@@ -1,5 +1,6 @@
 // ew_kernel.hip -- the second kernel of the unfused pair: D = act(C + bias)
-// (+ ReLU sign mask), reading back the product C that the first kernel (the
+// (+ ReLU sign mask or stored pre-activation), or D = C * f(aux) for the
+// backward epilogues, reading back the product C that the first kernel (the
 // tile or small-m kernel with no epilogue) stored in D's dtype.
 //
 // This is the separate elementwise pass that epilogue fusion removes (epilog
@@ -11,22 +12,31 @@
 
 namespace ge {
 
+// Work items per row: one per 32 columns, or per mask word when the mask is
+// written (its padding words are cleared too).
+__host__ __device__ inline int ew_items_per_row(const KernelArgs& p) {
+    return p.epilog == GE_EPILOG_RELU_AUX_BIAS ? p.ldaux : (p.n + 31) / 32;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int words = p.ldaux > 0 ? p.ldaux : (p.n + 31) / 32;   // work items per row
+    const int words = ew_items_per_row(p);
     const int64_t row = t / words;
     const int w = (int)(t - row * words);
     if (row >= p.m) return;
     const int n0 = w * 32;
     const int ep = p.epilog;
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+    const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;
+    const bool want_grad = ep == GE_EPILOG_DRELU || ep == GE_EPILOG_DGELU;
     if (n0 >= p.n) {
         if (want_aux) p.aux[row * p.ldaux + w] = 0u;   // row padding
         return;
     }
+    const bool has_bias = epilog_has_bias(ep);
     const bool row_bias = p.axis == GE_BIAS_ROW;
-    const float brow = row_bias ? load_scalar<DT>(p.bias, row) : 0.0f;
+    const float brow = (has_bias && row_bias) ? load_scalar<DT>(p.bias, row) : 0.0f;
     uint32_t bits = 0;
     const int64_t base = row * p.ldd;
 #pragma unroll
@@ -34,22 +44,24 @@ __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c)
         const int nc = n0 + 8 * g;
         if (nc >= p.n) break;
         const bool full = nc + 8 <= p.n;
-        float x[8], b[8];
+        float x[8], b[8], gf[8];
         if (full) {
             load8<DT>(c, base + nc, x);
-            if (!row_bias) load8<DT>(p.bias, nc, b);
+            if (has_bias && !row_bias) load8<DT>(p.bias, nc, b);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 x[j] = (nc + j < p.n) ? load_scalar<DT>(c, base + nc + j) : 0.0f;
-                b[j] = (!row_bias && nc + j < p.n) ? load_scalar<DT>(p.bias, nc + j) : 0.0f;
+                b[j] = (has_bias && !row_bias && nc + j < p.n) ? load_scalar<DT>(p.bias, nc + j) : 0.0f;
             }
         }
+        if (want_grad) grad_factor8<DT>(p, ep, row, nc, gf);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float pre = x[j] + (row_bias ? brow : b[j]);
+            const float pre = x[j] + (has_bias ? (row_bias ? brow : b[j]) : 0.0f);
             if (want_aux && pre > 0.0f && nc + j < p.n) bits |= 1u << (8 * g + j);
-            x[j] = activate(ep, pre);
+            x[j] = want_grad ? grad_apply(ep, pre, gf[j]) : activate(ep, pre);
+            b[j] = pre;
         }
         if (full) store8<DT>(p.D, base + nc, x);
         else {
@@ -57,13 +69,13 @@ __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c)
             for (int j = 0; j < 8; ++j)
                 if (nc + j < p.n) store_one<DT>(p.D, base + nc + j, x[j]);
         }
+        if (want_pre) store_pre8<DT>(p, row, nc, b);
     }
     if (want_aux) p.aux[row * p.ldaux + w] = bits;
 }
 
 int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* stream) {
-    const int words = args.ldaux > 0 ? args.ldaux : (args.n + 31) / 32;
-    const int64_t items = (int64_t)args.m * words;
+    const int64_t items = (int64_t)args.m * ew_items_per_row(args);
     const unsigned grid = (unsigned)((items + 255) / 256);
     switch (d_type) {
     case GE_F32:

@@ -169,11 +169,83 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Apply the activation of an epilogue to a pre-activation value.
+// GELU'(x) of the same tanh form.  With g = 0.5 (1 + tanh u) = 1 / (1 + e^{-2u})
+// and 1 - tanh^2 u = 4 g (1 - g), the product and chain rules give
+// GELU'(x) = g + 2 x g (1 - g) u'(x), u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2).
+// Saturates like gelu_tanh: g -> 0 gives 0, g -> 1 gives 1.
+__device__ __forceinline__ float gelu_tanh_deriv(float x) {
+    const float k0 = 0.7978845608028654f;          // sqrt(2/pi)
+    const float k1 = 0.044715f;
+    const float m2log2e = -2.0f * 1.4426950408889634f;
+    const float x2 = x * x;
+    const float u = k0 * (x + k1 * x2 * x);
+    const float g = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+    const float du = k0 * (1.0f + 3.0f * k1 * x2);
+    return g + 2.0f * x * g * (1.0f - g) * du;
+}
+
+// Epilogues that add a bias to the product (DRELU and DGELU take none).
+__host__ __device__ __forceinline__ bool epilog_has_bias(int epilog) {
+    return epilog == GE_EPILOG_BIAS || epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS ||
+           epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS;
+}
+
+// Apply the activation of an epilogue to a pre-activation value.  DRELU and
+// DGELU pass the product through; their factor comes from grad_factor8.
 __device__ __forceinline__ float activate(int epilog, float x) {
     if (epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS) return x > 0.0f ? x : 0.0f;
-    if (epilog == GE_EPILOG_GELU_BIAS) return gelu_tanh(x);
+    if (epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS) return gelu_tanh(x);
     return x;
+}
+
+// The backward factor of DRELU (the mask bit RELU_AUX_BIAS wrote) or DGELU
+// (GELU' of the pre-activation GELU_AUX_BIAS wrote) for the 8 columns
+// nc .. nc+7 of row m (nc a multiple of 8, m < m of the problem).  Columns at
+// or beyond n get 0 and are never read: the aux rows are only padded to 128
+// columns, while a tile may reach further.
+template <int DOUT>
+__device__ __forceinline__ void grad_factor8(const KernelArgs& p, int epilog, int64_t m, int nc, float* f) {
+    if (nc >= p.n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = 0.0f;
+        return;
+    }
+    if (epilog == GE_EPILOG_DRELU) {
+        const uint32_t w = p.aux[m * p.ldaux + (nc >> 5)] >> (nc & 31);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = ((w >> j) & 1u) ? 1.0f : 0.0f;
+        return;
+    }
+    float pre[8];
+    const int64_t idx = m * p.ldaux + nc;
+    if (nc + 8 <= p.n) {
+        load8<DOUT>(p.aux, idx, pre);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pre[j] = (nc + j < p.n) ? load_scalar<DOUT>(p.aux, idx + j) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = gelu_tanh_deriv(pre[j]);
+}
+
+// Apply the backward factor: DGELU multiplies; DRELU selects (C or +0), so
+// that a masked entry is exactly zero whatever C holds (-0, inf, NaN).
+__device__ __forceinline__ float grad_apply(int epilog, float x, float f) {
+    return epilog == GE_EPILOG_DRELU ? (f != 0.0f ? x : 0.0f) : x * f;
+}
+
+// GELU_AUX_BIAS: store the pre-activation of the 8 columns nc .. nc+7 of
+// row m into the aux matrix (D's dtype, row stride ldaux elements).
+template <int DOUT>
+__device__ __forceinline__ void store_pre8(const KernelArgs& p, int64_t m, int nc, const float* x) {
+    const int64_t idx = m * p.ldaux + nc;
+    if (nc + 8 <= p.n) {
+        store8<DOUT>(p.aux, idx, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (nc + j < p.n) store_one<DOUT>(p.aux, idx + j, x[j]);
+    }
 }
 
 }  // namespace ge

@@ -15,14 +15,15 @@ struct KernelArgs {
     const void* B;
     const void* bias;      // NULL for GE_EPILOG_NONE
     void* D;
-    uint32_t* aux;         // NULL unless RELU_AUX_BIAS
+    uint32_t* aux;         // RELU_AUX_BIAS/DRELU: mask words; GELU_AUX_BIAS/DGELU:
+                           // pre-activation matrix in D's dtype; else NULL
     const float* scale_a;  // NULL = 1.0
     const float* scale_b;  // NULL = 1.0
     float* partial;        // split-K fp32 partials (small-m path), or NULL
     uint32_t* counters;    // split-K arrival counters (small-m path), or NULL
     int32_t m, n, k;
     int32_t epilog, axis;
-    int32_t ldaux;         // mask row stride in 32-bit words
+    int32_t ldaux;         // aux row stride: 32-bit words (mask) or elements (matrix)
     int64_t lda, ldb, ldd;
     int32_t tiles_m, tiles_n;
     int32_t group_m;       // tile-rows per group in the launch order

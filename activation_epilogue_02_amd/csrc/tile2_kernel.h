@@ -521,9 +521,11 @@ ge_tile2_kernel(KernelArgs p) {
         if (p.scale_b) s *= *p.scale_b;
     }
     const int ep = p.epilog;
-    const bool has_bias = ep != GE_EPILOG_NONE;
+    const bool has_bias = epilog_has_bias(ep);
     const bool row_bias = p.axis == GE_BIAS_ROW;
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+    const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;                    // aux <- P
+    const bool want_grad = ep == GE_EPILOG_DRELU || ep == GE_EPILOG_DGELU;  // D = C * f(aux)
 
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
@@ -561,11 +563,20 @@ ge_tile2_kernel(KernelArgs p) {
                         for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DOUT>(p.bias, nc + j) : 0.0f;
                     }
                 }
+                float gf[8], pre[8];
+                if (want_grad) {
+                    if (mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
+                    else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) gf[j] = 0.0f;
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float x = v[g][j] * s + bc[j];
+                    pre[j] = x;
                     if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
-                    v[g][j] = activate(ep, x);
+                    v[g][j] = want_grad ? grad_apply(ep, x, gf[j]) : activate(ep, x);
                 }
                 if (mok) {
                     const int64_t idx = (int64_t)m * p.ldd + nc;
@@ -575,6 +586,7 @@ ge_tile2_kernel(KernelArgs p) {
                         for (int j = 0; j < 8; ++j)
                             if (nc + j < N) store_one<DOUT>(p.D, idx + j, v[g][j]);
                     }
+                    if (want_pre) store_pre8<DOUT>(p, m, nc, pre);
                 }
             }
             if (want_aux) {

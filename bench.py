@@ -220,10 +220,12 @@ def copy_calibration(mib: int, steps: int):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
-def cpu_baseline(w, inp, seconds: float, unit: str):
+def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole rows of D (all of K) through its GEMM, bias and activation passes,
-    repeated on further rows until about `seconds` of CPU time is spent."""
+    whole rows of D (all of K) through its GEMM, bias and activation passes
+    (for the backward epilogues: GEMM and DRELU / DGELU pass on the aux
+    input's rows), repeated on further rows until about `seconds` of CPU time
+    is spent."""
     import numpy as np
     import torch
 
@@ -239,6 +241,10 @@ def cpu_baseline(w, inp, seconds: float, unit: str):
         return t.view(torch.int16).numpy().view(np.uint16)
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    grad = w.epilog in ("drelu", "dgelu")
+    if grad:
+        aux_c = aux_in.detach().cpu().contiguous()
+        aux_c = aux_c.numpy().view(np.uint32) if w.epilog == "drelu" else raw(aux_c)
     Bc = raw(inp.B)
     bias = raw(inp.bias).reshape(-1)
     sa = float(inp.scale_a.item()) if inp.scale_a is not None else 1.0
@@ -252,9 +258,14 @@ def cpu_baseline(w, inp, seconds: float, unit: str):
         A_rows = raw(inp.A[start:start + rows])
         t0 = time.perf_counter()
         C = oracle.gemm(A_rows, w.in_dtype, Bc, w.in_dtype, w.op_b, sa, sb)
-        b = bias[start:start + rows] if w.axis == "row" else bias
-        P = oracle.bias_pass(C, b, w.out_dtype, w.axis)
-        oracle.act_pass(P, w.epilog)
+        if w.epilog == "drelu":
+            oracle.drelu_pass(C, aux_c[start:start + rows])
+        elif w.epilog == "dgelu":
+            oracle.dgelu_pass(C, aux_c[start:start + rows], w.out_dtype)
+        else:
+            b = bias[start:start + rows] if w.axis == "row" else bias
+            P = oracle.bias_pass(C, b, w.out_dtype, w.axis)
+            oracle.act_pass(P, w.epilog)
         dt = time.perf_counter() - t0
         t_total += dt
         done += rows
@@ -268,7 +279,8 @@ def cpu_baseline(w, inp, seconds: float, unit: str):
     return {"value": round(value, 6), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{done} rows of D (of {w.m}; {done}x{w.n} outputs, full K={w.k}, rows taken "
                       f"in order and again from row 0 once all are done) through the oracle's fp64 "
-                      f"GEMM, bias and activation passes in {t_total:.1f} s"}
+                      f"GEMM and {'DRELU/DGELU' if grad else 'bias and activation'} passes in "
+                      f"{t_total:.1f} s"}
 
 
 def main():
@@ -304,7 +316,10 @@ def main():
     copies = [inp]
     for r in range(1, rot):
         copies.append(synth.make_inputs(w, device="cuda", seed=w.seed + 100 * r))
-    bias = [c.bias.reshape(-1).contiguous() for c in copies]
+    grad = w.epilog in ("drelu", "dgelu")   # backward epilogues: no bias, an aux input
+    bias = [None if grad else c.bias.reshape(-1).contiguous() for c in copies]
+    aux_in = [synth.make_aux(w, device="cuda", seed=w.seed + 100 * r) if grad else None
+              for r in range(rot)]
 
     t0 = time.perf_counter()
     g = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
@@ -318,6 +333,8 @@ def main():
     def step(i, h=g, outputs=outs):
         c = copies[i % rot]
         D, aux, ws = outputs[i % rot]
+        if grad:
+            aux = aux_in[i % rot]
         # the stream current at call time: the capture stream while a graph
         # is being recorded
         B.gemm_epilog_execute(h.h, c.A, c.B, bias[i % rot], D, aux, c.scale_a, c.scale_b, ws,
@@ -405,7 +422,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, metric_unit)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, metric_unit, aux_in[0])
 
     out = {
         "metric": "fused GEMM+bias+act TFLOP/s and % MFMA peak; HBM GB/s at batch 16",

@@ -83,20 +83,35 @@ typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op;
 /* Epilogues, as the epilog page's paragraph on the epilog enum lists them
  * (BIAS, RELU_BIAS, RELU_AUX_BIAS), plus NONE and GELU_BIAS (GELU is named
  * as a fused activation on the cuBLASLt page, paragraph 2, and in the NVGEMM
- * page's section on why epilogue fusion matters).  With P the pre-activation
- * (the scaled product plus bias):
- *   NONE           D = s*A*B                        (no bias read)
+ * page's section on why epilogue fusion matters).  With C = s*A*B the scaled
+ * product and P the pre-activation (C plus bias):
+ *   NONE           D = C                            (no bias read)
  *   BIAS           D = P
  *   RELU_BIAS      D = max(P, 0)
  *   RELU_AUX_BIAS  D = max(P, 0), and aux bit (i,j) = (P[i][j] > 0)
- *   GELU_BIAS      D = 0.5 P (1 + tanh(sqrt(2/pi) (P + 0.044715 P^3)))
- * Conversion of the fp32 result to D's dtype rounds to nearest even. */
+ *   GELU_BIAS      D = GELU(P) = 0.5 P (1 + tanh(sqrt(2/pi) (P + 0.044715 P^3)))
+ * The training-side epilogues serve the backward pass, which needs what the
+ * forward activation saw (nvmath page, paragraph on limitations: RELU_AUX_BIAS
+ * produces the mask backward needs; its closing paragraph names GELU and the
+ * bias gradient as the next fusions):
+ *   GELU_AUX_BIAS  D = GELU(P), and aux[i][j] = P[i][j] in D's dtype (output)
+ *   DRELU          D = C * ReLU'(P): C where mask bit (i,j) of aux is set,
+ *                  else 0; aux is an input, the bit matrix RELU_AUX_BIAS wrote
+ *   DGELU          D = C * GELU'(P), P read from aux (an input, the matrix
+ *                  GELU_AUX_BIAS wrote); GELU' is the derivative of the tanh
+ *                  form above
+ * DRELU and DGELU read no bias (C is the gradient arriving from the next
+ * layer's product).  Conversion of the fp32 result to D's dtype rounds to
+ * nearest even. */
 typedef enum {
     GE_EPILOG_NONE = 0,
     GE_EPILOG_BIAS = 1,
     GE_EPILOG_RELU_BIAS = 2,
     GE_EPILOG_RELU_AUX_BIAS = 3,
-    GE_EPILOG_GELU_BIAS = 4
+    GE_EPILOG_GELU_BIAS = 4,
+    GE_EPILOG_GELU_AUX_BIAS = 5,
+    GE_EPILOG_DRELU = 6,
+    GE_EPILOG_DGELU = 7
 } ge_epilog;
 
 /* Bias broadcast axis.
@@ -158,9 +173,13 @@ typedef struct ge_plan_s* ge_handle;
 int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
 
 /* Choose the epilogue and bias axis and plan the launch (kernel, tile, grid,
- * workspace).  p may be NULL.  May be called again to re-plan.
- * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis),
- * GE_ERR_SHAPE (an unknown tile id or split in p). */
+ * workspace).  p may be NULL.  May be called again to re-plan.  The bias
+ * axis is validated for every epilogue but only used by those with a bias.
+ * The small-m kernel serves the inference epilogues (NONE .. GELU_BIAS); the
+ * automatic path takes the tile kernel for the others.
+ * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis, or the
+ * small-m path forced with a training-side epilogue), GE_ERR_SHAPE (an
+ * unknown tile id or split in p). */
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* p);
 
 /* Bytes of device workspace execute() needs (0 for the fused paths; m*ldd
@@ -168,21 +187,27 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
  * Errors: GE_ERR_NULL, GE_ERR_STATE (not planned). */
 int gemm_epilog_workspace_size(ge_handle h, size_t* bytes);
 
-/* Row stride of the aux mask in bits: round_up(n, 128), so each row starts
- * 16-byte aligned.  The mask is a row-major bit matrix of m rows: bit (i,j)
- * is bit j%32 of the little-endian 32-bit word at word index
- * i*(ld_bits/32) + j/32.  Bits j >= n of a row are written as 0.  The
- * buffer must hold m*ld_bits/8 bytes.  Errors: GE_ERR_NULL. */
+/* Row stride of the aux buffer in bits.
+ * Mask epilogues (RELU_AUX_BIAS writes it, DRELU reads it), and any handle
+ * not planned with a pre-activation epilogue: round_up(n, 128), so each row
+ * starts 16-byte aligned.  The mask is a row-major bit matrix of m rows: bit
+ * (i,j) is bit j%32 of the little-endian 32-bit word at word index
+ * i*(ld_bits/32) + j/32.  RELU_AUX_BIAS writes bits j >= n of a row as 0.
+ * Pre-activation epilogues (GELU_AUX_BIAS writes it, DGELU reads it):
+ * round_up(n, 128) elements of D's dtype, i.e. that many times 32 or 16 bits;
+ * a row-major m-row matrix whose padding columns are never written.
+ * The buffer must hold m*ld_bits/8 bytes.  Errors: GE_ERR_NULL. */
 int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits);
 
 /* Launch the planned computation on `stream` (a hipStream_t; NULL = the
  * null stream).  Asynchronous: returns once the kernel(s) are queued.
  *   A, B     device operands (see ge_desc)
  *   bias     device vector of m (ROW) or n (COL) bias_type values; NULL
- *            only for GE_EPILOG_NONE
+ *            only for NONE, DRELU and DGELU (which read no bias)
  *   D        device output, m x n with leading dimension ldd
- *   aux      device mask buffer (see gemm_epilog_aux_ld); required for
- *            RELU_AUX_BIAS, must be NULL otherwise
+ *   aux      device aux buffer (see gemm_epilog_aux_ld); required for
+ *            RELU_AUX_BIAS and GELU_AUX_BIAS (written) and for DRELU and
+ *            DGELU (read), must be NULL otherwise
  *   scale_a, scale_b
  *            device pointers to one fp32 each, the per-tensor dequantisation
  *            factors of fp8 inputs (D uses scale_a*scale_b*A*B); NULL means

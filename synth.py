@@ -36,6 +36,7 @@ class Workload:
     in_dtype: str         # dtype of A and B
     out_dtype: str        # dtype of D (and of the bias)
     epilog: str           # none | bias | relu_bias | relu_aux_bias | gelu_bias
+                          # | gelu_aux_bias | drelu | dgelu
     axis: str             # row: bias has m values; col: bias has n values
     op_b: int             # 0: B is k x n row-major; 1: B is n x k (Linear weight)
     seed: int
@@ -48,10 +49,17 @@ class Workload:
         return 2.0 * self.m * self.n * self.k
 
     def algorithmic_bytes(self) -> int:
-        """A, B, bias and D read or written once, plus the 1-bit mask."""
+        """A, B, bias and D read or written once, plus the aux buffer: the
+        1-bit mask (written by relu_aux_bias, read by drelu) or the m x n
+        pre-activation in D's dtype (written by gelu_aux_bias, read by dgelu)."""
         ea, eo = ELEM_SIZE[self.in_dtype], ELEM_SIZE[self.out_dtype]
-        nb = 0 if self.epilog == "none" else (self.m if self.axis == "row" else self.n) * eo
-        aux = self.m * (((self.n + 127) // 128) * 16) if self.epilog == "relu_aux_bias" else 0
+        biased = self.epilog not in ("none", "drelu", "dgelu")
+        nb = (self.m if self.axis == "row" else self.n) * eo if biased else 0
+        aux = 0
+        if self.epilog in ("relu_aux_bias", "drelu"):
+            aux = self.m * (((self.n + 127) // 128) * 16)
+        elif self.epilog in ("gelu_aux_bias", "dgelu"):
+            aux = self.m * self.n * eo
         scales = 8 if self.in_dtype == "e4m3" else 0
         return (self.m * self.k + self.k * self.n) * ea + nb + self.m * self.n * eo + aux + scales
 
@@ -77,7 +85,24 @@ WORKLOADS = {
     "C5b": Workload("C5b", "fp8-e4m3 RELU_BIAS 65536x8192x16384", 65536, 8192, 16384, "e4m3", "bf16",
                     "relu_bias", "row", 0, 1005, ("normal", 1 / math.sqrt(16384)),
                     ("normal", 1 / math.sqrt(16384)), ("normal", 0.1)),
+    # training-side epilogues at the square 8192^3 shape: the GELU forward
+    # that keeps its pre-activation, and the two backward products (the
+    # upstream gradient times the next layer's weight) scaled by GELU' or by
+    # ReLU' from the stored aux buffer
+    "F1a": Workload("F1a", "bf16 GELU_AUX_BIAS 8192x8192x8192", 8192, 8192, 8192, "bf16", "bf16",
+                    "gelu_aux_bias", "row", 0, 1006, ("normal", 1 / math.sqrt(8192)),
+                    ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
+    "F1b": Workload("F1b", "bf16 DGELU 8192x8192x8192", 8192, 8192, 8192, "bf16", "bf16",
+                    "dgelu", "row", 0, 1007, ("normal", 1 / math.sqrt(8192)),
+                    ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
+    "F1c": Workload("F1c", "bf16 DRELU 8192x8192x8192", 8192, 8192, 8192, "bf16", "bf16",
+                    "drelu", "row", 0, 1008, ("normal", 1 / math.sqrt(8192)),
+                    ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
 }
+
+# variance of the stored pre-activation a backward workload reads: that of
+# the forward's A*B (1 with the variances above) plus its bias (0.1)
+AUX_PRE_VARIANCE = 1.1
 
 
 def scaled(w: Workload, m: Optional[int] = None, n: Optional[int] = None,
@@ -148,3 +173,26 @@ def aux_ld_words(n: int) -> int:
     """Row stride, in 32-bit words, of the packed ReLU mask: rows padded to
     128 bits so every row starts 16-byte aligned."""
     return ((n + 127) // 128) * 4
+
+
+def aux_ld_elems(n: int) -> int:
+    """Row stride, in elements, of the pre-activation aux matrix: rows padded
+    to 128 elements."""
+    return ((n + 127) // 128) * 128
+
+
+def make_aux(w: Workload, device="cpu", seed: Optional[int] = None) -> torch.Tensor:
+    """The aux input of a backward workload, drawn after nothing else from a
+    generator seeded with seed + 1: for drelu, mask words with independent
+    fair bits (m x aux_ld_words); for dgelu, a pre-activation matrix
+    ~ N(0, AUX_PRE_VARIANCE) in D's dtype (m x aux_ld_elems)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.seed if seed is None else seed) + 1)
+    if w.epilog == "drelu":
+        t = torch.randint(0, 2 ** 32, (w.m, aux_ld_words(w.n)), generator=gen, device=device,
+                          dtype=torch.int64)
+        return (t - 2 ** 31).to(torch.int32)
+    if w.epilog == "dgelu":
+        x = _draw(gen, (w.m, aux_ld_elems(w.n)), ("normal", AUX_PRE_VARIANCE), device)
+        return x.to(TORCH_DTYPE[w.out_dtype])
+    raise ValueError(f"{w.epilog} reads no aux input")

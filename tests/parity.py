@@ -78,9 +78,30 @@ class Result:
         self.__dict__.update(kw)
 
 
+GRAD_EPILOGS = ("drelu", "dgelu")
+
+
+def aux_ld_elems(n: int) -> int:
+    """Row stride, in elements, of the pre-activation aux matrix."""
+    return round_up(n, 128)
+
+
+def make_aux_input(w: synth.Workload, device="cuda", seed=None) -> torch.Tensor:
+    """A seeded aux input for the backward epilogues: random mask words for
+    DRELU (padding bits random too: they must be ignored), a pre-activation
+    matrix ~ N(0, 4) in D's dtype for DGELU (padding columns NaN: never read)."""
+    g = torch.Generator().manual_seed(w.seed + 17 if seed is None else seed)
+    if w.epilog == "drelu":
+        words = synth.aux_ld_words(w.n)
+        t = torch.randint(-2 ** 31, 2 ** 31 - 1, (w.m, words), generator=g, dtype=torch.int64)
+        return t.to(torch.int32).to(device)
+    P = torch.randn((w.m, w.n), generator=g) * 2.0
+    return padded(P.to(synth.TORCH_DTYPE[w.out_dtype]).to(device), aux_ld_elems(w.n), w.out_dtype)
+
+
 def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int = 0,
                 unfused: int = 0, tile: int = 0, split_k: int = 0, poison=True,
-                device="cuda", lda=None, ldb=None, ldd=None):
+                device="cuda", lda=None, ldb=None, ldd=None, aux_in=None):
     """Execute the planned op through the C ABI; returns (D_full, aux, h-desc, buffers)."""
     a_dt, d_dt = w.in_dtype, w.out_dtype
     ea, ed = ESZ[a_dt], ESZ[d_dt]
@@ -102,11 +123,19 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
         aux = None
         if w.epilog == "relu_aux_bias":
             aux = torch.full((w.m, g.aux_ld_bits // 32), -1, dtype=torch.int32, device=device)
+        elif w.epilog == "gelu_aux_bias":
+            dt = synth.TORCH_DTYPE[d_dt]
+            assert g.aux_ld_bits == aux_ld_elems(w.n) * 8 * ed
+            aux = torch.full((w.m, aux_ld_elems(w.n)), float("nan"), dtype=dt, device=device)
+        elif w.epilog in GRAD_EPILOGS:
+            aux = aux_in if aux_in is not None else make_aux_input(w, device)
         ws = torch.empty(g.ws_bytes, dtype=torch.uint8, device=device) if g.ws_bytes else None
-        g.execute(A, Bm, bias if w.epilog != "none" else None, D, aux, sa, sb, ws)
+        with_bias = w.epilog not in ("none",) + GRAD_EPILOGS
+        g.execute(A, Bm, bias if with_bias else None, D, aux, sa, sb, ws)
         torch.cuda.synchronize()
         return Result(D=D, aux=aux, A=A, B=Bm, bias=bias, sa=sa, sb=sb, lda=lda, ldb=ldb,
-                      ldd=ldd, desc=desc, ldw=(g.aux_ld_bits // 32) if aux is not None else None)
+                      ldd=ldd, desc=desc,
+                      ldw=(g.aux_ld_bits // 32) if w.epilog in ("relu_aux_bias", "drelu") else None)
     finally:
         g.free()
 
@@ -119,6 +148,10 @@ def oracle_full(w: synth.Workload, r: Result):
     sa = float(r.sa.item()) if r.sa is not None else 1.0
     sb = float(r.sb.item()) if r.sb is not None else 1.0
     C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+    if w.epilog == "drelu":
+        return oracle.drelu_pass(C, codes(r.aux)), C, None
+    if w.epilog == "dgelu":
+        return oracle.dgelu_pass(C, codes(r.aux), d_dt), C, None
     if w.epilog == "none":
         P = C
     else:
@@ -150,7 +183,23 @@ def check_full(w: synth.Workload, r: Result, tol: Optional[float] = None):
             assert np.isnan(oracle.decode(np.ascontiguousarray(pad), w.out_dtype)).all(), "output padding written"
     if M is not None:
         check_mask(w, codes(r.aux), M, P)
+    if w.epilog == "gelu_aux_bias":
+        check_pre_aux(w, r, P, tol)
     return err
+
+
+def check_pre_aux(w, r, P, tol):
+    """GELU_AUX_BIAS: the aux matrix holds P in D's dtype; its padding
+    columns are never written."""
+    Ac = codes(r.aux)
+    Pd = oracle.decode(np.ascontiguousarray(Ac[:, : w.n]), w.out_dtype)
+    assert np.isfinite(Pd).all(), "non-finite pre-activation aux"
+    err = rel_fro(Pd, P)
+    assert err <= tol, f"aux pre-activation rel-Frobenius {err:.3e} > {tol:.1e}: {r.desc}"
+    if Ac.shape[1] > w.n:
+        pad = np.ascontiguousarray(Ac[:, w.n:])
+        dec = pad if w.out_dtype == "f32" else oracle.decode(pad, w.out_dtype)
+        assert np.isnan(dec).all(), "aux padding written"
 
 
 def check_mask(w, got_words: np.ndarray, want_words: np.ndarray, P: np.ndarray, rows=None):
@@ -201,8 +250,9 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     Ce = oracle.gemm_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej,
                              np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
                              w.op_b, sa, sb)
-    Pe = Ce if w.epilog == "none" else oracle.bias_entries(Ce, ei, ej, bias_c, d_dt, w.axis)
-    Ye = oracle.act_pass(Pe, w.epilog)
+    grad = w.epilog in GRAD_EPILOGS
+    Pe = Ce if (w.epilog == "none" or grad) else oracle.bias_entries(Ce, ei, ej, bias_c, d_dt, w.axis)
+    Ye = grad_entries(w, r, Ce, ei, ej) if grad else oracle.act_pass(Pe, w.epilog)
     D_rows_dev = r.D.index_select(0, torch.from_numpy(ei).to(r.D.device))
     De_all = codes(D_rows_dev)
     De = oracle.decode(np.ascontiguousarray(De_all[np.arange(len(ej)), ej]), d_dt)
@@ -211,13 +261,18 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     Ar = np.ascontiguousarray(A_rows[rslots][:, : w.k])
     Cr = oracle.gemm(Ar, a_dt, np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
                      w.op_b, sa, sb)
-    if w.epilog == "none":
+    ri = np.repeat(rows, w.n)
+    rj = np.tile(np.arange(w.n), len(rows))
+    if w.epilog == "none" or grad:
         Pr = Cr
     else:
-        ri = np.repeat(rows, w.n)
-        rj = np.tile(np.arange(w.n), len(rows))
         Pr = oracle.bias_entries(Cr.ravel(), ri, rj, bias_c, d_dt, w.axis).reshape(Cr.shape)
-    Yr = oracle.act_pass(Pr, w.epilog)
+    if grad:
+        aux_r = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))
+        Yr = (oracle.drelu_pass(Cr, aux_r) if w.epilog == "drelu"
+              else oracle.dgelu_pass(Cr, aux_r, d_dt))
+    else:
+        Yr = oracle.act_pass(Pr, w.epilog)
     Dr_c = codes(r.D.index_select(0, torch.from_numpy(rows).to(r.D.device)))[:, : w.n]
     Dr = oracle.decode(np.ascontiguousarray(Dr_c), d_dt)
     assert np.isfinite(De).all() and np.isfinite(Dr).all(), "non-finite outputs"
@@ -231,6 +286,11 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
         want_r = oracle.encode(Yr, d_dt).reshape(Yr.shape) if d_dt != "f32" else Yr.astype(np.float32)
         assert np.array_equal(Dr_c, want_r), "integer case not bit-exact (rows)"
     band_mis = None
+    if w.epilog == "gelu_aux_bias":
+        aux_e = codes(r.aux.index_select(0, torch.from_numpy(ei).to(r.aux.device)))[np.arange(len(ej)), ej]
+        assert rel_fro(oracle.decode(np.ascontiguousarray(aux_e), d_dt), Pe) <= tol, "aux entries"
+        aux_r = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))[:, : w.n]
+        assert rel_fro(oracle.decode(np.ascontiguousarray(aux_r), d_dt), Pr) <= tol, "aux rows"
     if w.epilog == "relu_aux_bias":
         Mr = oracle.mask_pass(Pr, r.ldw)
         got = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))
@@ -242,3 +302,17 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
         bad = (bits.astype(bool) != (Pe > 0)) & (np.abs(Pe) >= band)
         assert not bad.any(), f"{int(bad.sum())} sampled mask bits differ outside the band"
     return err_e, err_r, band_mis
+
+
+def grad_entries(w: synth.Workload, r: Result, Cv: np.ndarray, rows: np.ndarray, cols: np.ndarray):
+    """O6 / O7 at selected entries: C times the factor read from the aux input."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    aux_rows = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))
+    Cm = np.ascontiguousarray(np.asarray(Cv, dtype=np.float64).reshape(-1, 1))
+    if w.epilog == "drelu":
+        # one-column problems: column 0 of row t is entry t's mask word, shifted
+        words = (aux_rows[np.arange(len(cols)), cols // 32] >> (cols % 32).astype(np.uint32)) & 1
+        return oracle.drelu_pass(Cm, np.ascontiguousarray(words.reshape(-1, 1).astype(np.uint32))).ravel()
+    vals = np.ascontiguousarray(aux_rows[np.arange(len(cols)), cols].reshape(-1, 1))
+    return oracle.dgelu_pass(Cm, vals, w.out_dtype).ravel()

@@ -99,7 +99,7 @@ def test_plan_validation_and_state():
     try:
         assert status_of(B.gemm_epilog_workspace_size, h) == B.GE_ERR_STATE
         assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATE
-        assert status_of(B.gemm_epilog_plan, h, 7, 0) == B.GE_ERR_EPILOG
+        assert status_of(B.gemm_epilog_plan, h, 8, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, -1, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 2) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(0, 0, 99, 0)) == B.GE_ERR_SHAPE
@@ -140,6 +140,49 @@ def test_execute_validation_paths():
         assert ex(FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_WORKSPACE
         assert ex(FAKE, FAKE, FAKE, FAKE, workspace=FAKE, workspace_bytes=ws - 1) == B.GE_ERR_WORKSPACE
         assert ex(FAKE, FAKE, FAKE, FAKE, workspace=FAKE + 8, workspace_bytes=ws) == B.GE_ERR_ALIGN
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_training_epilogues_validation():
+    """GELU_AUX_BIAS needs a bias and writes a pre-activation matrix (row
+    stride round_up(n,128) elements); DRELU and DGELU read an aux input, take
+    no bias (ignored) and keep the mask / matrix strides."""
+    for d_type, bits in (("bf16", 16), ("f32", 32)):
+        a_type = "bf16" if d_type == "bf16" else "f32"
+        h = B.gemm_epilog_create(desc(a_type=a_type, d_type=d_type, n=200, ldb=200, ldd=200))
+        try:
+            ex = lambda *a, **k: status_of(B.gemm_epilog_execute, h, *a, **k)
+            B.gemm_epilog_plan(h, "gelu_aux_bias", "col")
+            assert B.gemm_epilog_aux_ld(h) == 256 * bits
+            assert ex(FAKE, FAKE, None, FAKE, FAKE) == B.GE_ERR_NULL      # bias required
+            assert ex(FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_EPILOG    # aux required
+            assert ex(FAKE, FAKE, FAKE, FAKE, FAKE + 8) == B.GE_ERR_ALIGN
+            B.gemm_epilog_plan(h, "dgelu", "row")
+            assert B.gemm_epilog_aux_ld(h) == 256 * bits
+            assert ex(FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_EPILOG    # aux input required
+            B.gemm_epilog_plan(h, "drelu", "row")
+            assert B.gemm_epilog_aux_ld(h) == 256                          # the mask's stride
+            assert ex(FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_EPILOG
+            assert ex(FAKE, FAKE, FAKE, FAKE, FAKE + 4) == B.GE_ERR_ALIGN
+            B.gemm_epilog_plan(h, "dgelu", "row", B.ge_pref(0, 1, 0, 0))  # unfused pair
+            assert B.gemm_epilog_workspace_size(h) >= 64 * 200 * (bits // 8)
+        finally:
+            B.gemm_epilog_free(h)
+
+
+def test_training_epilogues_take_the_tile_path():
+    """The small-m kernel serves the inference epilogues only: automatic
+    planning of a batch-16 Linear with a training epilogue takes the tile
+    kernel, and forcing the small-m path is refused."""
+    h = B.gemm_epilog_create(B.make_desc(16, 4096, 4096, "f16", "f16", 1))
+    try:
+        for ep in ("gelu_aux_bias", "drelu", "dgelu"):
+            B.gemm_epilog_plan(h, ep, "col")
+            assert "path=tile" in B.gemm_epilog_describe(h)
+            assert status_of(B.gemm_epilog_plan, h, ep, "col", B.ge_pref(2, 0, 0, 0)) == B.GE_ERR_EPILOG
+        B.gemm_epilog_plan(h, "gelu_bias", "col")
+        assert "path=smallm" in B.gemm_epilog_describe(h)
     finally:
         B.gemm_epilog_free(h)
 
