@@ -86,6 +86,7 @@ def lib():
         L.orc_gelu_deriv.argtypes = [dbl]
         L.orc_drelu.argtypes = [i64, i64, vp, i64, vp, vp]
         L.orc_dgelu.argtypes = [i64, i64, vp, ctypes.c_int, vp, i64, vp]
+        L.orc_bgrad.argtypes = [i64, i64, vp, ctypes.c_int, vp]
         _lib = L
     return _lib
 
@@ -242,6 +243,16 @@ def dgelu_pass(C: np.ndarray, P: np.ndarray, tp: str) -> np.ndarray:
     D = np.empty_like(C)
     _check(lib().orc_dgelu(m, n, _ptr(C), DTYPES[tp], _ptr(Pc), Pc.shape[1], _ptr(D)), "dgelu")
     return D
+
+
+def bgrad_pass(Y: np.ndarray, axis: str) -> np.ndarray:
+    """O8: the bias gradient, Y summed along the axis the bias was not
+    broadcast over (row: m values, col: n values)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float64)
+    m, n = Y.shape
+    g = np.empty(m if axis == "row" else n, dtype=np.float64)
+    _check(lib().orc_bgrad(m, n, _ptr(Y), AXES[axis], _ptr(g)), "bgrad")
+    return g
 
 
 def reference(A, ta, B, tb, bias, tbias, epilog, axis, op_b=0, sa=1.0, sb=1.0,

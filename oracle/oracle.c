@@ -367,3 +367,30 @@ int orc_dgelu(int64_t m, int64_t n, const double* C, int tp, const void* P, int6
             D[i * n + j] = C[i * n + j] * orc_gelu_deriv(dec_at(tp, P, i * ldp + j));
     return 0;
 }
+
+/* O8: the bias gradient of the backward epilogues (the dBias fusion the
+ * [nvmath page] closing paragraph looks ahead to).  The forward added the
+ * bias along one axis, so its gradient sums the backward result Y (O6 or O7,
+ * unrounded) along the other:
+ *   ROW (bias[i] was added to row i):    g[i] = sum_j Y[i][j]   (j ascending)
+ *   COL (bias[j] was added to column j): g[j] = sum_i Y[i][j]   (i ascending) */
+int orc_bgrad(int64_t m, int64_t n, const double* Y, int axis, double* g)
+{
+    if (axis == ORC_ROW) {
+        for (int64_t i = 0; i < m; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < n; ++j) s += Y[i * n + j];
+            g[i] = s;
+        }
+        return 0;
+    }
+    if (axis == ORC_COL) {
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int64_t i = 0; i < m; ++i) s += Y[i * n + j];
+            g[j] = s;
+        }
+        return 0;
+    }
+    return -1;
+}

@@ -376,3 +376,28 @@ def test_dgelu_is_upstream_times_slope_of_gelu(dt):
     h = 1e-5
     slope = (oracle.act_pass(Pd + h, "gelu_bias") - oracle.act_pass(Pd - h, "gelu_bias")) / (2 * h)
     assert np.allclose(D, C * slope, rtol=0, atol=1e-8)
+
+
+def test_bgrad_sums_along_the_other_axis():
+    """O8 against numpy's sums on a non-square matrix (an axis swap changes
+    the length), and exact counts for an all-ones backward result."""
+    rng = np.random.default_rng(10)
+    Y = rng.standard_normal((7, 12))
+    assert np.allclose(oracle.bgrad_pass(Y, "row"), Y.sum(axis=1), rtol=0, atol=1e-12)
+    assert np.allclose(oracle.bgrad_pass(Y, "col"), Y.sum(axis=0), rtol=0, atol=1e-12)
+    ones = np.ones((5, 9))
+    assert np.array_equal(oracle.bgrad_pass(ones, "row"), np.full(5, 9.0))
+    assert np.array_equal(oracle.bgrad_pass(ones, "col"), np.full(9, 5.0))
+
+
+def test_bgrad_of_drelu_counts_mask_bits():
+    """With C = 1, the DRELU result is the mask itself, so its bias gradient
+    counts the set bits of each row (row axis) or column (col axis)."""
+    rng = np.random.default_rng(11)
+    m, n = 6, 140
+    P = rng.standard_normal((m, n))
+    W = oracle.mask_pass(P, ((n + 127) // 128) * 4)
+    Y = oracle.drelu_pass(np.ones((m, n)), W)
+    bits = np.unpackbits(W.view(np.uint8), axis=1, bitorder="little")[:, :n]
+    assert np.array_equal(oracle.bgrad_pass(Y, "row"), bits.sum(axis=1).astype(np.float64))
+    assert np.array_equal(oracle.bgrad_pass(Y, "col"), bits.sum(axis=0).astype(np.float64))
