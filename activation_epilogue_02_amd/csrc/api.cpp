@@ -28,6 +28,8 @@ struct ge_plan_s {
     size_t ws_c = 0;         // unfused intermediate bytes
     size_t ws_partial = 0;   // split-K partial bytes
     size_t ws_counters = 0;  // split-K counter bytes
+    size_t ws_bgrad = 0;     // bias-gradient partial bytes
+    int32_t bgrad_parts = 0; // bias-gradient partials per entry
     int64_t ldaux = 0;       // mask row stride, 32-bit words
 };
 
@@ -64,11 +66,14 @@ bool has_bias(int e) {
 // Epilogues with an aux buffer: a bit mask (written by RELU_AUX_BIAS, read by
 // DRELU) or a pre-activation matrix in D's dtype (written by GELU_AUX_BIAS,
 // read by DGELU).
+bool is_bgrad(int e) { return e == GE_EPILOG_DRELU_BGRAD || e == GE_EPILOG_DGELU_BGRAD; }
 bool has_aux(int e) {
     return e == GE_EPILOG_RELU_AUX_BIAS || e == GE_EPILOG_DRELU || e == GE_EPILOG_GELU_AUX_BIAS ||
-           e == GE_EPILOG_DGELU;
+           e == GE_EPILOG_DGELU || is_bgrad(e);
 }
-bool aux_is_matrix(int e) { return e == GE_EPILOG_GELU_AUX_BIAS || e == GE_EPILOG_DGELU; }
+bool aux_is_matrix(int e) {
+    return e == GE_EPILOG_GELU_AUX_BIAS || e == GE_EPILOG_DGELU || e == GE_EPILOG_DGELU_BGRAD;
+}
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -173,7 +178,7 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
 
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* pref) {
     if (!h) return GE_ERR_NULL;
-    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_DGELU) return GE_ERR_EPILOG;
+    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_DGELU_BGRAD) return GE_ERR_EPILOG;
     if (bias_axis != GE_BIAS_ROW && bias_axis != GE_BIAS_COL) return GE_ERR_EPILOG;
     ge_pref pr = {0, 0, 0, 0};
     if (pref) pr = *pref;
@@ -235,6 +240,17 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.k_per_split = (int32_t)d.k;
     }
     q.ws_c = q.unfused ? round_up((size_t)d.m * (size_t)d.ldd * elem_size(d.d_type), 256) : 0;
+    // bias gradient: one fp32 partial per tile row (COL) or column (ROW) and
+    // gradient entry; the unfused pair sums its stored D in blocks of 256
+    q.ws_bgrad = 0;
+    q.bgrad_parts = 0;
+    if (is_bgrad(epilog)) {
+        const bool col = bias_axis == GE_BIAS_COL;
+        const int64_t parts = q.unfused ? ceil_div(col ? d.m : d.n, 256) : (col ? q.tiles_m : q.tiles_n);
+        if (parts > 65535) return GE_ERR_SHAPE;
+        q.bgrad_parts = (int32_t)parts;
+        q.ws_bgrad = round_up((size_t)parts * (size_t)(col ? d.n : d.m) * sizeof(float), 256);
+    }
     q.planned = true;
     *h = q;
     return GE_OK;
@@ -243,7 +259,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
 int gemm_epilog_workspace_size(ge_handle h, size_t* bytes) {
     if (!h || !bytes) return GE_ERR_NULL;
     if (!h->planned) return GE_ERR_STATE;
-    *bytes = h->ws_c + h->ws_partial + h->ws_counters;
+    *bytes = h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad;
     return GE_OK;
 }
 
@@ -263,18 +279,30 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     // a pointer may be NULL only when its buffer holds no elements
     if ((!A && d.m * d.k > 0) || (!B && d.k * d.n > 0) || (!D && d.m * d.n > 0)) return GE_ERR_NULL;
     const int64_t bias_len = h->axis == GE_BIAS_ROW ? d.m : d.n;
-    if (has_bias(h->epilog) && !bias && bias_len > 0) return GE_ERR_NULL;
-    const bool want_aux = has_aux(h->epilog) && d.m > 0;
+    if ((has_bias(h->epilog) || is_bgrad(h->epilog)) && !bias && bias_len > 0) return GE_ERR_NULL;
+    const bool want_aux = has_aux(h->epilog) && d.m > 0 && d.n > 0;   // else aux holds nothing
     if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
     if (d.a_type != GE_F8_E4M3 && (scale_a || scale_b)) return GE_ERR_DTYPE;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||
         !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
         return GE_ERR_ALIGN;
-    const size_t need = h->ws_c + h->ws_partial + h->ws_counters;
+    const size_t need = h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad;
     if (need > 0 && (!workspace || workspace_bytes < need)) return GE_ERR_WORKSPACE;
     if (test_fail_launch()) return GE_ERR_HIP;
-    if (d.m == 0 || d.n == 0) return GE_OK;   // empty output: nothing to compute
+    if (d.m == 0 || d.n == 0) {
+        // empty output; a bias gradient over no rows (or columns) is zero
+        if (is_bgrad(h->epilog) && bias_len > 0) {
+            KernelArgs z;
+            memset(&z, 0, sizeof(z));
+            z.bias = bias;
+            z.m = (int32_t)d.m;
+            z.n = (int32_t)d.n;
+            z.axis = h->axis;
+            if (launch_bgrad_reduce(d.d_type, z, 0, stream) != 0) return GE_ERR_HIP;
+        }
+        return GE_OK;
+    }
 
     KernelArgs a;
     memset(&a, 0, sizeof(a));
@@ -306,6 +334,8 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
         if (launch_clear_counters(a.counters, h->tiles_n, stream) != 0) return GE_ERR_HIP;
     }
 
+    if (is_bgrad(h->epilog)) a.partial = (float*)(ws + h->ws_c + h->ws_partial + h->ws_counters);
+
     KernelArgs k1 = a;
     if (h->unfused) {
         // kernel 1: the plain product, rounded to d_type, into the workspace
@@ -325,7 +355,11 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
         // kernel 2: D = act(C + bias) (+ mask)
         err = launch_elementwise(d.d_type, a, ws, stream);
         if (err != 0) return GE_ERR_HIP;
+        // the bias gradient of the stored D
+        if (is_bgrad(h->epilog) && launch_bgrad_sum(d.d_type, a, h->bgrad_parts, stream) != 0)
+            return GE_ERR_HIP;
     }
+    if (is_bgrad(h->epilog) && launch_bgrad_reduce(d.d_type, a, h->bgrad_parts, stream) != 0) return GE_ERR_HIP;
     return GE_OK;
 }
 
@@ -369,7 +403,7 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
              t ? (t->kernel == 2 || t->kernel == 4 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
              h->split_k,
              h->unfused,
-             h->ws_c + h->ws_partial + h->ws_counters, (long long)h->ldaux);
+             h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad, (long long)h->ldaux);
     return GE_OK;
 }
 

@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c)
     const int ep = p.epilog;
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
     const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;
-    const bool want_grad = ep == GE_EPILOG_DRELU || ep == GE_EPILOG_DGELU;
+    const bool want_grad = epilog_is_grad(ep);
     if (n0 >= p.n) {
         if (want_aux) p.aux[row * p.ldaux + w] = 0u;   // row padding
         return;
@@ -86,6 +86,74 @@ int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* 
         break;
     case GE_BF16:
         hipLaunchKernelGGL(ge_ew_kernel<GE_BF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        break;
+    default:
+        return (int)hipErrorInvalidDeviceFunction;
+    }
+    return (int)hipGetLastError();
+}
+
+// ---- bias gradient: partial sums and their reduction -----------------------------
+// Unfused pair: sums of the stored D along the bias-gradient axis over blocks
+// of 256 rows (COL: partial[rb * n + j]) or 256 columns (ROW: partial[cb * m + i]).
+template <int DT>
+__global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int blk = blockIdx.y;
+    if (p.axis == GE_BIAS_COL) {
+        if (idx >= p.n) return;
+        const int i1 = min(p.m, (blk + 1) * 256);
+        float v = 0.0f;
+        for (int i = blk * 256; i < i1; ++i) v += load_scalar<DT>(p.D, (int64_t)i * p.ldd + idx);
+        p.partial[(int64_t)blk * p.n + idx] = v;
+    } else {
+        if (idx >= p.m) return;
+        const int j1 = min(p.n, (blk + 1) * 256);
+        float v = 0.0f;
+        for (int j = blk * 256; j < j1; ++j) v += load_scalar<DT>(p.D, (int64_t)idx * p.ldd + j);
+        p.partial[(int64_t)blk * p.m + idx] = v;
+    }
+}
+
+// g[idx] = sum over t = 0 .. parts-1 of partial[t * len + idx], in that
+// order, converted to D's dtype and written to the bias pointer (the
+// gradient's output).  parts = 0 writes zeros (an empty sum).
+template <int DT>
+__global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p, int parts) {
+    const int len = p.axis == GE_BIAS_COL ? p.n : p.m;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= len) return;
+    float v = 0.0f;
+    for (int t = 0; t < parts; ++t) v += p.partial[(int64_t)t * len + idx];
+    store_one<DT>((void*)p.bias, idx, v);
+}
+
+int launch_bgrad_sum(int d_type, const KernelArgs& args, int parts, void* stream) {
+    const int len = args.axis == GE_BIAS_COL ? args.n : args.m;
+    if (len <= 0 || parts <= 0) return 0;
+    const dim3 grid((unsigned)((len + 255) / 256), (unsigned)parts);
+    switch (d_type) {
+    case GE_F32: hipLaunchKernelGGL(ge_sum_kernel<GE_F32>, grid, dim3(256), 0, (hipStream_t)stream, args); break;
+    case GE_F16: hipLaunchKernelGGL(ge_sum_kernel<GE_F16>, grid, dim3(256), 0, (hipStream_t)stream, args); break;
+    case GE_BF16: hipLaunchKernelGGL(ge_sum_kernel<GE_BF16>, grid, dim3(256), 0, (hipStream_t)stream, args); break;
+    default: return (int)hipErrorInvalidDeviceFunction;
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_bgrad_reduce(int d_type, const KernelArgs& args, int parts, void* stream) {
+    const int len = args.axis == GE_BIAS_COL ? args.n : args.m;
+    if (len <= 0) return 0;
+    const unsigned grid = (unsigned)((len + 255) / 256);
+    switch (d_type) {
+    case GE_F32:
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F32>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
+        break;
+    case GE_F16:
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
+        break;
+    case GE_BF16:
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_BF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
         break;
     default:
         return (int)hipErrorInvalidDeviceFunction;

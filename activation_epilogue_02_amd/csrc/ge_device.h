@@ -190,8 +190,22 @@ __host__ __device__ __forceinline__ bool epilog_has_bias(int epilog) {
            epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS;
 }
 
-// Apply the activation of an epilogue to a pre-activation value.  DRELU and
-// DGELU pass the product through; their factor comes from grad_factor8.
+// Backward epilogues (the product scaled by an activation derivative read
+// from aux), and those of them that also return the bias gradient.
+__host__ __device__ __forceinline__ bool epilog_is_grad(int epilog) {
+    return epilog == GE_EPILOG_DRELU || epilog == GE_EPILOG_DGELU || epilog == GE_EPILOG_DRELU_BGRAD ||
+           epilog == GE_EPILOG_DGELU_BGRAD;
+}
+__host__ __device__ __forceinline__ bool epilog_is_bgrad(int epilog) {
+    return epilog == GE_EPILOG_DRELU_BGRAD || epilog == GE_EPILOG_DGELU_BGRAD;
+}
+__host__ __device__ __forceinline__ bool epilog_reads_mask(int epilog) {
+    return epilog == GE_EPILOG_DRELU || epilog == GE_EPILOG_DRELU_BGRAD;
+}
+
+// Apply the activation of an epilogue to a pre-activation value.  The
+// backward epilogues pass the product through; their factor comes from
+// grad_factor8.
 __device__ __forceinline__ float activate(int epilog, float x) {
     if (epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS) return x > 0.0f ? x : 0.0f;
     if (epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS) return gelu_tanh(x);
@@ -210,7 +224,7 @@ __device__ __forceinline__ void grad_factor8(const KernelArgs& p, int epilog, in
         for (int j = 0; j < 8; ++j) f[j] = 0.0f;
         return;
     }
-    if (epilog == GE_EPILOG_DRELU) {
+    if (epilog_reads_mask(epilog)) {
         const uint32_t w = p.aux[m * p.ldaux + (nc >> 5)] >> (nc & 31);
 #pragma unroll
         for (int j = 0; j < 8; ++j) f[j] = ((w >> j) & 1u) ? 1.0f : 0.0f;
@@ -231,7 +245,81 @@ __device__ __forceinline__ void grad_factor8(const KernelArgs& p, int epilog, in
 // Apply the backward factor: DGELU multiplies; DRELU selects (C or +0), so
 // that a masked entry is exactly zero whatever C holds (-0, inf, NaN).
 __device__ __forceinline__ float grad_apply(int epilog, float x, float f) {
-    return epilog == GE_EPILOG_DRELU ? (f != 0.0f ? x : 0.0f) : x * f;
+    return epilog_reads_mask(epilog) ? (f != 0.0f ? x : 0.0f) : x * f;
+}
+
+// ---- bias gradient (DRELU_BGRAD, DGELU_BGRAD) --------------------------------
+// The tile kernels sum their fp32 outputs along the bias-gradient axis: COL
+// (the bias was added to every row: g[j] = sum_i D[i][j]) gives per-column
+// sums over the tile's rows, ROW (g[i] = sum_j D[i][j]) per-row sums over its
+// columns.  Each lane adds what it computed; the lanes sharing a column (COL)
+// or row (ROW) and then the waves sharing it are summed in a fixed order, and
+// the tile writes its partial to partial[t * len + idx] (t the tile's row
+// index for COL, column index for ROW; len = n or m).  A second kernel sums
+// the partials over t in order, so the result is deterministic.
+template <int FM, int FN>
+struct BgradAcc {
+    float col[FN][2][8];   // COL: columns nb + 16g + 8h + j of fragment column fn
+    float row[FM];         // ROW: the lane's row of fragment row fm
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) col[f][g][j] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < FM; ++f) row[f] = 0.0f;
+    }
+};
+
+// Reduce a tile's sums and write its partial.  smem holds at least
+// max(WM*BN, WN*BM) floats and is free once every wave passed the first
+// barrier here; every thread of the workgroup must call this.
+template <int BM, int BN, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void bgrad_tile(const KernelArgs& p, BgradAcc<FM, FN>& acc, float* red, int tm, int tn,
+                                           int wm, int wn, int lane, int tid, int nthreads) {
+    constexpr int TM = BM / WM, TN = BN / WN;
+    const int r32 = lane & 31, h = lane >> 5;
+    const bool col_axis = p.axis == GE_BIAS_COL;
+    __syncthreads();   // every wave is done with the LDS stages
+    if (col_axis) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float v = acc.col[f][g][j];
+#pragma unroll
+                    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);   // the 32 rows of a half
+                    if (r32 == 0) red[wm * BN + wn * TN + f * 32 + 16 * g + 8 * h + j] = v;
+                }
+    } else {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const float v = acc.row[f] + __shfl_xor(acc.row[f], 32);   // both column halves
+            if (h == 0) red[wn * BM + wm * TM + f * 32 + r32] = v;
+        }
+    }
+    __syncthreads();
+    if (col_axis) {
+        for (int c = tid; c < BN; c += nthreads) {
+            const int n = tn * BN + c;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WM; ++w) v += red[w * BN + c];
+            if (n < p.n) p.partial[(int64_t)tm * p.n + n] = v;
+        }
+    } else {
+        for (int r = tid; r < BM; r += nthreads) {
+            const int m = tm * BM + r;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) v += red[w * BM + r];
+            if (m < p.m) p.partial[(int64_t)tn * p.m + m] = v;
+        }
+    }
 }
 
 // GELU_AUX_BIAS: store the pre-activation of the 8 columns nc .. nc+7 of

@@ -19,7 +19,7 @@ struct KernelArgs {
                            // pre-activation matrix in D's dtype; else NULL
     const float* scale_a;  // NULL = 1.0
     const float* scale_b;  // NULL = 1.0
-    float* partial;        // split-K fp32 partials (small-m path), or NULL
+    float* partial;        // fp32 partials: split-K (small-m path) or bias gradient, or NULL
     uint32_t* counters;    // split-K arrival counters (small-m path), or NULL
     int32_t m, n, k;
     int32_t epilog, axis;
@@ -79,6 +79,13 @@ int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsi
 
 // Zero n split-K arrival counters on `stream` (a kernel, graph-capturable).
 int launch_clear_counters(uint32_t* p, int n, void* stream);
+
+// Bias gradient.  launch_bgrad_sum: the unfused pair's partial sums of the
+// stored D over blocks of 256 rows (COL) or columns (ROW) into args.partial
+// (`parts` blocks).  launch_bgrad_reduce: sum `parts` partials per entry, in
+// order, into args.bias (D's dtype); parts = 0 writes zeros.
+int launch_bgrad_sum(int d_type, const KernelArgs& args, int parts, void* stream);
+int launch_bgrad_reduce(int d_type, const KernelArgs& args, int parts, void* stream);
 
 // Launch the unfused pair's elementwise kernel: D = act(C + bias) (+ mask),
 // reading C (d_type, leading dimension ldd) from `c`.

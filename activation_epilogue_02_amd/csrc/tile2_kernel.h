@@ -525,7 +525,11 @@ ge_tile2_kernel(KernelArgs p) {
     const bool row_bias = p.axis == GE_BIAS_ROW;
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
     const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;                    // aux <- P
-    const bool want_grad = ep == GE_EPILOG_DRELU || ep == GE_EPILOG_DGELU;  // D = C * f(aux)
+    const bool want_grad = epilog_is_grad(ep);                              // D = C * f(aux)
+    const bool want_bgrad = epilog_is_bgrad(ep);                            // + bias gradient
+    const bool bgrad_col = p.axis == GE_BIAS_COL;
+    BgradAcc<C::FM, C::FN> bg;
+    bg.clear();
 
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
@@ -578,6 +582,14 @@ ge_tile2_kernel(KernelArgs p) {
                     if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
                     v[g][j] = want_grad ? grad_apply(ep, x, gf[j]) : activate(ep, x);
                 }
+                if (want_bgrad) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float val = (mok && nc + j < N) ? v[g][j] : 0.0f;
+                        if (bgrad_col) bg.col[fn][g][j] += val;
+                        else bg.row[fm] += val;
+                    }
+                }
                 if (mok) {
                     const int64_t idx = (int64_t)m * p.ldd + nc;
                     if (full) store8<DOUT>(p.D, idx, v[g]);
@@ -595,6 +607,8 @@ ge_tile2_kernel(KernelArgs p) {
             }
         }
     }
+    if (want_bgrad)
+        bgrad_tile<BM, BN, WM, WN, C::FM, C::FN>(p, bg, (float*)smem, tm, tn, wm, wn, lane, tid, C::NT);
     if (want_aux && tn == p.tiles_n - 1) {
         const int w0 = (p.tiles_n * BN) >> 5;
         const int nw = p.ldaux - w0;

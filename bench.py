@@ -241,10 +241,11 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
         return t.view(torch.int16).numpy().view(np.uint16)
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    grad = w.epilog in ("drelu", "dgelu")
+    grad = w.epilog in ("drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad")
+    mask_in = w.epilog in ("drelu", "drelu_bgrad")
     if grad:
         aux_c = aux_in.detach().cpu().contiguous()
-        aux_c = aux_c.numpy().view(np.uint32) if w.epilog == "drelu" else raw(aux_c)
+        aux_c = aux_c.numpy().view(np.uint32) if mask_in else raw(aux_c)
     Bc = raw(inp.B)
     bias = raw(inp.bias).reshape(-1)
     sa = float(inp.scale_a.item()) if inp.scale_a is not None else 1.0
@@ -258,10 +259,11 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
         A_rows = raw(inp.A[start:start + rows])
         t0 = time.perf_counter()
         C = oracle.gemm(A_rows, w.in_dtype, Bc, w.in_dtype, w.op_b, sa, sb)
-        if w.epilog == "drelu":
-            oracle.drelu_pass(C, aux_c[start:start + rows])
-        elif w.epilog == "dgelu":
-            oracle.dgelu_pass(C, aux_c[start:start + rows], w.out_dtype)
+        if grad:
+            Y = (oracle.drelu_pass(C, aux_c[start:start + rows]) if mask_in
+                 else oracle.dgelu_pass(C, aux_c[start:start + rows], w.out_dtype))
+            if w.epilog.endswith("_bgrad"):
+                oracle.bgrad_pass(Y, w.axis)
         else:
             b = bias[start:start + rows] if w.axis == "row" else bias
             P = oracle.bias_pass(C, b, w.out_dtype, w.axis)
@@ -316,8 +318,12 @@ def main():
     copies = [inp]
     for r in range(1, rot):
         copies.append(synth.make_inputs(w, device="cuda", seed=w.seed + 100 * r))
-    grad = w.epilog in ("drelu", "dgelu")   # backward epilogues: no bias, an aux input
-    bias = [None if grad else c.bias.reshape(-1).contiguous() for c in copies]
+    # backward epilogues: an aux input and no bias read; the bias-gradient
+    # ones write the gradient to the bias pointer
+    grad = w.epilog in ("drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad")
+    bgrad = w.epilog.endswith("_bgrad")
+    bias = [torch.empty_like(c.bias.reshape(-1)) if bgrad else
+            (None if grad else c.bias.reshape(-1).contiguous()) for c in copies]
     aux_in = [synth.make_aux(w, device="cuda", seed=w.seed + 100 * r) if grad else None
               for r in range(rot)]
 

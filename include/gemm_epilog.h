@@ -100,9 +100,15 @@ typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op;
  *   DGELU          D = C * GELU'(P), P read from aux (an input, the matrix
  *                  GELU_AUX_BIAS wrote); GELU' is the derivative of the tanh
  *                  form above
- * DRELU and DGELU read no bias (C is the gradient arriving from the next
- * layer's product).  Conversion of the fp32 result to D's dtype rounds to
- * nearest even. */
+ *   DRELU_BGRAD, DGELU_BGRAD
+ *                  D as DRELU / DGELU, and the bias gradient written to the
+ *                  bias pointer (an output here, D's dtype): the fp32 values
+ *                  of D summed along the other axis, g[i] = sum_j D[i][j]
+ *                  (ROW, m values) or g[j] = sum_i D[i][j] (COL, n values);
+ *                  the unfused pair sums the stored, rounded D instead
+ * The backward epilogues read no bias (C is the gradient arriving from the
+ * next layer's product).  Conversion of the fp32 result to D's dtype rounds
+ * to nearest even. */
 typedef enum {
     GE_EPILOG_NONE = 0,
     GE_EPILOG_BIAS = 1,
@@ -111,7 +117,9 @@ typedef enum {
     GE_EPILOG_GELU_BIAS = 4,
     GE_EPILOG_GELU_AUX_BIAS = 5,
     GE_EPILOG_DRELU = 6,
-    GE_EPILOG_DGELU = 7
+    GE_EPILOG_DGELU = 7,
+    GE_EPILOG_DRELU_BGRAD = 8,
+    GE_EPILOG_DGELU_BGRAD = 9
 } ge_epilog;
 
 /* Bias broadcast axis.
@@ -182,18 +190,21 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
  * unknown tile id or split in p). */
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* p);
 
-/* Bytes of device workspace execute() needs (0 for the fused paths; m*ldd
- * elements of d_type, rounded up to 256 bytes, for the unfused pair).
+/* Bytes of device workspace execute() needs: 0 for most fused launches; the
+ * unfused pair's intermediate (m*ldd elements of d_type); the small-m path's
+ * split-K partials and counters; the bias-gradient epilogues' fp32 partial
+ * sums (one per tile row or column and gradient entry).  Each part is rounded
+ * up to 256 bytes.
  * Errors: GE_ERR_NULL, GE_ERR_STATE (not planned). */
 int gemm_epilog_workspace_size(ge_handle h, size_t* bytes);
 
 /* Row stride of the aux buffer in bits.
- * Mask epilogues (RELU_AUX_BIAS writes it, DRELU reads it), and any handle
+ * Mask epilogues (RELU_AUX_BIAS writes it, DRELU and DRELU_BGRAD read it), and any handle
  * not planned with a pre-activation epilogue: round_up(n, 128), so each row
  * starts 16-byte aligned.  The mask is a row-major bit matrix of m rows: bit
  * (i,j) is bit j%32 of the little-endian 32-bit word at word index
  * i*(ld_bits/32) + j/32.  RELU_AUX_BIAS writes bits j >= n of a row as 0.
- * Pre-activation epilogues (GELU_AUX_BIAS writes it, DGELU reads it):
+ * Pre-activation epilogues (GELU_AUX_BIAS writes it, DGELU and DGELU_BGRAD read it):
  * round_up(n, 128) elements of D's dtype, i.e. that many times 32 or 16 bits;
  * a row-major m-row matrix whose padding columns are never written.
  * The buffer must hold m*ld_bits/8 bytes.  Errors: GE_ERR_NULL. */
@@ -203,11 +214,12 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits);
  * null stream).  Asynchronous: returns once the kernel(s) are queued.
  *   A, B     device operands (see ge_desc)
  *   bias     device vector of m (ROW) or n (COL) bias_type values; NULL
- *            only for NONE, DRELU and DGELU (which read no bias)
+ *            only for NONE, DRELU and DGELU (which read no bias); for
+ *            DRELU_BGRAD and DGELU_BGRAD the bias gradient is written here
  *   D        device output, m x n with leading dimension ldd
  *   aux      device aux buffer (see gemm_epilog_aux_ld); required for
- *            RELU_AUX_BIAS and GELU_AUX_BIAS (written) and for DRELU and
- *            DGELU (read), must be NULL otherwise
+ *            RELU_AUX_BIAS and GELU_AUX_BIAS (written) and for the backward
+ *            epilogues (read), must be NULL otherwise
  *   scale_a, scale_b
  *            device pointers to one fp32 each, the per-tensor dequantisation
  *            factors of fp8 inputs (D uses scale_a*scale_b*A*B); NULL means

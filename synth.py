@@ -36,7 +36,7 @@ class Workload:
     in_dtype: str         # dtype of A and B
     out_dtype: str        # dtype of D (and of the bias)
     epilog: str           # none | bias | relu_bias | relu_aux_bias | gelu_bias
-                          # | gelu_aux_bias | drelu | dgelu
+                          # | gelu_aux_bias | drelu | dgelu | drelu_bgrad | dgelu_bgrad
     axis: str             # row: bias has m values; col: bias has n values
     op_b: int             # 0: B is k x n row-major; 1: B is n x k (Linear weight)
     seed: int
@@ -53,12 +53,13 @@ class Workload:
         1-bit mask (written by relu_aux_bias, read by drelu) or the m x n
         pre-activation in D's dtype (written by gelu_aux_bias, read by dgelu)."""
         ea, eo = ELEM_SIZE[self.in_dtype], ELEM_SIZE[self.out_dtype]
+        # the bias is read, or (bias-gradient epilogues) written, once
         biased = self.epilog not in ("none", "drelu", "dgelu")
         nb = (self.m if self.axis == "row" else self.n) * eo if biased else 0
         aux = 0
-        if self.epilog in ("relu_aux_bias", "drelu"):
+        if self.epilog in ("relu_aux_bias", "drelu", "drelu_bgrad"):
             aux = self.m * (((self.n + 127) // 128) * 16)
-        elif self.epilog in ("gelu_aux_bias", "dgelu"):
+        elif self.epilog in ("gelu_aux_bias", "dgelu", "dgelu_bgrad"):
             aux = self.m * self.n * eo
         scales = 8 if self.in_dtype == "e4m3" else 0
         return (self.m * self.k + self.k * self.n) * ea + nb + self.m * self.n * eo + aux + scales
@@ -97,6 +98,11 @@ WORKLOADS = {
                     ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
     "F1c": Workload("F1c", "bf16 DRELU 8192x8192x8192", 8192, 8192, 8192, "bf16", "bf16",
                     "drelu", "row", 0, 1008, ("normal", 1 / math.sqrt(8192)),
+                    ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
+    # the backward of a Linear layer's GELU with its bias gradient: the bias
+    # was added to every row, so its gradient sums the columns
+    "F1d": Workload("F1d", "bf16 DGELU_BGRAD 8192x8192x8192", 8192, 8192, 8192, "bf16", "bf16",
+                    "dgelu_bgrad", "col", 0, 1009, ("normal", 1 / math.sqrt(8192)),
                     ("normal", 1 / math.sqrt(8192)), ("normal", 0.1)),
 }
 
@@ -188,11 +194,11 @@ def make_aux(w: Workload, device="cpu", seed: Optional[int] = None) -> torch.Ten
     ~ N(0, AUX_PRE_VARIANCE) in D's dtype (m x aux_ld_elems)."""
     gen = torch.Generator(device=device)
     gen.manual_seed((w.seed if seed is None else seed) + 1)
-    if w.epilog == "drelu":
+    if w.epilog in ("drelu", "drelu_bgrad"):
         t = torch.randint(0, 2 ** 32, (w.m, aux_ld_words(w.n)), generator=gen, device=device,
                           dtype=torch.int64)
         return (t - 2 ** 31).to(torch.int32)
-    if w.epilog == "dgelu":
+    if w.epilog in ("dgelu", "dgelu_bgrad"):
         x = _draw(gen, (w.m, aux_ld_elems(w.n)), ("normal", AUX_PRE_VARIANCE), device)
         return x.to(TORCH_DTYPE[w.out_dtype])
     raise ValueError(f"{w.epilog} reads no aux input")

@@ -78,7 +78,13 @@ class Result:
         self.__dict__.update(kw)
 
 
-GRAD_EPILOGS = ("drelu", "dgelu")
+GRAD_EPILOGS = ("drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad")
+BGRAD_EPILOGS = ("drelu_bgrad", "dgelu_bgrad")
+
+
+def base_grad(ep: str) -> str:
+    """The backward epilogue without the bias gradient."""
+    return ep.replace("_bgrad", "")
 
 
 def aux_ld_elems(n: int) -> int:
@@ -91,7 +97,7 @@ def make_aux_input(w: synth.Workload, device="cuda", seed=None) -> torch.Tensor:
     DRELU (padding bits random too: they must be ignored), a pre-activation
     matrix ~ N(0, 4) in D's dtype for DGELU (padding columns NaN: never read)."""
     g = torch.Generator().manual_seed(w.seed + 17 if seed is None else seed)
-    if w.epilog == "drelu":
+    if base_grad(w.epilog) == "drelu":
         words = synth.aux_ld_words(w.n)
         t = torch.randint(-2 ** 31, 2 ** 31 - 1, (w.m, words), generator=g, dtype=torch.int64)
         return t.to(torch.int32).to(device)
@@ -131,11 +137,18 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
             aux = aux_in if aux_in is not None else make_aux_input(w, device)
         ws = torch.empty(g.ws_bytes, dtype=torch.uint8, device=device) if g.ws_bytes else None
         with_bias = w.epilog not in ("none",) + GRAD_EPILOGS
+        if w.epilog in BGRAD_EPILOGS:
+            # the bias gradient is written to the bias pointer: NaN-filled so
+            # that an entry left unwritten shows
+            bias = torch.full((w.m if w.axis == "row" else w.n,), float("nan"),
+                              dtype=synth.TORCH_DTYPE[d_dt], device=device)
+            with_bias = True
         g.execute(A, Bm, bias if with_bias else None, D, aux, sa, sb, ws)
         torch.cuda.synchronize()
         return Result(D=D, aux=aux, A=A, B=Bm, bias=bias, sa=sa, sb=sb, lda=lda, ldb=ldb,
                       ldd=ldd, desc=desc,
-                      ldw=(g.aux_ld_bits // 32) if w.epilog in ("relu_aux_bias", "drelu") else None)
+                      ldw=(g.aux_ld_bits // 32) if w.epilog in ("relu_aux_bias", "drelu", "drelu_bgrad")
+                      else None)
     finally:
         g.free()
 
@@ -148,9 +161,9 @@ def oracle_full(w: synth.Workload, r: Result):
     sa = float(r.sa.item()) if r.sa is not None else 1.0
     sb = float(r.sb.item()) if r.sb is not None else 1.0
     C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
-    if w.epilog == "drelu":
+    if base_grad(w.epilog) == "drelu":
         return oracle.drelu_pass(C, codes(r.aux)), C, None
-    if w.epilog == "dgelu":
+    if base_grad(w.epilog) == "dgelu":
         return oracle.dgelu_pass(C, codes(r.aux), d_dt), C, None
     if w.epilog == "none":
         P = C
@@ -185,6 +198,19 @@ def check_full(w: synth.Workload, r: Result, tol: Optional[float] = None):
         check_mask(w, codes(r.aux), M, P)
     if w.epilog == "gelu_aux_bias":
         check_pre_aux(w, r, P, tol)
+    if w.epilog in BGRAD_EPILOGS:
+        check_bgrad(w, r, Y, tol)
+    return err
+
+
+def check_bgrad(w, r, Y, tol):
+    """The bias gradient written to the bias pointer against the oracle's O8
+    on the unrounded backward result."""
+    want = oracle.bgrad_pass(Y, w.axis)
+    got = oracle.decode(np.ascontiguousarray(codes(r.bias)), w.out_dtype)
+    assert np.isfinite(got).all(), f"bias gradient not written everywhere: {r.desc}"
+    err = rel_fro(got, want)
+    assert err <= tol, f"bias gradient rel-Frobenius {err:.3e} > {tol:.1e}: {r.desc}"
     return err
 
 
@@ -269,7 +295,7 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
         Pr = oracle.bias_entries(Cr.ravel(), ri, rj, bias_c, d_dt, w.axis).reshape(Cr.shape)
     if grad:
         aux_r = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))
-        Yr = (oracle.drelu_pass(Cr, aux_r) if w.epilog == "drelu"
+        Yr = (oracle.drelu_pass(Cr, aux_r) if base_grad(w.epilog) == "drelu"
               else oracle.dgelu_pass(Cr, aux_r, d_dt))
     else:
         Yr = oracle.act_pass(Pr, w.epilog)
@@ -310,7 +336,7 @@ def grad_entries(w: synth.Workload, r: Result, Cv: np.ndarray, rows: np.ndarray,
     cols = np.asarray(cols, dtype=np.int64)
     aux_rows = codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))
     Cm = np.ascontiguousarray(np.asarray(Cv, dtype=np.float64).reshape(-1, 1))
-    if w.epilog == "drelu":
+    if base_grad(w.epilog) == "drelu":
         # one-column problems: column 0 of row t is entry t's mask word, shifted
         words = (aux_rows[np.arange(len(cols)), cols // 32] >> (cols % 32).astype(np.uint32)) & 1
         return oracle.drelu_pass(Cm, np.ascontiguousarray(words.reshape(-1, 1).astype(np.uint32))).ravel()

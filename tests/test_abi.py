@@ -99,7 +99,7 @@ def test_plan_validation_and_state():
     try:
         assert status_of(B.gemm_epilog_workspace_size, h) == B.GE_ERR_STATE
         assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATE
-        assert status_of(B.gemm_epilog_plan, h, 8, 0) == B.GE_ERR_EPILOG
+        assert status_of(B.gemm_epilog_plan, h, 10, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, -1, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 2) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(0, 0, 99, 0)) == B.GE_ERR_SHAPE
@@ -171,13 +171,37 @@ def test_training_epilogues_validation():
             B.gemm_epilog_free(h)
 
 
+def test_bias_gradient_workspace_and_validation():
+    """The bias-gradient epilogues write the gradient to the bias pointer
+    (required) and need fp32 partials: one per tile row (col axis) or tile
+    column (row axis) and gradient entry; the unfused pair one per 256-row or
+    -column block."""
+    h = B.gemm_epilog_create(B.make_desc(1000, 600, 64, "bf16", "bf16", 0))
+    try:
+        ex = lambda *a, **k: status_of(B.gemm_epilog_execute, h, *a, **k)
+        r256 = lambda x: (x + 255) // 256 * 256
+        B.gemm_epilog_plan(h, "dgelu_bgrad", "col", B.ge_pref(1, 0, 11, 0))   # 256 x 256 tiles
+        assert B.gemm_epilog_workspace_size(h) == r256(4 * 600 * 4)
+        assert ex(FAKE, FAKE, None, FAKE, FAKE, workspace=FAKE, workspace_bytes=1 << 20) == B.GE_ERR_NULL
+        assert ex(FAKE, FAKE, FAKE, FAKE, None, workspace=FAKE, workspace_bytes=1 << 20) == B.GE_ERR_EPILOG
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_WORKSPACE
+        B.gemm_epilog_plan(h, "drelu_bgrad", "row", B.ge_pref(1, 0, 11, 0))
+        assert B.gemm_epilog_workspace_size(h) == r256(3 * 1000 * 4)
+        assert B.gemm_epilog_aux_ld(h) == 640                                  # the mask's stride
+        B.gemm_epilog_plan(h, "dgelu_bgrad", "col", B.ge_pref(0, 1, 0, 0))    # unfused pair
+        assert B.gemm_epilog_workspace_size(h) == r256(1000 * 600 * 2) + r256(4 * 600 * 4)
+        assert B.gemm_epilog_aux_ld(h) == 640 * 16
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_training_epilogues_take_the_tile_path():
     """The small-m kernel serves the inference epilogues only: automatic
     planning of a batch-16 Linear with a training epilogue takes the tile
     kernel, and forcing the small-m path is refused."""
     h = B.gemm_epilog_create(B.make_desc(16, 4096, 4096, "f16", "f16", 1))
     try:
-        for ep in ("gelu_aux_bias", "drelu", "dgelu"):
+        for ep in ("gelu_aux_bias", "drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad"):
             B.gemm_epilog_plan(h, ep, "col")
             assert "path=tile" in B.gemm_epilog_describe(h)
             assert status_of(B.gemm_epilog_plan, h, ep, "col", B.ge_pref(2, 0, 0, 0)) == B.GE_ERR_EPILOG

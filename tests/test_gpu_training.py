@@ -17,7 +17,7 @@ from parity import (check_full, check_sampled, codes, decode_output, make_aux_in
 
 pytestmark = pytest.mark.gpu
 
-TRAIN = ["gelu_aux_bias", "drelu", "dgelu"]
+TRAIN = ["gelu_aux_bias", "drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad"]
 COMBOS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "f32"), ("e4m3", "bf16")]
 
 
@@ -49,8 +49,9 @@ def test_training_epilogues_every_tile(tile, a, d, op_b):
     if a == "e4m3" and tile == 13:
         pytest.skip("the pipelined 64x64 tile takes 16-bit inputs only")
     k = 456 if a == "e4m3" else 200
-    for ep in TRAIN:
-        w = wl(300, 520, k, a, d, ep, "col", op_b, seed=tile)
+    cases = [(ep, "col") for ep in TRAIN] + [("drelu_bgrad", "row"), ("dgelu_bgrad", "row")]
+    for ep, axis in cases:
+        w = wl(300, 520, k, a, d, ep, axis, op_b, seed=tile)
         r = run_library(w, synth.make_inputs(w), pad=2, path=1, tile=tile)
         check_full(w, r)
 
@@ -99,6 +100,41 @@ def test_drelu_integer_bit_exact(tile, a, d):
     Y, _, _ = oracle_full(w, r)
     want = Y.astype(np.float32) if d == "f32" else oracle.encode(Y, d).reshape(Y.shape)
     assert np.array_equal(codes(r.D)[:, :n], want)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("mnk", [(0, 70, 40), (50, 0, 40), (50, 70, 0), (1, 1, 1)])
+def test_bias_gradient_degenerate_shapes(axis, mnk):
+    """An empty sum is zero: m = 0 (col axis) or n = 0 (row axis) still
+    writes the gradient; k = 0 gives D = 0 and a zero gradient."""
+    m, n, k = mnk
+    w = wl(m, n, k, "bf16", "bf16", "dgelu_bgrad", axis, 0, seed=3)
+    ru8 = lambda x: max(8, (x + 7) // 8 * 8)   # 16-byte rows
+    r = run_library(w, synth.make_inputs(w), path=1, lda=ru8(k), ldb=ru8(n), ldd=ru8(n))
+    got = oracle.decode(np.ascontiguousarray(codes(r.bias)), "bf16")
+    if m and n:
+        check_full(w, r)
+    else:
+        assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_dgelu_bgrad_full_size():
+    """bf16 DGELU_BGRAD at 8192^3 in the planner's launch configuration: D
+    sampled (4096 entries + 16 rows) and the bias gradient of 8 columns, each
+    a sum over all 8192 rows, from the oracle's own GEMM of those columns."""
+    w = synth.WORKLOADS["F1d"]
+    inp = synth.make_inputs(w, device="cuda")
+    r = run_library(w, inp, path=0, aux_in=synth.make_aux(w, device="cuda"))
+    assert "tile_id=11" in r.desc, r.desc
+    check_sampled(w, r, seed=w.seed)
+    cols = np.array([0, 1, 255, 256, 4095, 4096, 8190, 8191], dtype=np.int64)
+    Ac = codes(r.A)[:, : w.k]
+    Bsel = np.ascontiguousarray(codes(r.B)[: w.k][:, cols])
+    C = oracle.gemm(np.ascontiguousarray(Ac), "bf16", Bsel, "bf16")
+    Y = oracle.dgelu_pass(C, np.ascontiguousarray(codes(r.aux)[:, cols]), "bf16")
+    want = oracle.bgrad_pass(Y, "col")
+    got = oracle.decode(np.ascontiguousarray(codes(r.bias)[cols]), "bf16")
+    assert rel_fro(got, want) <= tolerance("bf16", "bf16"), (got, want)
 
 
 def test_dgelu_full_size_sampled():
