@@ -26,7 +26,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # Oracle-private codes (independent of the library's enums).
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
 EPILOGS = {"none": 0, "bias": 1, "relu_bias": 2, "relu_aux_bias": 3,
-           "gelu_bias": 4, "gelu_erf": 5, "gelu_aux_bias": 4}   # O5's Y is O3's GELU
+           "gelu_bias": 4, "gelu_erf": 5, "gelu_aux_bias": 4,   # O5's Y is O3's GELU
+           "tanh_bias": 6}
 AXES = {"row": 0, "col": 1}
 _NP_CODE_TYPE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16,
                  "e4m3": np.uint8}

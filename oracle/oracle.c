@@ -44,7 +44,8 @@
 /* ---- codes private to the oracle ---------------------------------------- */
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3 };
 enum { ORC_NONE = 0, ORC_BIAS = 1, ORC_RELU_BIAS = 2, ORC_RELU_AUX_BIAS = 3,
-       ORC_GELU_BIAS = 4, ORC_GELU_ERF = 5 /* report-only erf form */ };
+       ORC_GELU_BIAS = 4, ORC_GELU_ERF = 5 /* report-only erf form */,
+       ORC_TANH_BIAS = 6 };
 enum { ORC_ROW = 0, ORC_COL = 1 };
 
 /* ---- number formats ------------------------------------------------------
@@ -289,13 +290,16 @@ double orc_act1(int epilog, double x)
     case ORC_RELU_AUX_BIAS: return x > 0.0 ? x : 0.0; /* max(x,0); NaN -> 0 */
     case ORC_GELU_BIAS: return gelu_tanh(x);
     case ORC_GELU_ERF: return gelu_erf(x);
+    /* Tanh is among the predefined epilogues the [nvmath page] names
+     * (limitations paragraph: Bias, ReLU, Tanh, ...): Y = tanh(P). */
+    case ORC_TANH_BIAS: return tanh(x);
     }
     return NAN;
 }
 
 int orc_act(int64_t cnt, int epilog, const double* P, double* Y)
 {
-    if (epilog < ORC_NONE || epilog > ORC_GELU_ERF) return -1;
+    if (epilog < ORC_NONE || epilog > ORC_TANH_BIAS) return -1;
     for (int64_t t = 0; t < cnt; ++t) Y[t] = orc_act1(epilog, P[t]);
     return 0;
 }

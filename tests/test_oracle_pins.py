@@ -401,3 +401,39 @@ def test_bgrad_of_drelu_counts_mask_bits():
     bits = np.unpackbits(W.view(np.uint8), axis=1, bitorder="little")[:, :n]
     assert np.array_equal(oracle.bgrad_pass(Y, "row"), bits.sum(axis=1).astype(np.float64))
     assert np.array_equal(oracle.bgrad_pass(Y, "col"), bits.sum(axis=0).astype(np.float64))
+
+
+def test_tanh_epilogue_properties():
+    """O3 for TANH_BIAS: odd, zero at zero, bounded by 1 and saturating,
+    slope 1 at 0, and equal to 2*sigmoid(2x) - 1 (a different closed form)."""
+    xs = np.linspace(-9.0, 9.0, 181)
+    ys = oracle.act_pass(xs, "tanh_bias")
+    assert np.allclose(ys, -oracle.act_pass(-xs, "tanh_bias"), rtol=0, atol=0)
+    assert oracle.act1(0.0, "tanh_bias") == 0.0
+    assert np.all(np.abs(ys) <= 1.0) and abs(ys[-1] - 1.0) < 1e-7
+    h = 1e-6
+    assert abs((oracle.act1(h, "tanh_bias") - oracle.act1(-h, "tanh_bias")) / (2 * h) - 1.0) < 1e-9
+    assert np.allclose(ys, 2.0 / (1.0 + np.exp(-2.0 * xs)) - 1.0, rtol=0, atol=1e-15)
+
+
+def test_tanh_epilogue_after_zero_product_gives_tanh_of_bias():
+    """A = 0: D = tanh(bias) along the bias axis (P3 for the Tanh epilogue)."""
+    m, n, k = 3, 4, 5
+    bias = f32([0.5, -1.0, 2.0])
+    Y, P, _ = oracle.reference(f32(np.zeros((m, k))), "f32", f32(np.ones((k, n))), "f32",
+                               bias, "f32", "tanh_bias", "row")
+    assert np.allclose(Y, np.tanh(np.repeat(bias.astype(np.float64)[:, None], n, axis=1)), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_gemm_scale_factors_any_dtype(dt):
+    """O1's factor sa*sb applies to every input dtype: with small integers the
+    product is exact, so the scaled result is exactly sa*sb times it."""
+    rng = np.random.default_rng(12)
+    A = rng.integers(-4, 5, (6, 9)).astype(np.float32)
+    B = rng.integers(-4, 5, (9, 7)).astype(np.float32)
+    enc = {"f32": lambda x: x, "f16": f16_codes, "bf16": bf16_codes}[dt]
+    C1 = oracle.gemm(np.ascontiguousarray(enc(A)), dt, np.ascontiguousarray(enc(B)), dt)
+    Cs = oracle.gemm(np.ascontiguousarray(enc(A)), dt, np.ascontiguousarray(enc(B)), dt, 0, 0.5, 3.0)
+    assert np.array_equal(C1, A.astype(np.float64) @ B.astype(np.float64))
+    assert np.array_equal(Cs, 1.5 * C1)
