@@ -105,7 +105,8 @@ def _dominant(stats):
     """The fused kernel: the library kernel (ge::ge_*, not the unfused pair's
     elementwise pass or the counter clear) with the most GPU time."""
     cands = [r for r in stats if "ge::ge_" in r["Name"] and "ge_ew_kernel" not in r["Name"]
-             and "ge_clear" not in r["Name"]]
+             and "ge_clear" not in r["Name"] and "ge_bgrad_reduce" not in r["Name"]
+             and "ge_sum_kernel" not in r["Name"]]
     if not cands:
         raise SystemExit("digest: no fused library kernel in the kernel stats")
     return max(cands, key=lambda r: float(r["TotalDurationNs"]))
