@@ -24,7 +24,7 @@ GE_F32, GE_F16, GE_BF16, GE_F8_E4M3 = 0, 1, 2, 3
 GE_OP_N, GE_OP_T = 0, 1
 GE_EPILOG_NONE, GE_EPILOG_BIAS, GE_EPILOG_RELU_BIAS, GE_EPILOG_RELU_AUX_BIAS, \
     GE_EPILOG_GELU_BIAS, GE_EPILOG_GELU_AUX_BIAS, GE_EPILOG_DRELU, GE_EPILOG_DGELU, \
-    GE_EPILOG_DRELU_BGRAD, GE_EPILOG_DGELU_BGRAD = range(10)
+    GE_EPILOG_DRELU_BGRAD, GE_EPILOG_DGELU_BGRAD, GE_EPILOG_TANH_BIAS = range(11)
 GE_BIAS_ROW, GE_BIAS_COL = 0, 1
 
 DTYPE_CODE = {"f32": GE_F32, "f16": GE_F16, "bf16": GE_BF16, "e4m3": GE_F8_E4M3,
@@ -34,7 +34,7 @@ EPILOG_CODE = {"none": GE_EPILOG_NONE, "bias": GE_EPILOG_BIAS, "relu_bias": GE_E
                "relu_aux_bias": GE_EPILOG_RELU_AUX_BIAS, "gelu_bias": GE_EPILOG_GELU_BIAS,
                "gelu_aux_bias": GE_EPILOG_GELU_AUX_BIAS, "drelu": GE_EPILOG_DRELU,
                "dgelu": GE_EPILOG_DGELU, "drelu_bgrad": GE_EPILOG_DRELU_BGRAD,
-               "dgelu_bgrad": GE_EPILOG_DGELU_BGRAD}
+               "dgelu_bgrad": GE_EPILOG_DGELU_BGRAD, "tanh_bias": GE_EPILOG_TANH_BIAS}
 AXIS_CODE = {"row": GE_BIAS_ROW, "col": GE_BIAS_COL}
 TORCH_DTYPE = {GE_F32: torch.float32, GE_F16: torch.float16, GE_BF16: torch.bfloat16,
                GE_F8_E4M3: torch.float8_e4m3fn}

@@ -61,7 +61,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Epilogues that add a bias (DRELU and DGELU read none).
 bool has_bias(int e) {
     return e == GE_EPILOG_BIAS || e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_RELU_AUX_BIAS ||
-           e == GE_EPILOG_GELU_BIAS || e == GE_EPILOG_GELU_AUX_BIAS;
+           e == GE_EPILOG_GELU_BIAS || e == GE_EPILOG_GELU_AUX_BIAS || e == GE_EPILOG_TANH_BIAS;
 }
 // Epilogues with an aux buffer: a bit mask (written by RELU_AUX_BIAS, read by
 // DRELU) or a pre-activation matrix in D's dtype (written by GELU_AUX_BIAS,
@@ -178,7 +178,7 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
 
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* pref) {
     if (!h) return GE_ERR_NULL;
-    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_DGELU_BGRAD) return GE_ERR_EPILOG;
+    if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_TANH_BIAS) return GE_ERR_EPILOG;
     if (bias_axis != GE_BIAS_ROW && bias_axis != GE_BIAS_COL) return GE_ERR_EPILOG;
     ge_pref pr = {0, 0, 0, 0};
     if (pref) pr = *pref;
@@ -200,7 +200,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     if (q.ldaux > INT32_MAX) return GE_ERR_SHAPE;
 
     // the small-m kernel serves the inference epilogues only
-    const bool smallm_epilog = epilog <= GE_EPILOG_GELU_BIAS;
+    const bool smallm_epilog = epilog <= GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_TANH_BIAS;
     int path = pr.path;
     if (path == 0) path = (smallm_supported(d) && smallm_epilog) ? PATH_SMALLM : PATH_TILE;
     if (path == PATH_SMALLM && !smallm_supported(d)) return GE_ERR_SHAPE;
@@ -283,7 +283,6 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     const bool want_aux = has_aux(h->epilog) && d.m > 0 && d.n > 0;   // else aux holds nothing
     if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
-    if (d.a_type != GE_F8_E4M3 && (scale_a || scale_b)) return GE_ERR_DTYPE;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||
         !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
         return GE_ERR_ALIGN;

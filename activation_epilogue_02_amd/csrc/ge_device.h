@@ -187,7 +187,7 @@ __device__ __forceinline__ float gelu_tanh_deriv(float x) {
 // Epilogues that add a bias to the product (DRELU and DGELU take none).
 __host__ __device__ __forceinline__ bool epilog_has_bias(int epilog) {
     return epilog == GE_EPILOG_BIAS || epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS ||
-           epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS;
+           epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS || epilog == GE_EPILOG_TANH_BIAS;
 }
 
 // Backward epilogues (the product scaled by an activation derivative read
@@ -209,6 +209,7 @@ __host__ __device__ __forceinline__ bool epilog_reads_mask(int epilog) {
 __device__ __forceinline__ float activate(int epilog, float x) {
     if (epilog == GE_EPILOG_RELU_BIAS || epilog == GE_EPILOG_RELU_AUX_BIAS) return x > 0.0f ? x : 0.0f;
     if (epilog == GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_GELU_AUX_BIAS) return gelu_tanh(x);
+    if (epilog == GE_EPILOG_TANH_BIAS) return tanhf(x);   // the device library's tanh: once per output
     return x;
 }
 

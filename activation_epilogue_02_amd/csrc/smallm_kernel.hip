@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
     // that their latency hides under the W stream instead of adding to the
     // end of the kernel
     const int ep = p.epilog;
-    const bool has_bias = ep != GE_EPILOG_NONE;
+    const bool has_bias = epilog_has_bias(ep);
     float bpre[4] = {0.f, 0.f, 0.f, 0.f};
     if (wave == 0 && has_bias) {
 #pragma unroll
@@ -183,6 +183,9 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
     }
 
     const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+    float s = 1.0f;   // the product's scale (alpha)
+    if (p.scale_a) s *= *p.scale_a;
+    if (p.scale_b) s *= *p.scale_b;
     const int m = r;
     const bool mok = m < M;
     float v[4];
@@ -190,7 +193,7 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = n0 + 4 * q + i;
-        const float x = sum[i] + bpre[i];
+        const float x = sum[i] * s + bpre[i];
         if (want_aux && x > 0.0f && n < N) bits |= 1u << (4 * q + i);
         v[i] = activate(ep, x);
     }

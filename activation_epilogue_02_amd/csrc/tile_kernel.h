@@ -322,11 +322,10 @@ ge_tile_kernel(KernelArgs p) {
     }
 
     // ---- fused epilogue on the accumulators ----
+    // the product's scale: fp8 dequantisation factors, or an alpha for any dtype
     float s = 1.0f;
-    if constexpr (DIN == GE_F8_E4M3) {
-        if (p.scale_a) s *= *p.scale_a;
-        if (p.scale_b) s *= *p.scale_b;
-    }
+    if (p.scale_a) s *= *p.scale_a;
+    if (p.scale_b) s *= *p.scale_b;
     const int ep = p.epilog;
     const bool has_bias = epilog_has_bias(ep);
     const bool row_bias = p.axis == GE_BIAS_ROW;

@@ -84,12 +84,15 @@ typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op;
  * (BIAS, RELU_BIAS, RELU_AUX_BIAS), plus NONE and GELU_BIAS (GELU is named
  * as a fused activation on the cuBLASLt page, paragraph 2, and in the NVGEMM
  * page's section on why epilogue fusion matters).  With C = s*A*B the scaled
- * product and P the pre-activation (C plus bias):
+ * product (s = scale_a * scale_b, see execute) and P the pre-activation (C
+ * plus bias):
  *   NONE           D = C                            (no bias read)
  *   BIAS           D = P
  *   RELU_BIAS      D = max(P, 0)
  *   RELU_AUX_BIAS  D = max(P, 0), and aux bit (i,j) = (P[i][j] > 0)
  *   GELU_BIAS      D = GELU(P) = 0.5 P (1 + tanh(sqrt(2/pi) (P + 0.044715 P^3)))
+ *   TANH_BIAS      D = tanh(P)  (Tanh is among the predefined epilogues the
+ *                  nvmath page lists in its paragraph on limitations)
  * The training-side epilogues serve the backward pass, which needs what the
  * forward activation saw (nvmath page, paragraph on limitations: RELU_AUX_BIAS
  * produces the mask backward needs; its closing paragraph names GELU and the
@@ -119,7 +122,8 @@ typedef enum {
     GE_EPILOG_DRELU = 6,
     GE_EPILOG_DGELU = 7,
     GE_EPILOG_DRELU_BGRAD = 8,
-    GE_EPILOG_DGELU_BGRAD = 9
+    GE_EPILOG_DGELU_BGRAD = 9,
+    GE_EPILOG_TANH_BIAS = 10
 } ge_epilog;
 
 /* Bias broadcast axis.
@@ -183,8 +187,8 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
 /* Choose the epilogue and bias axis and plan the launch (kernel, tile, grid,
  * workspace).  p may be NULL.  May be called again to re-plan.  The bias
  * axis is validated for every epilogue but only used by those with a bias.
- * The small-m kernel serves the inference epilogues (NONE .. GELU_BIAS); the
- * automatic path takes the tile kernel for the others.
+ * The small-m kernel serves the inference epilogues (NONE .. GELU_BIAS and
+ * TANH_BIAS); the automatic path takes the tile kernel for the others.
  * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis, or the
  * small-m path forced with a training-side epilogue), GE_ERR_SHAPE (an
  * unknown tile id or split in p). */
@@ -221,9 +225,10 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits);
  *            RELU_AUX_BIAS and GELU_AUX_BIAS (written) and for the backward
  *            epilogues (read), must be NULL otherwise
  *   scale_a, scale_b
- *            device pointers to one fp32 each, the per-tensor dequantisation
- *            factors of fp8 inputs (D uses scale_a*scale_b*A*B); NULL means
- *            1.0.  Must be NULL for non-fp8 inputs.
+ *            device pointers to one fp32 each; the product is scaled by
+ *            s = scale_a * scale_b before the bias (D uses s*A*B): the
+ *            per-tensor dequantisation factors of fp8 inputs, or an arbitrary
+ *            alpha for any input dtype.  NULL means 1.0.
  *   workspace, workspace_bytes
  *            device scratch of at least gemm_epilog_workspace_size bytes
  *            (may be NULL/0 when that size is 0)
@@ -231,8 +236,8 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits);
  * when k == 0).  Every non-NULL pointer must be 16-byte aligned (scales:
  * 4-byte).  The
  * output and aux buffers must not overlap the inputs.
- * Errors: GE_ERR_NULL, GE_ERR_STATE, GE_ERR_EPILOG, GE_ERR_DTYPE (scales
- * given for non-fp8 inputs), GE_ERR_ALIGN, GE_ERR_WORKSPACE, GE_ERR_HIP. */
+ * Errors: GE_ERR_NULL, GE_ERR_STATE, GE_ERR_EPILOG, GE_ERR_ALIGN,
+ * GE_ERR_WORKSPACE, GE_ERR_HIP. */
 int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* bias,
                         void* D, void* aux, const float* scale_a, const float* scale_b,
                         void* workspace, size_t workspace_bytes, void* stream);

@@ -99,7 +99,7 @@ def test_plan_validation_and_state():
     try:
         assert status_of(B.gemm_epilog_workspace_size, h) == B.GE_ERR_STATE
         assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATE
-        assert status_of(B.gemm_epilog_plan, h, 10, 0) == B.GE_ERR_EPILOG
+        assert status_of(B.gemm_epilog_plan, h, 11, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, -1, 0) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 2) == B.GE_ERR_EPILOG
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(0, 0, 99, 0)) == B.GE_ERR_SHAPE
@@ -126,7 +126,7 @@ def test_execute_validation_paths():
         assert ex(FAKE, FAKE, FAKE, None, FAKE) == B.GE_ERR_NULL
         assert ex(FAKE, FAKE, None, FAKE, FAKE) == B.GE_ERR_NULL            # bias required
         assert ex(FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_EPILOG          # aux required
-        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_DTYPE  # scale on bf16
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, None) == B.GE_ERR_ALIGN  # alpha pointer
         assert ex(FAKE + 2, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_ALIGN
         assert ex(FAKE, FAKE + 8, FAKE, FAKE, FAKE) == B.GE_ERR_ALIGN
         assert ex(FAKE, FAKE, FAKE + 4, FAKE, FAKE) == B.GE_ERR_ALIGN

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 COMBOS = [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
           ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
-EPILOGS = ["none", "bias", "relu_bias", "relu_aux_bias", "gelu_bias"]
+EPILOGS = ["none", "bias", "relu_bias", "relu_aux_bias", "gelu_bias", "tanh_bias"]
 
 
 def wl(m, n, k, a, d, ep, axis="row", op_b=0, seed=7, **kw):
@@ -146,7 +146,7 @@ def test_empty_output_is_noop():
 @pytest.mark.parametrize("a,d", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
 @pytest.mark.parametrize("split", [0, 3])
 def test_smallm_path(m, n, k, a, d, split):
-    for ep in ("gelu_bias", "relu_aux_bias"):
+    for ep in ("gelu_bias", "relu_aux_bias", "tanh_bias"):
         for axis in ("col", "row"):
             w = wl(m, n, k, a, d, ep, axis, op_b=1, seed=m * 1000 + n)
             r = run_library(w, synth.make_inputs(w), pad=1, path=2, split_k=split)
