@@ -1,0 +1,10 @@
+// tile2_f8_f16.hip -- instantiations of the pipelined tile kernel for
+// fp8 (OCP E4M3) inputs and fp16 output (one translation unit per dtype pair, so
+// that they compile in parallel).
+#include "tile2_kernel.h"
+
+namespace ge {
+
+TileFn pick_tile2_f8_f16(int op_b, int tile_id) { return pick_op2<GE_F8_E4M3, GE_F16>(op_b, tile_id); }
+
+}  // namespace ge

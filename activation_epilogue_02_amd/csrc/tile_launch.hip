@@ -11,9 +11,13 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
     if (!t) return (int)hipErrorInvalidDeviceFunction;
     TileFn fn = nullptr;
     if (t->kernel >= 2) {
-        if (a_type == GE_F16) fn = pick_tile2_f16(d_type, op_b, tile_id);
-        else if (a_type == GE_BF16) fn = pick_tile2_bf16(d_type, op_b, tile_id);
-        else if (a_type == GE_F8_E4M3) fn = pick_tile2_f8(d_type, op_b, tile_id);
+        if (a_type == GE_F16 && d_type == GE_F16) fn = pick_tile2_f16_f16(op_b, tile_id);
+        else if (a_type == GE_F16 && d_type == GE_F32) fn = pick_tile2_f16_f32(op_b, tile_id);
+        else if (a_type == GE_BF16 && d_type == GE_BF16) fn = pick_tile2_bf16_bf16(op_b, tile_id);
+        else if (a_type == GE_BF16 && d_type == GE_F32) fn = pick_tile2_bf16_f32(op_b, tile_id);
+        else if (a_type == GE_F8_E4M3 && d_type == GE_BF16) fn = pick_tile2_f8_bf16(op_b, tile_id);
+        else if (a_type == GE_F8_E4M3 && d_type == GE_F16) fn = pick_tile2_f8_f16(op_b, tile_id);
+        else if (a_type == GE_F8_E4M3 && d_type == GE_F32) fn = pick_tile2_f8_f32(op_b, tile_id);
     } else {
         switch (a_type) {
         case GE_F32: fn = pick_tile_f32(d_type, op_b, tile_id); break;
