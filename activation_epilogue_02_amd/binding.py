@@ -81,9 +81,11 @@ def lib():
         L.gemm_epilog_status_string.argtypes = [ctypes.c_int]
         L.gemm_epilog_status_string.restype = ctypes.c_char_p
         L.gemm_epilog_describe.argtypes = [vp, ctypes.c_char_p, sz]
+        L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp,
+                                           ctypes.POINTER(ctypes.c_float)]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
-                  "gemm_epilog_describe"):
+                  "gemm_epilog_describe", "gemm_epilog_autotune"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -161,6 +163,20 @@ def gemm_epilog_free(h: Optional[int]) -> None:
 
 def gemm_epilog_status_string(status: int) -> str:
     return lib().gemm_epilog_status_string(status).decode()
+
+
+def gemm_epilog_autotune(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,
+                         workspace=None, workspace_bytes=None, iters: int = 5, stream=None) -> float:
+    """Time the candidate kernels on these buffers and keep the fastest in the
+    plan; returns its mean milliseconds per call."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    best = ctypes.c_float(0.0)
+    _check(lib().gemm_epilog_autotune(h, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux),
+                                      _ptr(scale_a), _ptr(scale_b), _ptr(workspace), workspace_bytes,
+                                      iters, stream, ctypes.byref(best)),
+           "gemm_epilog_autotune")
+    return best.value
 
 
 def gemm_epilog_describe(h: int) -> str:

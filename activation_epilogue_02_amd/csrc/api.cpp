@@ -30,6 +30,7 @@ struct ge_plan_s {
     size_t ws_counters = 0;  // split-K counter bytes
     size_t ws_bgrad = 0;     // bias-gradient partial bytes
     int32_t bgrad_parts = 0; // bias-gradient partials per entry
+    ge_pref pref = {0, 0, 0, 0};   // the preferences the plan was made with
     int64_t ldaux = 0;       // mask row stride, 32-bit words
 };
 
@@ -252,6 +253,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.ws_bgrad = round_up((size_t)parts * (size_t)(col ? d.n : d.m) * sizeof(float), 256);
     }
     q.planned = true;
+    q.pref = pr;
     *h = q;
     return GE_OK;
 }
@@ -381,6 +383,79 @@ const char* gemm_epilog_status_string(int s) {
     case GE_ERR_ALLOC: return "GE_ERR_ALLOC: host allocation failed";
     }
     return "unknown status";
+}
+
+int gemm_epilog_autotune(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                         const float* scale_a, const float* scale_b, void* workspace, size_t workspace_bytes,
+                         int32_t iters, void* stream, float* best_ms) {
+    if (!h) return GE_ERR_NULL;
+    if (!h->planned) return GE_ERR_STATE;
+    if (iters < 1) return GE_ERR_SHAPE;
+    const ge_plan_s orig = *h;
+    // candidates: tile ids (tile path) or K splits (small-m path)
+    int cand[kNumTiles + 8];
+    int nc = 0;
+    if (orig.path == PATH_SMALLM) {
+        const int64_t steps = ceil_div(orig.d.k, 32);
+        for (int s = 1; s <= 64 && s <= (steps > 0 ? steps : 1); s *= 2) cand[nc++] = s;
+    } else {
+        for (int i = 0; i < kNumTiles; ++i) cand[nc++] = kTiles[i].id;
+    }
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return GE_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return GE_ERR_HIP;
+    }
+    ge_plan_s best = orig;
+    float best_t = -1.0f;
+    int status = GE_OK;
+    for (int c = 0; c < nc && status == GE_OK; ++c) {
+        ge_pref pr = orig.pref;
+        if (orig.path == PATH_SMALLM) {
+            pr.path = PATH_SMALLM;
+            pr.split_k = cand[c];
+        } else {
+            pr.path = PATH_TILE;
+            pr.tile = cand[c];
+        }
+        ge_plan_s trial = orig;
+        if (gemm_epilog_plan(&trial, orig.epilog, orig.axis, &pr) != GE_OK) continue;   // not for this dtype
+        size_t need = 0;
+        gemm_epilog_workspace_size(&trial, &need);
+        if (need > workspace_bytes) continue;
+        // one untimed call (also validates the arguments), then the timed ones
+        int r = gemm_epilog_execute(&trial, A, B, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
+                                    stream);
+        if (r != GE_OK) {
+            status = r;
+            break;
+        }
+        if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) { status = GE_ERR_HIP; break; }
+        for (int i = 0; i < iters && r == GE_OK; ++i)
+            r = gemm_epilog_execute(&trial, A, B, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
+                                    stream);
+        if (r != GE_OK) { status = r; break; }
+        float ms = 0.0f;
+        if (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            status = GE_ERR_HIP;
+            break;
+        }
+        ms /= (float)iters;
+        if (best_t < 0.0f || ms < best_t) {
+            best_t = ms;
+            best = trial;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (status != GE_OK) return status;
+    if (best_t < 0.0f) return GE_ERR_WORKSPACE;   // no candidate fits the workspace
+    best.pref = orig.pref;
+    *h = best;
+    if (best_ms) *best_ms = best_t;
+    return GE_OK;
 }
 
 int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {

@@ -252,6 +252,27 @@ const char* gemm_epilog_status_string(int status);
  * into buf (always NUL-terminated when cap > 0).  Errors: GE_ERR_NULL. */
 int gemm_epilog_describe(ge_handle h, char* buf, size_t cap);
 
+/* Autotune a planned handle on the caller's buffers (the cuBLASLt page's
+ * paragraph on limitations and the nvmath page's paragraph on timing both
+ * suggest letting the library try its kernels when the default choice is not
+ * fast enough).  Every candidate the plan's path and input dtype allow -- the
+ * tile ids of the tile path, or the K splits 1, 2, 4, ... of the small-m
+ * path -- is re-planned with the same epilogue, bias axis and unfused
+ * choice, run once, then `iters` times between two HIP events on `stream`;
+ * the fastest replaces the plan (the shape heuristic's own choice is among
+ * the candidates, so the result is never slower than it as measured).
+ * Candidates whose workspace would exceed workspace_bytes are skipped.
+ * Arguments as for execute, which this calls: it overwrites D, aux (and, for
+ * the bias-gradient epilogues, bias) like execute does.  Unlike execute it
+ * synchronises `stream` and creates and destroys two HIP events; nothing is
+ * allocated on the device.  *best_ms (may be NULL) receives the winner's mean
+ * time per call.  Errors: those of execute, GE_ERR_SHAPE (iters < 1), and
+ * GE_ERR_HIP if event creation or timing fails (the plan is then unchanged). */
+int gemm_epilog_autotune(ge_handle h, const void* A, const void* B, const void* bias,
+                         void* D, void* aux, const float* scale_a, const float* scale_b,
+                         void* workspace, size_t workspace_bytes, int32_t iters, void* stream,
+                         float* best_ms);
+
 #ifdef __cplusplus
 }
 #endif

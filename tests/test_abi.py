@@ -211,6 +211,20 @@ def test_training_epilogues_take_the_tile_path():
         B.gemm_epilog_free(h)
 
 
+def test_autotune_prechecks():
+    """Checks that fail before anything runs: no handle, no plan, iters < 1."""
+    L = B.lib()
+    assert L.gemm_epilog_autotune(None, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, 5, None,
+                                  None) == B.GE_ERR_NULL
+    h = B.gemm_epilog_create(desc())
+    try:
+        assert status_of(B.gemm_epilog_autotune, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATE
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert status_of(B.gemm_epilog_autotune, h, FAKE, FAKE, FAKE, FAKE, iters=0) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_fp8_scales_alignment():
     h = B.gemm_epilog_create(desc(a_type="e4m3", d_type="bf16", k=48))
     try:
