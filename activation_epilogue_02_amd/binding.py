@@ -45,7 +45,7 @@ class ge_desc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32),
                 ("d_type", ctypes.c_int32), ("bias_type", ctypes.c_int32),
-                ("op_b", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("op_b", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldd", ctypes.c_int64)]
 
 
@@ -105,12 +105,12 @@ def _ptr(x) -> Optional[int]:
 
 
 def make_desc(m, n, k, a_type, d_type, op_b=GE_OP_N, lda=None, ldb=None, ldd=None,
-              b_type=None, bias_type=None) -> ge_desc:
+              b_type=None, bias_type=None, batch=0) -> ge_desc:
     a = DTYPE_CODE[a_type] if not isinstance(a_type, int) else a_type
     d = DTYPE_CODE[d_type] if not isinstance(d_type, int) else d_type
     b = a if b_type is None else (DTYPE_CODE[b_type] if not isinstance(b_type, int) else b_type)
     bt = d if bias_type is None else (DTYPE_CODE[bias_type] if not isinstance(bias_type, int) else bias_type)
-    return ge_desc(m, n, k, a, b, d, bt, op_b, 0,
+    return ge_desc(m, n, k, a, b, d, bt, op_b, batch,
                    k if lda is None else lda,
                    (n if op_b == GE_OP_N else k) if ldb is None else ldb,
                    n if ldd is None else ldd)
@@ -193,8 +193,8 @@ class GemmEpilog:
     bias holds m (axis 'row') or n (axis 'col') values of D's dtype.
     """
 
-    def __init__(self, m, n, k, a_dtype, d_dtype, op_b=GE_OP_N, lda=None, ldb=None, ldd=None):
-        self.desc = make_desc(m, n, k, a_dtype, d_dtype, op_b, lda, ldb, ldd)
+    def __init__(self, m, n, k, a_dtype, d_dtype, op_b=GE_OP_N, lda=None, ldb=None, ldd=None, batch=0):
+        self.desc = make_desc(m, n, k, a_dtype, d_dtype, op_b, lda, ldb, ldd, batch=batch)
         self.h = gemm_epilog_create(self.desc)
         self.epilog = None
 

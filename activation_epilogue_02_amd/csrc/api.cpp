@@ -162,7 +162,7 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
     const ge_desc& d = *desc;
     if (d.m < 0 || d.n < 0 || d.k < 0) return GE_ERR_SHAPE;
     if (d.m > INT32_MAX || d.n > INT32_MAX || d.k > INT32_MAX) return GE_ERR_SHAPE;
-    if (d.reserved != 0 || (d.op_b != GE_OP_N && d.op_b != GE_OP_T)) return GE_ERR_SHAPE;
+    if (d.batch < 0 || d.batch > 65535 || (d.op_b != GE_OP_N && d.op_b != GE_OP_T)) return GE_ERR_SHAPE;
     if (!dtype_combo_ok(d.a_type, d.b_type, d.d_type)) return GE_ERR_DTYPE;
     if (d.bias_type != d.d_type) return GE_ERR_DTYPE;
     if (d.lda < d.k || d.ldd < d.n) return GE_ERR_SHAPE;
@@ -224,8 +224,9 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         if (grid > INT32_MAX) return GE_ERR_SHAPE;
         q.grid = (unsigned)grid;
         if (split > 1) {
-            q.ws_partial = round_up((size_t)split * q.tiles_n * 256 * sizeof(float), 256);
-            q.ws_counters = round_up((size_t)q.tiles_n * sizeof(uint32_t), 256);
+            const size_t nbs = d.batch > 1 ? (size_t)d.batch : 1;
+            q.ws_partial = round_up(nbs * (size_t)split * q.tiles_n * 256 * sizeof(float), 256);
+            q.ws_counters = round_up(nbs * (size_t)q.tiles_n * sizeof(uint32_t), 256);
         }
     } else {
         if (pr.split_k > 1) return GE_ERR_SHAPE;
@@ -240,7 +241,8 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.grid = (unsigned)(tm * tn);
         q.k_per_split = (int32_t)d.k;
     }
-    q.ws_c = q.unfused ? round_up((size_t)d.m * (size_t)d.ldd * elem_size(d.d_type), 256) : 0;
+    const size_t nb = d.batch > 1 ? (size_t)d.batch : 1;   // products per launch
+    q.ws_c = q.unfused ? round_up(nb * (size_t)d.m * (size_t)d.ldd * elem_size(d.d_type), 256) : 0;
     // bias gradient: one fp32 partial per tile row (COL) or column (ROW) and
     // gradient entry; the unfused pair sums its stored D in blocks of 256
     q.ws_bgrad = 0;
@@ -250,7 +252,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         const int64_t parts = q.unfused ? ceil_div(col ? d.m : d.n, 256) : (col ? q.tiles_m : q.tiles_n);
         if (parts > 65535) return GE_ERR_SHAPE;
         q.bgrad_parts = (int32_t)parts;
-        q.ws_bgrad = round_up((size_t)parts * (size_t)(col ? d.n : d.m) * sizeof(float), 256);
+        q.ws_bgrad = round_up(nb * (size_t)parts * (size_t)(col ? d.n : d.m) * sizeof(float), 256);
     }
     q.planned = true;
     q.pref = pr;
@@ -300,6 +302,8 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
             z.m = (int32_t)d.m;
             z.n = (int32_t)d.n;
             z.axis = h->axis;
+            z.batch = d.batch > 1 ? d.batch : 1;
+            z.bs_bias = bias_len * elem_size(d.d_type);
             if (launch_bgrad_reduce(d.d_type, z, 0, stream) != 0) return GE_ERR_HIP;
         }
         return GE_OK;
@@ -328,11 +332,22 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     a.group_m = h->group_m;
     a.split_k = h->split_k;
     a.k_per_split = h->k_per_split;
+    // batched: the packed per-product strides, in bytes (counters: elements)
+    const int64_t len = h->axis == GE_BIAS_COL ? d.n : d.m;
+    a.batch = d.batch > 1 ? d.batch : 1;
+    a.bs_a = d.m * d.lda * elem_size(d.a_type);
+    a.bs_b = (d.op_b == GE_OP_N ? d.k : d.n) * d.ldb * elem_size(d.b_type);
+    a.bs_d = d.m * d.ldd * elem_size(d.d_type);
+    a.bs_bias = len * elem_size(d.d_type);
+    a.bs_aux = d.m * h->ldaux * (aux_is_matrix(h->epilog) ? elem_size(d.d_type) : 4);
+    a.bs_part = h->path == PATH_SMALLM ? (int64_t)h->split_k * h->tiles_n * 256 * (int64_t)sizeof(float)
+                                       : (int64_t)h->bgrad_parts * len * (int64_t)sizeof(float);
+    a.bs_cnt = h->tiles_n;
     uint8_t* ws = (uint8_t*)workspace;
     if (h->split_k > 1) {
         a.partial = (float*)(ws + h->ws_c);
         a.counters = (uint32_t*)(ws + h->ws_c + h->ws_partial);
-        if (launch_clear_counters(a.counters, h->tiles_n, stream) != 0) return GE_ERR_HIP;
+        if (launch_clear_counters(a.counters, h->tiles_n * a.batch, stream) != 0) return GE_ERR_HIP;
     }
 
     if (is_bgrad(h->epilog)) a.partial = (float*)(ws + h->ws_c + h->ws_partial + h->ws_counters);

@@ -19,7 +19,10 @@ __host__ __device__ inline int ew_items_per_row(const KernelArgs& p) {
 }
 
 template <int DT>
-__global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p, const void* c) {
+__global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p_all, const void* c_all) {
+    // this product of a batch; its intermediate C sits at D's per-product offset
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);
+    const void* c = (const uint8_t*)c_all + (int64_t)blockIdx.y * p_all.bs_d;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int words = ew_items_per_row(p);
     const int64_t row = t / words;
@@ -79,13 +82,13 @@ int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* 
     const unsigned grid = (unsigned)((items + 255) / 256);
     switch (d_type) {
     case GE_F32:
-        hipLaunchKernelGGL(ge_ew_kernel<GE_F32>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        hipLaunchKernelGGL(ge_ew_kernel<GE_F32>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, c);
         break;
     case GE_F16:
-        hipLaunchKernelGGL(ge_ew_kernel<GE_F16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        hipLaunchKernelGGL(ge_ew_kernel<GE_F16>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, c);
         break;
     case GE_BF16:
-        hipLaunchKernelGGL(ge_ew_kernel<GE_BF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, c);
+        hipLaunchKernelGGL(ge_ew_kernel<GE_BF16>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, c);
         break;
     default:
         return (int)hipErrorInvalidDeviceFunction;
@@ -97,7 +100,8 @@ int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* 
 // Unfused pair: sums of the stored D along the bias-gradient axis over blocks
 // of 256 rows (COL: partial[rb * n + j]) or 256 columns (ROW: partial[cb * m + i]).
 template <int DT>
-__global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p) {
+__global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p_all) {
+    const KernelArgs p = batch_slice(p_all, blockIdx.z);   // this product of a batch
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int blk = blockIdx.y;
     if (p.axis == GE_BIAS_COL) {
@@ -119,7 +123,8 @@ __global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p) {
 // order, converted to D's dtype and written to the bias pointer (the
 // gradient's output).  parts = 0 writes zeros (an empty sum).
 template <int DT>
-__global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p, int parts) {
+__global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p_all, int parts) {
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
     const int len = p.axis == GE_BIAS_COL ? p.n : p.m;
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= len) return;
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p, int parts) 
 int launch_bgrad_sum(int d_type, const KernelArgs& args, int parts, void* stream) {
     const int len = args.axis == GE_BIAS_COL ? args.n : args.m;
     if (len <= 0 || parts <= 0) return 0;
-    const dim3 grid((unsigned)((len + 255) / 256), (unsigned)parts);
+    const dim3 grid((unsigned)((len + 255) / 256), (unsigned)parts, (unsigned)args.batch);
     switch (d_type) {
     case GE_F32: hipLaunchKernelGGL(ge_sum_kernel<GE_F32>, grid, dim3(256), 0, (hipStream_t)stream, args); break;
     case GE_F16: hipLaunchKernelGGL(ge_sum_kernel<GE_F16>, grid, dim3(256), 0, (hipStream_t)stream, args); break;
@@ -147,13 +152,13 @@ int launch_bgrad_reduce(int d_type, const KernelArgs& args, int parts, void* str
     const unsigned grid = (unsigned)((len + 255) / 256);
     switch (d_type) {
     case GE_F32:
-        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F32>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F32>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, parts);
         break;
     case GE_F16:
-        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_F16>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, parts);
         break;
     case GE_BF16:
-        hipLaunchKernelGGL(ge_bgrad_reduce<GE_BF16>, dim3(grid), dim3(256), 0, (hipStream_t)stream, args, parts);
+        hipLaunchKernelGGL(ge_bgrad_reduce<GE_BF16>, dim3(grid, args.batch), dim3(256), 0, (hipStream_t)stream, args, parts);
         break;
     default:
         return (int)hipErrorInvalidDeviceFunction;

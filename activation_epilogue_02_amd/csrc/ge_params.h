@@ -29,7 +29,25 @@ struct KernelArgs {
     int32_t group_m;       // tile-rows per group in the launch order
     int32_t split_k;       // K slices (small-m path)
     int32_t k_per_split;   // K elements per slice, multiple of the k step
+    // batched launches: products 1 .. batch-1 read and write at these byte
+    // offsets per product (counters: elements); the product's index comes
+    // from the launch grid (see batch_slice)
+    int32_t batch;
+    int64_t bs_a, bs_b, bs_d, bs_bias, bs_aux, bs_part, bs_cnt;
 };
+
+// The arguments of product z of a batched launch.
+__host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z) {
+    KernelArgs q = p;
+    q.A = p.A ? (const void*)((const uint8_t*)p.A + z * p.bs_a) : nullptr;
+    q.B = p.B ? (const void*)((const uint8_t*)p.B + z * p.bs_b) : nullptr;
+    q.bias = p.bias ? (const void*)((const uint8_t*)p.bias + z * p.bs_bias) : nullptr;
+    q.D = p.D ? (void*)((uint8_t*)p.D + z * p.bs_d) : nullptr;
+    q.aux = p.aux ? (uint32_t*)((uint8_t*)p.aux + z * p.bs_aux) : nullptr;
+    q.partial = p.partial ? (float*)((uint8_t*)p.partial + z * p.bs_part) : nullptr;
+    q.counters = p.counters ? p.counters + z * p.bs_cnt : nullptr;
+    return q;
+}
 
 // Kernel families.
 enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };

@@ -58,7 +58,8 @@ __device__ __forceinline__ u32x4 sm_load_masked(const uint16_t* row, int col, in
 }
 
 template <int DIN, int DOUT>
-__global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p) {
+__global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_all) {
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
     __shared__ f32x4 red[kSmWaves][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -257,7 +258,7 @@ int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsi
     else if (a_type == GE_BF16 && d_type == GE_BF16) fn = ge_smallm_kernel<GE_BF16, GE_BF16>;
     else if (a_type == GE_BF16 && d_type == GE_F32) fn = ge_smallm_kernel<GE_BF16, GE_F32>;
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSmWaves * 64), 0, (hipStream_t)stream, args);
+    hipLaunchKernelGGL(fn, dim3(grid, args.batch), dim3(kSmWaves * 64), 0, (hipStream_t)stream, args);
     return (int)hipGetLastError();
 }
 

@@ -127,7 +127,8 @@ __device__ __forceinline__ int swz_row(int row) {
 
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB>
 __global__ void __launch_bounds__(WM* WN * 64)
-ge_tile2_kernel(KernelArgs p) {
+ge_tile2_kernel(KernelArgs p_all) {
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
     using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB>;
     constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
     using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;

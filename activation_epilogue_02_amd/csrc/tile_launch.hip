@@ -28,7 +28,7 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
     }
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     const int threads = t->wm * t->wn * 64;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, (hipStream_t)stream, args);
+    hipLaunchKernelGGL(fn, dim3(grid, args.batch), dim3(threads), 0, (hipStream_t)stream, args);
     return (int)hipGetLastError();
 }
 

@@ -139,12 +139,19 @@ typedef enum { GE_BIAS_ROW = 0, GE_BIAS_COL = 1 } ge_bias_axis;
  *   BF16 inputs -> d_type BF16 or F32
  *   E4M3 inputs -> d_type BF16, F16 or F32
  * bias_type must equal d_type (for every epilogue): there is no implicit
- * conversion (nvmath page, paragraph on dtype agreement). */
+ * conversion (nvmath page, paragraph on dtype agreement).
+ * batch: 0 or 1 for one product; B > 1 (at most 65535) for B independent
+ * products of the same shape and epilogue in one launch, their buffers
+ * packed back to back: product b reads A + b*m*lda, B + b*k*ldb (N) or
+ * b*n*ldb (T), the bias (or writes the bias gradient) at b*len (len = m for
+ * ROW, n for COL), writes D + b*m*ldd and aux + b*m*(aux_ld_bits/8) bytes
+ * (all offsets in elements of the buffer's dtype unless stated).  The fp8
+ * scales are shared.  The workspace scales with B. */
 typedef struct {
     int64_t m, n, k;
     int32_t a_type, b_type, d_type, bias_type; /* ge_dtype */
     int32_t op_b;                              /* ge_op (op_a is always N) */
-    int32_t reserved;                          /* must be 0 */
+    int32_t batch;                             /* independent products, 0 = 1 */
     int64_t lda, ldb, ldd;                     /* in elements */
 } ge_desc;
 

@@ -225,6 +225,29 @@ def test_autotune_prechecks():
         B.gemm_epilog_free(h)
 
 
+def test_batch_validation_and_workspace():
+    """batch 0 or 1 is one product; up to 65535 products; the workspace of
+    the unfused pair and of the small-m split scales with the batch."""
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 40, "bf16", "bf16", batch=-1)) == B.GE_ERR_SHAPE
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 40, "bf16", "bf16", batch=65536)) == B.GE_ERR_SHAPE
+    r256 = lambda x: (x + 255) // 256 * 256
+    sizes = {}
+    for nb in (0, 1, 3):
+        h = B.gemm_epilog_create(B.make_desc(64, 48, 40, "bf16", "bf16", batch=nb))
+        try:
+            B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(0, 1, 0, 0))
+            sizes[nb] = B.gemm_epilog_workspace_size(h)
+        finally:
+            B.gemm_epilog_free(h)
+    assert sizes[0] == sizes[1] == r256(64 * 48 * 2) and sizes[3] == r256(3 * 64 * 48 * 2)
+    h = B.gemm_epilog_create(B.make_desc(16, 4096, 4096, "f16", "f16", 1, batch=2))
+    try:
+        B.gemm_epilog_plan(h, "gelu_bias", "col", B.ge_pref(2, 0, 0, 4))
+        assert B.gemm_epilog_workspace_size(h) == r256(2 * 4 * 256 * 256 * 4) + r256(2 * 256 * 4)
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_fp8_scales_alignment():
     h = B.gemm_epilog_create(desc(a_type="e4m3", d_type="bf16", k=48))
     try:
