@@ -28,6 +28,8 @@ struct ge_plan_s {
     size_t ws_c = 0;         // unfused intermediate bytes
     size_t ws_partial = 0;   // split-K partial bytes
     size_t ws_counters = 0;  // split-K counter bytes
+    int64_t n_counters = 0;  // split-K arrival counters per product
+    int64_t part_bytes = 0;  // split-K partial bytes per product
     size_t ws_bgrad = 0;     // bias-gradient partial bytes
     int32_t bgrad_parts = 0; // bias-gradient partials per entry
     ge_pref pref = {0, 0, 0, 0};   // the preferences the plan was made with
@@ -124,7 +126,7 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
 // 16-bit ones).
 bool tile_supports(const TileShape* t, int a_type) {
     if (t->kernel == 1) return true;
-    if (t->id == 13) return a_type == GE_F16 || a_type == GE_BF16;
+    if (t->id == 13 || t->id == 14) return a_type == GE_F16 || a_type == GE_BF16;
     return a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
 }
 
@@ -209,6 +211,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     q.path = path;
     q.split_k = 1;
     q.ws_partial = q.ws_counters = 0;
+    q.n_counters = q.part_bytes = 0;
     if (path == PATH_SMALLM) {
         q.tile_id = 0;
         q.tiles_m = 1;
@@ -225,14 +228,26 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.grid = (unsigned)grid;
         if (split > 1) {
             const size_t nbs = d.batch > 1 ? (size_t)d.batch : 1;
-            q.ws_partial = round_up(nbs * (size_t)split * q.tiles_n * 256 * sizeof(float), 256);
-            q.ws_counters = round_up(nbs * (size_t)q.tiles_n * sizeof(uint32_t), 256);
+            q.n_counters = q.tiles_n;
+            q.part_bytes = (int64_t)split * q.tiles_n * 256 * (int64_t)sizeof(float);
+            q.ws_partial = round_up(nbs * (size_t)q.part_bytes, 256);
+            q.ws_counters = round_up(nbs * (size_t)q.n_counters * sizeof(uint32_t), 256);
         }
     } else {
-        if (pr.split_k > 1) return GE_ERR_SHAPE;
         q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n, d.a_type);
+        // the automatic split-K 64 x 64 tile serves problems with so few tiles
+        // (at most a quarter of the CUs) and so long a K that the slices'
+        // parallelism outweighs their partial exchange, which costs about as
+        // much as 30 K steps of the unsplit tile (measured: 1024 x 512 x 2048
+        // takes 13 us unsplit and 29 / 45 us in 2 / 4 slices); the
+        // bias-gradient partials would share its partial buffer
+        if (!pr.tile && q.tile_id == 13 && !is_bgrad(epilog) && d.k >= 4096 &&
+            ceil_div(d.m, 64) * ceil_div(d.n, 64) <= 64)
+            q.tile_id = 14;
         const TileShape* t = find_tile(q.tile_id);
         if (!tile_supports(t, d.a_type)) return GE_ERR_SHAPE;
+        if (pr.split_k > 1 && t->kernel != 5) return GE_ERR_SHAPE;   // only the split-K tile splits K
+        if (t->kernel == 5 && is_bgrad(epilog)) return GE_ERR_EPILOG;
         const int64_t tm = ceil_div(d.m, t->bm), tn = ceil_div(d.n, t->bn);
         if (tm * tn > INT32_MAX) return GE_ERR_SHAPE;
         q.tiles_m = (int32_t)tm;
@@ -240,6 +255,32 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.group_m = (int32_t)(tm < 8 ? (tm > 0 ? tm : 1) : 8);
         q.grid = (unsigned)(tm * tn);
         q.k_per_split = (int32_t)d.k;
+        if (t->kernel == 5) {
+            // K slices of whole 64-element steps: the largest power of two
+            // that keeps the grid within 128 workgroups and every slice at
+            // four or more steps, unless forced.  The last slice of a tile
+            // reads every partial, so more slices cost more than they gain
+            // (measured at 256 x 256 x 65536: 245 us unsplit, 61 us in 8
+            // slices, 118 us in 32)
+            const int64_t steps = ceil_div(d.k, 64);
+            int split = pr.split_k;
+            if (split <= 0) {
+                split = 1;
+                while (tm * tn * split * 2 <= 128 && steps >= split * 2 * 4) split *= 2;
+            }
+            if (split > steps) split = steps > 0 ? (int)steps : 1;
+            if (split > 65535) return GE_ERR_SHAPE;
+            q.k_per_split = (int32_t)(ceil_div(steps, split) * 64);
+            split = q.k_per_split > 0 ? (int)ceil_div(d.k, q.k_per_split) : 1;
+            q.split_k = split;
+            if (split > 1) {
+                const size_t nbs = d.batch > 1 ? (size_t)d.batch : 1;
+                q.n_counters = tm * tn;
+                q.part_bytes = tm * tn * split * (int64_t)t->bm * t->bn * (int64_t)sizeof(float);
+                q.ws_partial = round_up(nbs * (size_t)q.part_bytes, 256);
+                q.ws_counters = round_up(nbs * (size_t)q.n_counters * sizeof(uint32_t), 256);
+            }
+        }
     }
     const size_t nb = d.batch > 1 ? (size_t)d.batch : 1;   // products per launch
     q.ws_c = q.unfused ? round_up(nb * (size_t)d.m * (size_t)d.ldd * elem_size(d.d_type), 256) : 0;
@@ -340,14 +381,13 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     a.bs_d = d.m * d.ldd * elem_size(d.d_type);
     a.bs_bias = len * elem_size(d.d_type);
     a.bs_aux = d.m * h->ldaux * (aux_is_matrix(h->epilog) ? elem_size(d.d_type) : 4);
-    a.bs_part = h->path == PATH_SMALLM ? (int64_t)h->split_k * h->tiles_n * 256 * (int64_t)sizeof(float)
-                                       : (int64_t)h->bgrad_parts * len * (int64_t)sizeof(float);
-    a.bs_cnt = h->tiles_n;
+    a.bs_part = h->split_k > 1 ? h->part_bytes : (int64_t)h->bgrad_parts * len * (int64_t)sizeof(float);
+    a.bs_cnt = h->n_counters;
     uint8_t* ws = (uint8_t*)workspace;
     if (h->split_k > 1) {
         a.partial = (float*)(ws + h->ws_c);
         a.counters = (uint32_t*)(ws + h->ws_c + h->ws_partial);
-        if (launch_clear_counters(a.counters, h->tiles_n * a.batch, stream) != 0) return GE_ERR_HIP;
+        if (launch_clear_counters(a.counters, (int)(h->n_counters * a.batch), stream) != 0) return GE_ERR_HIP;
     }
 
     if (is_bgrad(h->epilog)) a.partial = (float*)(ws + h->ws_c + h->ws_partial + h->ws_counters);
@@ -489,7 +529,7 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
              h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
              t ? t->wn : 8, h->tile_id, t ? t->kernel : 0,
-             t ? (t->kernel == 2 || t->kernel == 4 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
+             t ? (t->kernel >= 2 && t->kernel != 3 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
              h->split_k,
              h->unfused,
              h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad, (long long)h->ldaux);

@@ -125,7 +125,7 @@ __device__ __forceinline__ int swz_row(int row) {
     else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
 }
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB>
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false>
 __global__ void __launch_bounds__(WM* WN * 64)
 ge_tile2_kernel(KernelArgs p_all) {
     const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
@@ -137,14 +137,20 @@ ge_tile2_kernel(KernelArgs p_all) {
     int tm, tn;
     tile_coords<DIN, DOUT, OPB, BM, BN, WM, WN>(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int M = p.m, N = p.n, K = p.k;
+    const int M = p.m, N = p.n;
+    // split-K (SPLIT): this workgroup takes K slice blockIdx.z of k_per_split
+    // elements; its partial accumulators are summed in slice order by the
+    // last slice to finish the tile, which then runs the epilogue
+    const int slice = SPLIT ? (int)blockIdx.z : 0;
+    const int ks = SPLIT ? slice * p.k_per_split : 0;
+    const int K = SPLIT ? max(0, min(p.k - ks, p.k_per_split)) : p.k;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int wm = wave % WM, wn = wave / WM;
     const int r32 = lane & 31, h = lane >> 5;
-    const uint8_t* gA = (const uint8_t*)p.A;
-    const uint8_t* gB = (const uint8_t*)p.B;
+    const uint8_t* gA = (const uint8_t*)p.A + (int64_t)ks * ESZ;
+    const uint8_t* gB = (const uint8_t*)p.B + (OPB == GE_OP_T ? (int64_t)ks * ESZ : (int64_t)ks * p.ldb * ESZ);
     const int KT = (K + BK - 1) / BK;       // K steps
     const int KF = K / BK;                  // full K steps (direct copies)
 
@@ -515,6 +521,54 @@ ge_tile2_kernel(KernelArgs p_all) {
     }
     }   // copy mode
 
+    if constexpr (SPLIT) {
+        if (p.split_k > 1) {
+            // publish this slice's accumulators (lane-major, in the register
+            // layout), count the arrival, and let the last slice sum them.
+            // Device-scope atomic accesses keep the partials coherent across
+            // the dies' separate L2s without a cache-wide fence.
+            constexpr int PER = 16 * C::FM * C::FN;   // floats per thread
+            const int64_t tile_lin = blockIdx.x;
+            float* mine = p.partial + (tile_lin * p.split_k + slice) * (int64_t)(C::NT * PER) + (int64_t)tid * PER;
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        __hip_atomic_store(mine + (i * C::FM + j) * 16 + e, acc[i][j][e], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            // every lane's stores are performed before the arrival is counted
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __shared__ int split_last;
+            __syncthreads();
+            if (tid == 0)
+                split_last = (int)__hip_atomic_fetch_add(&p.counters[tile_lin], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT) == p.split_k - 1;
+            __syncthreads();
+            if (!split_last) return;
+            // the loads below depend on the counter's value (the clobber keeps
+            // them below the branch)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+            for (int sl = 0; sl < p.split_k; ++sl) {
+                const float* ps = p.partial + (tile_lin * p.split_k + sl) * (int64_t)(C::NT * PER) + (int64_t)tid * PER;
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[i][j][e] += __hip_atomic_load(ps + (i * C::FM + j) * 16 + e, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (tid == 0) p.counters[tile_lin] = 0u;   // re-arm for the next launch
+        }
+    }
+
     // ---- fused epilogue on the accumulators (as in tile_kernel.h) ----
     // the product's scale: fp8 dequantisation factors, or an alpha for any dtype
     float s = 1.0f;
@@ -634,6 +688,10 @@ TileFn pick_tile2(int tile_id) {
     case 12: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 2, false, 128>;
     case 13:   // 16-bit inputs only (64-byte fp8 k rows have no swizzle here)
         if constexpr (Elem<DIN>::size == 2) return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128>;
+        else return nullptr;
+    case 14:   // tile 13 with split-K
+        if constexpr (Elem<DIN>::size == 2)
+            return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128, true>;
         else return nullptr;
     }
     return nullptr;

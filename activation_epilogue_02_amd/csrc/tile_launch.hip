@@ -28,7 +28,8 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
     }
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     const int threads = t->wm * t->wn * 64;
-    hipLaunchKernelGGL(fn, dim3(grid, args.batch), dim3(threads), 0, (hipStream_t)stream, args);
+    const unsigned slices = t->kernel == 5 ? (unsigned)args.split_k : 1u;   // split-K tiles: K slices in z
+    hipLaunchKernelGGL(fn, dim3(grid, args.batch, slices), dim3(threads), 0, (hipStream_t)stream, args);
     return (int)hipGetLastError();
 }
 

@@ -169,9 +169,14 @@ typedef struct {
  *          with 4 waves, 256x256 with 8 waves, 256x128, 128x128), 9..10
  *          the same kernel with register-staged copies (256x256 with 8 or
  *          4 waves), 11..12 with 128-byte K steps (256x256 with 8 or 4
- *          waves), 13 a 64x64 tile of it (fp16/bf16 only).  An id the input
- *          dtype does not support gives GE_ERR_SHAPE.
- * split_k: 0 auto, else the number of K slices (small-m path only) */
+ *          waves), 13 a 64x64 tile of it (fp16/bf16 only), 14 that tile with
+ *          split-K (fp16/bf16 only; K slices in parallel, fp32 partials in
+ *          the workspace summed in slice order by the tile's last slice before
+ *          the epilogue; not with the bias-gradient epilogues).  An id the
+ *          input dtype does not support gives GE_ERR_SHAPE.  The automatic
+ *          choice takes 14 for fp16/bf16 problems of at most 64 such tiles
+ *          with k >= 4096.
+ * split_k: 0 auto, else the number of K slices (small-m path, or tile 14) */
 typedef struct {
     int32_t path;
     int32_t unfused;

@@ -279,6 +279,7 @@ def test_forced_launch_failure_hook(monkeypatch):
     (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=2x2 tile_id=7 kernel=2 stages=3"),
     (4096, 1024, 4096, 1, "f16", "tile_id=8 kernel=2"),
     (1024, 512, 2048, 0, "f16", "tile=64x64 waves=2x2 tile_id=13 kernel=4 stages=4"),
+    (256, 256, 65536, 0, "bf16", "tile=64x64 waves=2x2 tile_id=14 kernel=5 stages=4 grid=16 group_m=4 split_k=8 "),
     (128, 64, 256, 0, "f32", "tile=64x64"),
 ])
 def test_planner_choices(m, n, k, op_b, a, expect):
@@ -291,7 +292,7 @@ def test_planner_choices(m, n, k, op_b, a, expect):
         B.gemm_epilog_free(h)
 
 
-@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13, 14])
 def test_pipelined_tiles_reject_fp32_inputs(tile):
     h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "f32", "f32", 0))
     try:
@@ -304,6 +305,38 @@ def test_small_pipelined_tile_rejects_fp8():
     h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "e4m3", "bf16", 0))
     try:
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, 13, 0)) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_split_k_tile_plan():
+    """Tile 14 (the 64x64 tile with split-K): 16-bit inputs only, no
+    bias-gradient epilogues, partials (tiles x split x 64 x 64 fp32) and one
+    counter per tile in the workspace; other tiles refuse a split."""
+    h = B.gemm_epilog_create(B.make_desc(1024, 512, 2048, "f16", "f16", 0))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 0))
+        assert "tile_id=14" in B.gemm_epilog_describe(h) and "split_k=1 " in B.gemm_epilog_describe(h)
+        assert B.gemm_epilog_workspace_size(h) == 0     # 128 tiles already fill the 128-workgroup budget
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 4))
+        assert B.gemm_epilog_workspace_size(h) == 128 * 4 * 64 * 64 * 4 + 512
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 3))
+        assert "split_k=3 " in B.gemm_epilog_describe(h)
+        assert status_of(B.gemm_epilog_plan, h, "bias", "row", B.ge_pref(1, 0, 13, 3)) == B.GE_ERR_SHAPE
+        assert status_of(B.gemm_epilog_plan, h, "dgelu_bgrad", "col", B.ge_pref(1, 0, 14, 0)) == B.GE_ERR_EPILOG
+        B.gemm_epilog_plan(h, "dgelu_bgrad", "col")     # automatic: the unsplit tile
+        assert "tile_id=13" in B.gemm_epilog_describe(h)
+    finally:
+        B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(256, 256, 65536, "bf16", "bf16", 0))
+    try:
+        B.gemm_epilog_plan(h, "dgelu_bgrad", "col")     # a bias gradient never takes the split tile
+        assert "tile_id=13" in B.gemm_epilog_describe(h)
+    finally:
+        B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(512, 512, 2048, "e4m3", "bf16", 0))
+    try:
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, 14, 0)) == B.GE_ERR_SHAPE
     finally:
         B.gemm_epilog_free(h)
 
