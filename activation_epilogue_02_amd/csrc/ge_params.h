@@ -65,7 +65,7 @@ enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 struct TileShape {
     int32_t id, bm, bn, wm, wn, kernel, stages;
 };
-constexpr int kNumTiles = 14;
+constexpr int kNumTiles = 15;
 constexpr TileShape kTiles[kNumTiles] = {
     {1, 64, 64, 2, 2, 1, 2},     // 4 waves, 32 x 32 per wave
     {2, 128, 128, 2, 2, 1, 2},   // 4 waves, 64 x 64 per wave
@@ -81,6 +81,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {12, 256, 256, 2, 2, 4, 2},  // 128-byte K steps for 16-bit inputs: 4 waves
     {13, 64, 64, 2, 2, 4, 4},    // 128-byte K steps, 16-bit inputs only: 4 waves, 32 x 32 per wave
     {14, 64, 64, 2, 2, 5, 4},    // tile 13 with split-K (kernel 5): small problems with long K
+    {15, 256, 128, 4, 2, 2, 4},  // 8 waves, 64 x 64 per wave (two waves per SIMD; fp8's fastest)
 };
 
 // LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64

@@ -689,6 +689,7 @@ TileFn pick_tile2(int tile_id) {
     case 13:   // 16-bit inputs only (64-byte fp8 k rows have no swizzle here)
         if constexpr (Elem<DIN>::size == 2) return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128>;
         else return nullptr;
+    case 15: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 128, 4, 2, 4, false, 64>;
     case 14:   // tile 13 with split-K
         if constexpr (Elem<DIN>::size == 2)
             return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128, true>;

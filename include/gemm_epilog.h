@@ -175,7 +175,7 @@ typedef struct {
  *          the epilogue; not with the bias-gradient epilogues).  An id the
  *          input dtype does not support gives GE_ERR_SHAPE.  The automatic
  *          choice takes 14 for fp16/bf16 problems of at most 64 such tiles
- *          with k >= 4096.
+ *          with k >= 4096.  15: the pipelined kernel at 256x128 with 8 waves.
  * split_k: 0 auto, else the number of K slices (small-m path, or tile 14) */
 typedef struct {
     int32_t path;

@@ -276,7 +276,7 @@ def test_forced_launch_failure_hook(monkeypatch):
     (16, 4096, 4096, 1, "f32", "path=tile"),
     (8192, 8192, 8192, 0, "bf16", "tile=256x256 waves=2x4 tile_id=11 kernel=4 stages=2"),
     (65536, 8192, 16384, 0, "bf16", "tile_id=11 kernel=4"),
-    (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=2x2 tile_id=7 kernel=2 stages=3"),
+    (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=4x2 tile_id=15 kernel=2 stages=3"),
     (4096, 1024, 4096, 1, "f16", "tile_id=8 kernel=2"),
     (1024, 512, 2048, 0, "f16", "tile=64x64 waves=2x2 tile_id=13 kernel=4 stages=4"),
     (256, 256, 65536, 0, "bf16", "tile=64x64 waves=2x2 tile_id=14 kernel=5 stages=4 grid=16 group_m=4 split_k=8 "),
@@ -292,7 +292,7 @@ def test_planner_choices(m, n, k, op_b, a, expect):
         B.gemm_epilog_free(h)
 
 
-@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15])
 def test_pipelined_tiles_reject_fp32_inputs(tile):
     h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "f32", "f32", 0))
     try:

@@ -55,7 +55,7 @@ def test_every_tile_shape(tile, a, d, op_b):
     check_full(w, r)
 
 
-PIPELINED = [5, 6, 7, 8, 9, 10, 11, 12, 13, 14]
+PIPELINED = [5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]
 COMBOS16 = [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
             ("e4m3", "bf16"), ("e4m3", "f16"), ("e4m3", "f32")]
 
@@ -83,7 +83,7 @@ def test_pipelined_tiles_ragged(tile, a, d, op_b):
 
 
 @pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129, 256, 385, 512])
-@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11, 13, 14])
+@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11, 13, 14, 15])
 @pytest.mark.parametrize("a", ["bf16", "e4m3"])
 def test_pipelined_short_and_ragged_k(k, tile, a):
     skip_unsupported(tile, a)

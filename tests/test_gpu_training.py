@@ -37,7 +37,7 @@ def test_training_epilogues_ragged(a, d, ep, axis, op_b):
     check_full(w, r)
 
 
-TILES = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14]
+TILES = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]
 
 
 @pytest.mark.parametrize("tile", TILES)
