@@ -206,15 +206,19 @@ class GemmEpilog:
         return self
 
     def alloc_outputs(self, device="cuda"):
+        """D (and the aux output, workspace) for the planned problem; with
+        batch > 1, leading dimension batch, each product packed after the
+        previous one as the ABI's batch strides expect."""
         d = self.desc
-        D = torch.empty((d.m, d.ldd), dtype=TORCH_DTYPE[d.d_type], device=device)[:, :d.n]
+        lead = (d.batch,) if d.batch > 1 else ()
+        D = torch.empty(lead + (d.m, d.ldd), dtype=TORCH_DTYPE[d.d_type], device=device)[..., :d.n]
         aux = None
         if self.epilog == GE_EPILOG_RELU_AUX_BIAS:
-            aux = torch.empty((d.m, self.aux_ld_bits // 32), dtype=torch.int32, device=device)
+            aux = torch.empty(lead + (d.m, self.aux_ld_bits // 32), dtype=torch.int32, device=device)
         elif self.epilog == GE_EPILOG_GELU_AUX_BIAS:
             # the pre-activation matrix, D's dtype, round_up(n, 128) columns
             dt = TORCH_DTYPE[d.d_type]
-            aux = torch.empty((d.m, self.aux_ld_bits // torch.finfo(dt).bits), dtype=dt,
+            aux = torch.empty(lead + (d.m, self.aux_ld_bits // torch.finfo(dt).bits), dtype=dt,
                               device=device)
         ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device) if self.ws_bytes else None
         return D, aux, ws
