@@ -88,6 +88,7 @@ def lib():
         L.orc_drelu.argtypes = [i64, i64, vp, i64, vp, vp]
         L.orc_dgelu.argtypes = [i64, i64, vp, ctypes.c_int, vp, i64, vp]
         L.orc_bgrad.argtypes = [i64, i64, vp, ctypes.c_int, vp]
+        L.orc_add_beta_c.argtypes = [i64, i64, vp, dbl, ctypes.c_int, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -244,6 +245,19 @@ def dgelu_pass(C: np.ndarray, P: np.ndarray, tp: str) -> np.ndarray:
     D = np.empty_like(C)
     _check(lib().orc_dgelu(m, n, _ptr(C), DTYPES[tp], _ptr(Pc), Pc.shape[1], _ptr(D)), "dgelu")
     return D
+
+
+def add_beta_c(C: np.ndarray, beta: float, Cin: np.ndarray, tc: str) -> np.ndarray:
+    """O1b: C + beta * Cin, Cin given as raw codes of dtype tc, shape (m, ldc)."""
+    C = np.ascontiguousarray(C, dtype=np.float64)
+    m, n = C.shape
+    Cc = _codes(Cin, tc)
+    if Cc.shape[0] != m:
+        raise ValueError("oracle add_beta_c: rows differ")
+    P0 = np.empty_like(C)
+    _check(lib().orc_add_beta_c(m, n, _ptr(C), float(beta), DTYPES[tc], _ptr(Cc), Cc.shape[1], _ptr(P0)),
+           "add_beta_c")
+    return P0
 
 
 def bgrad_pass(Y: np.ndarray, axis: str) -> np.ndarray:

@@ -398,3 +398,17 @@ int orc_bgrad(int64_t m, int64_t n, const double* Y, int axis, double* g)
     }
     return -1;
 }
+
+/* O1b: an added input term, P0 = C + beta * Cin, before the bias (the general
+ * epilogue alpha*A*B + beta*C + bias of the [cuBLASLt page], paragraph on
+ * compute and scale types; alpha is O1's sa*sb).  Cin is given as codes of
+ * dtype tc with row stride ldc, decoded exactly. */
+int orc_add_beta_c(int64_t m, int64_t n, const double* C, double beta, int tc, const void* Cin, int64_t ldc,
+                   double* P0)
+{
+    if (ldc < n || tc < ORC_F32 || tc > ORC_E4M3) return -1;
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            P0[i * n + j] = C[i * n + j] + beta * dec_at(tc, Cin, i * ldc + j);
+    return 0;
+}

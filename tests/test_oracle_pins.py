@@ -437,3 +437,19 @@ def test_gemm_scale_factors_any_dtype(dt):
     Cs = oracle.gemm(np.ascontiguousarray(enc(A)), dt, np.ascontiguousarray(enc(B)), dt, 0, 0.5, 3.0)
     assert np.array_equal(C1, A.astype(np.float64) @ B.astype(np.float64))
     assert np.array_equal(Cs, 1.5 * C1)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_add_beta_c_exact_cases(dt):
+    """O1b: beta = 0 leaves the product; A = 0 leaves beta * C exactly (small
+    integers); the result is linear in beta (padded C rows)."""
+    rng = np.random.default_rng(13)
+    m, n, ld = 4, 6, 8
+    Cin = rng.integers(-8, 9, (m, ld)).astype(np.float32)
+    codes = np.ascontiguousarray({"f32": lambda x: x, "f16": f16_codes, "bf16": bf16_codes}[dt](Cin))
+    P = rng.standard_normal((m, n))
+    assert np.array_equal(oracle.add_beta_c(P, 0.0, codes, dt), P)
+    Z = np.zeros((m, n))
+    assert np.array_equal(oracle.add_beta_c(Z, 2.5, codes, dt), 2.5 * Cin[:, :n].astype(np.float64))
+    d = oracle.add_beta_c(Z, 3.0, codes, dt) - oracle.add_beta_c(Z, 1.0, codes, dt)
+    assert np.array_equal(d, 2.0 * Cin[:, :n].astype(np.float64))
