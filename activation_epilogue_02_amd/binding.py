@@ -83,9 +83,10 @@ def lib():
         L.gemm_epilog_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp,
                                            ctypes.POINTER(ctypes.c_float)]
+        L.gemm_epilog_execute_c.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
-                  "gemm_epilog_describe", "gemm_epilog_autotune"):
+                  "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -163,6 +164,18 @@ def gemm_epilog_free(h: Optional[int]) -> None:
 
 def gemm_epilog_status_string(status: int) -> str:
     return lib().gemm_epilog_status_string(status).decode()
+
+
+def gemm_epilog_execute_c(h: int, A, B, C, ldc: int, beta, bias, D, aux=None, scale_a=None,
+                          scale_b=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+    """execute with the added input term beta*C (C in D's dtype, row stride
+    ldc elements; beta a device fp32 scalar)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gemm_epilog_execute_c(h, _ptr(A), _ptr(B), _ptr(C), ldc, _ptr(beta), _ptr(bias), _ptr(D),
+                                       _ptr(aux), _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
+                                       workspace_bytes, stream),
+           "gemm_epilog_execute_c")
 
 
 def gemm_epilog_autotune(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,

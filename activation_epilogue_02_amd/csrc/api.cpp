@@ -317,9 +317,11 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
     return GE_OK;
 }
 
-int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,
-                        const float* scale_a, const float* scale_b, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+// execute and execute_c: cin (NULL = no added term) is C in D's dtype with
+// row stride ldc, scaled by the device scalar *beta
+static int execute_impl(ge_handle h, const void* A, const void* B, const void* cin, int64_t ldc, const float* beta,
+                        const void* bias, void* D, void* aux, const float* scale_a, const float* scale_b,
+                        void* workspace, size_t workspace_bytes, void* stream) {
     if (!h) return GE_ERR_NULL;
     if (!h->planned) return GE_ERR_STATE;
     const ge_desc& d = h->d;
@@ -330,6 +332,10 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     const bool want_aux = has_aux(h->epilog) && d.m > 0 && d.n > 0;   // else aux holds nothing
     if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
+    if (cin) {
+        if (ldc < h->d.n) return GE_ERR_SHAPE;
+        if ((ldc * elem_size(h->d.d_type)) % 16 || !aligned(cin, 16) || !aligned(beta, 4)) return GE_ERR_ALIGN;
+    }
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||
         !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
         return GE_ERR_ALIGN;
@@ -346,7 +352,6 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
             z.n = (int32_t)d.n;
             z.axis = h->axis;
             z.batch = d.batch > 1 ? d.batch : 1;
-            z.bs_bias = bias_len * elem_size(d.d_type);
             if (launch_bgrad_reduce(d.d_type, z, 0, stream) != 0) return GE_ERR_HIP;
         }
         return GE_OK;
@@ -378,13 +383,11 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     // batched: the packed per-product strides, in bytes (counters: elements)
     const int64_t len = h->axis == GE_BIAS_COL ? d.n : d.m;
     a.batch = d.batch > 1 ? d.batch : 1;
-    a.bs_a = d.m * d.lda * elem_size(d.a_type);
-    a.bs_b = (d.op_b == GE_OP_N ? d.k : d.n) * d.ldb * elem_size(d.b_type);
-    a.bs_d = d.m * d.ldd * elem_size(d.d_type);
-    a.bs_bias = len * elem_size(d.d_type);
-    a.bs_aux = d.m * h->ldaux * (aux_is_matrix(h->epilog) ? elem_size(d.d_type) : 4);
     a.bs_part = h->split_k > 1 ? h->part_bytes : (int64_t)h->bgrad_parts * len * (int64_t)sizeof(float);
     a.bs_cnt = h->n_counters;
+    a.cin = cin;
+    a.beta = beta;
+    a.ldc = ldc;
     uint8_t* ws = (uint8_t*)workspace;
     if (h->split_k > 1) {
         a.partial = (float*)(ws + h->ws_c);
@@ -398,6 +401,7 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     if (h->unfused) {
         // kernel 1: the plain product, rounded to d_type, into the workspace
         k1.epilog = GE_EPILOG_NONE;
+        k1.cin = nullptr;   // the second kernel adds beta * C
         k1.bias = nullptr;
         k1.aux = nullptr;
         k1.ldaux = 0;
@@ -419,6 +423,21 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
     }
     if (is_bgrad(h->epilog) && launch_bgrad_reduce(d.d_type, a, h->bgrad_parts, stream) != 0) return GE_ERR_HIP;
     return GE_OK;
+}
+
+int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                        const float* scale_a, const float* scale_b, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
+                        stream);
+}
+
+int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void* C, int64_t ldc,
+                          const float* beta, const void* bias, void* D, void* aux, const float* scale_a,
+                          const float* scale_b, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h) return GE_ERR_NULL;
+    if (!beta || (!C && h->d.m * h->d.n > 0)) return GE_ERR_NULL;
+    return execute_impl(h, A, B, C, ldc, beta, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes, stream);
 }
 
 int gemm_epilog_free(ge_handle h) {

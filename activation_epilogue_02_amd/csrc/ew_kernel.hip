@@ -21,8 +21,8 @@ __host__ __device__ inline int ew_items_per_row(const KernelArgs& p) {
 template <int DT>
 __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p_all, const void* c_all) {
     // this product of a batch; its intermediate C sits at D's per-product offset
-    const KernelArgs p = batch_slice(p_all, blockIdx.y);
-    const void* c = (const uint8_t*)c_all + (int64_t)blockIdx.y * p_all.bs_d;
+    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.y, 0);
+    const void* c = (const uint8_t*)c_all + (int64_t)blockIdx.y * p_all.m * p_all.ldd * Elem<DT>::size;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int words = ew_items_per_row(p);
     const int64_t row = t / words;
@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p_all, const void
     }
     const bool has_bias = epilog_has_bias(ep);
     const bool row_bias = p.axis == GE_BIAS_ROW;
+    const float beta = p.cin ? *p.beta : 0.0f;
     const float brow = (has_bias && row_bias) ? load_scalar<DT>(p.bias, row) : 0.0f;
     uint32_t bits = 0;
     const int64_t base = row * p.ldd;
@@ -59,9 +60,13 @@ __global__ void __launch_bounds__(256) ge_ew_kernel(KernelArgs p_all, const void
             }
         }
         if (want_grad) grad_factor8<DT>(p, ep, row, nc, gf);
+        float cb[8];   // the added input term beta * C
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cb[j] = 0.0f;
+        if (beta != 0.0f) beta_c8<DT>(p, beta, row, nc, cb);   // beta = 0: C is not read
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float pre = x[j] + (has_bias ? (row_bias ? brow : b[j]) : 0.0f);
+            const float pre = (x[j] + cb[j]) + (has_bias ? (row_bias ? brow : b[j]) : 0.0f);
             if (want_aux && pre > 0.0f && nc + j < p.n) bits |= 1u << (8 * g + j);
             x[j] = want_grad ? grad_apply(ep, pre, gf[j]) : activate(ep, pre);
             b[j] = pre;
@@ -101,7 +106,7 @@ int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* 
 // of 256 rows (COL: partial[rb * n + j]) or 256 columns (ROW: partial[cb * m + i]).
 template <int DT>
 __global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice(p_all, blockIdx.z);   // this product of a batch
+    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.z, 0);   // this product
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int blk = blockIdx.y;
     if (p.axis == GE_BIAS_COL) {
@@ -124,7 +129,7 @@ __global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p_all) {
 // gradient's output).  parts = 0 writes zeros (an empty sum).
 template <int DT>
 __global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p_all, int parts) {
-    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
+    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.y, 0);   // this product
     const int len = p.axis == GE_BIAS_COL ? p.n : p.m;
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= len) return;

@@ -323,6 +323,21 @@ __device__ __forceinline__ void bgrad_tile(const KernelArgs& p, BgradAcc<FM, FN>
     }
 }
 
+// The added input term beta * C for the 8 columns nc .. nc+7 of row m
+// (nc a multiple of 8, m within the problem); columns at or beyond n get 0.
+template <int DOUT>
+__device__ __forceinline__ void beta_c8(const KernelArgs& p, float beta, int64_t m, int nc, float* cb) {
+    const int64_t idx = m * p.ldc + nc;
+    if (nc + 8 <= p.n) {
+        load8<DOUT>(p.cin, idx, cb);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cb[j] = (nc + j < p.n) ? load_scalar<DOUT>(p.cin, idx + j) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cb[j] *= beta;
+}
+
 // GELU_AUX_BIAS: store the pre-activation of the 8 columns nc .. nc+7 of
 // row m into the aux matrix (D's dtype, row stride ldaux elements).
 template <int DOUT>

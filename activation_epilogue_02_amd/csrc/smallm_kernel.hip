@@ -59,7 +59,7 @@ __device__ __forceinline__ u32x4 sm_load_masked(const uint16_t* row, int col, in
 
 template <int DIN, int DOUT>
 __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
+    const KernelArgs p = batch_slice<2, Elem<DOUT>::size>(p_all, blockIdx.y, p_all.n);   // this product
     __shared__ f32x4 red[kSmWaves][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -189,12 +189,15 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_a
     if (p.scale_b) s *= *p.scale_b;
     const int m = r;
     const bool mok = m < M;
+    const float beta = p.cin ? *p.beta : 0.0f;   // beta = 0: C is not read
     float v[4];
     uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = n0 + 4 * q + i;
-        const float x = sum[i] * s + bpre[i];
+        float cb = 0.0f;   // the added input term beta * C
+        if (beta != 0.0f && mok && n < N) cb = beta * load_scalar<DOUT>(p.cin, (int64_t)m * p.ldc + n);
+        const float x = (sum[i] * s + cb) + bpre[i];
         if (want_aux && x > 0.0f && n < N) bits |= 1u << (4 * q + i);
         v[i] = activate(ep, x);
     }

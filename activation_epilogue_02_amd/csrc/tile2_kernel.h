@@ -128,7 +128,8 @@ __device__ __forceinline__ int swz_row(int row) {
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false>
 __global__ void __launch_bounds__(WM* WN * 64)
 ge_tile2_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
+    const KernelArgs p = batch_slice<Elem<DIN>::size, Elem<DOUT>::size>(   // this product of a batch
+        p_all, blockIdx.y, OPB == GE_OP_N ? p_all.k : p_all.n);
     using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB>;
     constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
     using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;
@@ -581,6 +582,9 @@ ge_tile2_kernel(KernelArgs p_all) {
     const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;                    // aux <- P
     const bool want_grad = epilog_is_grad(ep);                              // D = C * f(aux)
     const bool want_bgrad = epilog_is_bgrad(ep);                            // + bias gradient
+    // + beta * C; with beta = 0 C is not read (so it may hold anything)
+    const float beta = p.cin ? *p.beta : 0.0f;
+    const bool with_c = p.cin != nullptr && beta != 0.0f;
     const bool bgrad_col = p.axis == GE_BIAS_COL;
     BgradAcc<C::FM, C::FN> bg;
     bg.clear();
@@ -621,7 +625,10 @@ ge_tile2_kernel(KernelArgs p_all) {
                         for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DOUT>(p.bias, nc + j) : 0.0f;
                     }
                 }
-                float gf[8], pre[8];
+                float gf[8], pre[8], cb[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cb[j] = 0.0f;
+                if (with_c && mok) beta_c8<DOUT>(p, beta, m, nc, cb);
                 if (want_grad) {
                     if (mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
                     else {
@@ -631,7 +638,7 @@ ge_tile2_kernel(KernelArgs p_all) {
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float x = v[g][j] * s + bc[j];
+                    const float x = (v[g][j] * s + cb[j]) + bc[j];
                     pre[j] = x;
                     if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
                     v[g][j] = want_grad ? grad_apply(ep, x, gf[j]) : activate(ep, x);

@@ -254,6 +254,22 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
                         void* D, void* aux, const float* scale_a, const float* scale_b,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* execute with a further input term: the product becomes s*A*B + beta*C
+ * before the bias, activation or derivative, i.e. D = epilogue(s*A*B +
+ * beta*C + bias) -- the general alpha/beta form that the cuBLASLt page's
+ * paragraph on compute and scale types implies (alpha = s, see execute).
+ *   C     device matrix, m x n in D's dtype, row stride ldc >= n elements
+ *         (ldc * element size a multiple of 16 bytes); may be D itself (an
+ *         in-place update: every element is read before it is written, by
+ *         the same thread); with batch > 1, product b reads C + b*m*ldc
+ *   beta  device pointer to one fp32, 4-byte aligned; when it holds 0, C is
+ *         not read (it may hold anything, NaN included)
+ * The other arguments, the asynchrony and the errors are as for execute, plus
+ * GE_ERR_NULL (beta NULL, or C NULL with m*n > 0) and GE_ERR_SHAPE (ldc < n). */
+int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void* C, int64_t ldc,
+                          const float* beta, const void* bias, void* D, void* aux, const float* scale_a,
+                          const float* scale_b, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Release the handle (NULL is accepted).  Host-only. */
 int gemm_epilog_free(ge_handle h);
 

@@ -107,7 +107,8 @@ def make_aux_input(w: synth.Workload, device="cuda", seed=None) -> torch.Tensor:
 
 def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int = 0,
                 unfused: int = 0, tile: int = 0, split_k: int = 0, poison=True,
-                device="cuda", lda=None, ldb=None, ldd=None, aux_in=None):
+                device="cuda", lda=None, ldb=None, ldd=None, aux_in=None, cin=None, beta=None,
+                in_place=False):
     """Execute the planned op through the C ABI; returns (D_full, aux, h-desc, buffers)."""
     a_dt, d_dt = w.in_dtype, w.out_dtype
     ea, ed = ESZ[a_dt], ESZ[d_dt]
@@ -143,10 +144,25 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
             bias = torch.full((w.m if w.axis == "row" else w.n,), float("nan"),
                               dtype=synth.TORCH_DTYPE[d_dt], device=device)
             with_bias = True
-        g.execute(A, Bm, bias if with_bias else None, D, aux, sa, sb, ws)
+        if cin is not None:
+            # the added input term: C in D's dtype, padded rows (NaN padding),
+            # or D itself (in place)
+            beta_t = torch.tensor([beta], dtype=torch.float32, device=device)
+            if in_place:
+                D[:, : w.n] = cin.to(device)
+                C, ldc = D, ldd
+            else:
+                C = padded(cin.to(device), ldd, d_dt, poison)
+                ldc = ldd
+            cin_host = cin.detach().cpu().contiguous()
+            B.gemm_epilog_execute_c(g.h, A, Bm, C, ldc, beta_t, bias if with_bias else None, D, aux, sa, sb,
+                                    ws, None if ws is None else ws.numel(), None)
+        else:
+            cin_host = None
+            g.execute(A, Bm, bias if with_bias else None, D, aux, sa, sb, ws)
         torch.cuda.synchronize()
         return Result(D=D, aux=aux, A=A, B=Bm, bias=bias, sa=sa, sb=sb, lda=lda, ldb=ldb,
-                      ldd=ldd, desc=desc,
+                      ldd=ldd, desc=desc, cin=cin_host, beta=beta,
                       ldw=(g.aux_ld_bits // 32) if w.epilog in ("relu_aux_bias", "drelu", "drelu_bgrad")
                       else None)
     finally:
@@ -161,6 +177,8 @@ def oracle_full(w: synth.Workload, r: Result):
     sa = float(r.sa.item()) if r.sa is not None else 1.0
     sb = float(r.sb.item()) if r.sb is not None else 1.0
     C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+    if getattr(r, "cin", None) is not None and r.beta != 0.0:
+        C = oracle.add_beta_c(C, r.beta, codes(r.cin), d_dt)
     if base_grad(w.epilog) == "drelu":
         return oracle.drelu_pass(C, codes(r.aux)), C, None
     if base_grad(w.epilog) == "dgelu":

@@ -248,6 +248,26 @@ def test_batch_validation_and_workspace():
         B.gemm_epilog_free(h)
 
 
+def test_execute_c_validation():
+    """execute_c's own checks fail before anything runs."""
+    h = B.gemm_epilog_create(desc())
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        L = B.lib()
+        ex = lambda C, ldc, beta: L.gemm_epilog_execute_c(h, FAKE, FAKE, C, ldc, beta, FAKE, FAKE, None, None,
+                                                          None, None, 0, None)
+        assert ex(FAKE, 48, None) == B.GE_ERR_NULL        # beta
+        assert ex(None, 48, FAKE) == B.GE_ERR_NULL        # C
+        assert ex(FAKE, 40, FAKE) == B.GE_ERR_SHAPE       # ldc < n
+        assert ex(FAKE, 52, FAKE) == B.GE_ERR_ALIGN       # ldc * 2 bytes not a multiple of 16
+        assert ex(FAKE + 8, 48, FAKE) == B.GE_ERR_ALIGN   # C
+        assert ex(FAKE, 48, FAKE + 2) == B.GE_ERR_ALIGN   # beta
+        assert L.gemm_epilog_execute_c(None, FAKE, FAKE, FAKE, 48, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                                       None) == B.GE_ERR_NULL
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_fp8_scales_alignment():
     h = B.gemm_epilog_create(desc(a_type="e4m3", d_type="bf16", k=48))
     try:

@@ -135,3 +135,58 @@ def test_autotune_skips_candidates_beyond_the_workspace():
     ws = 4 * 768 * 4   # four tile rows of 256
     desc, _ = autotuned_desc(w, inp, ws_bytes=ws)
     assert "tile=256x" in desc, desc
+
+
+def c_input(w, seed=21, poison=False):
+    """A seeded C term in D's dtype (m x n), optionally NaN-poisoned."""
+    g = torch.Generator().manual_seed(seed)
+    c = torch.randn((w.m, w.n), generator=g).to(synth.TORCH_DTYPE[w.out_dtype])
+    if poison:
+        c[::3, ::5] = float("nan")
+    return c
+
+
+@pytest.mark.parametrize("a,d", COMBOS, ids=[f"{a}->{d}" for a, d in COMBOS])
+@pytest.mark.parametrize("ep", ["none", "bias", "relu_aux_bias", "gelu_bias", "tanh_bias", "gelu_aux_bias",
+                                "dgelu", "dgelu_bgrad"])
+@pytest.mark.parametrize("tile", [0, 1])
+def test_beta_c_every_dtype_tile_paths(a, d, ep, tile):
+    """D = epilogue(s*A*B + beta*C + bias) on the planner's tile and the
+    register-staged 64x64 tile, both B layouts, ragged shapes."""
+    for op_b in (0, 1):
+        w = wl(150, 200, 136, a, d, ep, "col", op_b, seed=op_b + 5)
+        r = run_library(w, with_alpha(synth.make_inputs(w), 0.5, 1.0), pad=1, path=1, tile=tile,
+                        cin=c_input(w), beta=0.75)
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_beta_c_small_m(split):
+    w = wl(16, 520, 1000, "f16", "f16", "gelu_bias", "col", 1, seed=split)
+    r = run_library(w, synth.make_inputs(w), pad=1, path=2, split_k=split, cin=c_input(w), beta=-1.5)
+    assert "path=smallm" in r.desc
+    check_full(w, r)
+
+
+@pytest.mark.parametrize("ep", ["relu_aux_bias", "tanh_bias"])
+def test_beta_c_unfused_and_in_place(ep):
+    w = wl(260, 300, 96, "bf16", "bf16", ep, "row", 0, seed=6)
+    inp = synth.make_inputs(w)
+    check_full(w, run_library(w, inp, pad=1, unfused=1, cin=c_input(w), beta=2.0))
+    # C == D: every element is read before the same thread writes it
+    check_full(w, run_library(w, inp, pad=1, cin=c_input(w), beta=2.0, in_place=True))
+    check_full(w, run_library(w, inp, pad=1, unfused=1, cin=c_input(w), beta=2.0, in_place=True))
+
+
+def test_beta_zero_does_not_read_c():
+    """beta = 0: C is not read, so NaNs in it do not reach D, and D equals
+    the plain execute bit for bit."""
+    w = wl(300, 260, 200, "bf16", "bf16", "gelu_bias", "row", 0, seed=9)
+    inp = synth.make_inputs(w)
+    r0 = run_library(w, inp)
+    r1 = run_library(w, inp, cin=c_input(w, poison=True), beta=0.0)
+    assert torch.equal(r0.D.view(torch.int16), r1.D.view(torch.int16))
+    ws = wl(16, 520, 1000, "f16", "f16", "gelu_bias", "col", 1, seed=2)
+    s0 = run_library(ws, synth.make_inputs(ws), path=2)
+    s1 = run_library(ws, synth.make_inputs(ws), path=2, cin=c_input(ws, poison=True), beta=0.0)
+    assert torch.equal(s0.D.view(torch.int16), s1.D.view(torch.int16))
