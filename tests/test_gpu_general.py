@@ -190,3 +190,65 @@ def test_beta_zero_does_not_read_c():
     s0 = run_library(ws, synth.make_inputs(ws), path=2)
     s1 = run_library(ws, synth.make_inputs(ws), path=2, cin=c_input(ws, poison=True), beta=0.0)
     assert torch.equal(s0.D.view(torch.int16), s1.D.view(torch.int16))
+
+
+def test_graph_replays_match_eager():
+    """The paths with workspace state -- small-m split-K counters and
+    partials, the split-K tile, the bias-gradient partials -- and execute_c,
+    captured in one HIP graph: every replay, with eager work and
+    synchronisation in between, reproduces the eager results bit for bit."""
+    dev = "cuda"
+    cases = [
+        (wl(16, 1040, 4096, "f16", "f16", "gelu_bias", "col", 1, seed=1), dict(path=2, split_k=4)),
+        (wl(256, 256, 8192, "bf16", "bf16", "relu_aux_bias", "row", 0, seed=2), dict(path=1, tile=14, split_k=4)),
+        (wl(300, 264, 200, "bf16", "bf16", "dgelu_bgrad", "col", 0, seed=3), dict(path=1)),
+        (wl(300, 264, 200, "bf16", "bf16", "tanh_bias", "row", 0, seed=4), dict(path=1, beta=True)),
+    ]
+    runs = []
+    for w, pref in cases:
+        use_c = pref.pop("beta", False)
+        g = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
+        g.plan(w.epilog, w.axis, **pref)
+        inp = synth.make_inputs(w)
+        A, Bm = inp.A.to(dev), inp.B.to(dev)
+        bias = inp.bias.reshape(-1).to(dev)
+        if w.epilog.endswith("_bgrad"):
+            bias = torch.empty_like(bias)
+        D, aux, ws = g.alloc_outputs(dev)
+        if w.epilog in ("dgelu", "dgelu_bgrad"):
+            aux = synth.make_aux(w, device=dev)
+        C = c_input(w).to(dev) if use_c else None
+        beta = torch.tensor([0.5], device=dev) if use_c else None
+
+        def call(g=g, A=A, Bm=Bm, bias=bias, D=D, aux=aux, ws=ws, C=C, beta=beta, w=w):
+            s = torch.cuda.current_stream().cuda_stream
+            if C is not None:
+                B.gemm_epilog_execute_c(g.h, A, Bm, C, C.stride(0), beta, bias, D, aux, workspace=ws, stream=s)
+            else:
+                B.gemm_epilog_execute(g.h, A, Bm, bias, D, aux, None, None, ws,
+                                      None if ws is None else ws.numel(), s)
+        runs.append((g, call, D, bias))
+    eager = []
+    for g, call, D, bias in runs:
+        call()
+        torch.cuda.synchronize()
+        eager.append((D.clone(), bias.clone()))
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _, call, _, _ in runs:
+                call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for _, _, D, bias in runs:
+            D.fill_(float("nan"))   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (g, _, D, bias), (De, be) in zip(runs, eager):
+            assert torch.equal(D.view(torch.int16), De.view(torch.int16)), (rep, g.describe())
+            assert torch.equal(bias.view(torch.int16), be.view(torch.int16)), (rep, g.describe())
+    for g, _, _, _ in runs:
+        g.free()
