@@ -15,6 +15,11 @@
 //    in flight while the matrix cores work on the current one.  A wave waits
 //    for its own copies with s_waitcnt vmcnt(n) and the workgroup meets at a
 //    plain s_barrier (no memory fence, which would drain every copy).
+//  * LDS holds the A stages first, then the B stages, so consecutive stages
+//    of one operand are A_BYTES (or B_BYTES) apart -- 32 KiB at 256 x 256 --
+//    within the 16-bit immediate offset of the LDS reads; with two stages the
+//    main loop takes two steps per iteration, and each stage's base becomes
+//    such an immediate instead of a per-read address add.
 //  * Since the LDS address of a lane is fixed by the lane id, the layout is
 //    chosen on the global side: lane (row R, slot s) fetches chunk
 //    s ^ g(R) of its row, which XOR-swizzles the 16-byte chunks of each LDS
@@ -194,12 +199,13 @@ ge_tile2_kernel(KernelArgs p_all) {
 
     // direct copy c (A copies first, then B) of full K step t into stage t % SE
     auto copy_one = [&](int t, int c) {
-        uint8_t* st = smem + (t % SE) * C::STAGE;
+        uint8_t* sa = smem + (t % SE) * C::A_BYTES;                      // A stages first,
+        uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;    // then B stages
         if (c < C::A_INS)
-            copy_to_lds16(srcA[c] + (int64_t)t * stepA, lds_addr(st + (wave * C::A_INS + c) * 1024));
+            copy_to_lds16(srcA[c] + (int64_t)t * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
         else
             copy_to_lds16(srcB[c - C::A_INS] + (int64_t)t * stepB,
-                          lds_addr(st + C::A_BYTES + (wave * C::B_INS + c - C::A_INS) * 1024));
+                          lds_addr(sb + (wave * C::B_INS + c - C::A_INS) * 1024));
     };
     // issue the direct copies of full K step t into stage t % SE
     auto issue_direct = [&](int t) {
@@ -209,7 +215,8 @@ ge_tile2_kernel(KernelArgs p_all) {
 
     // the ragged last K step t: through registers, elements at k >= K zeroed
     auto issue_tail = [&](int t) {
-        uint8_t* st = smem + (t % SE) * C::STAGE;
+        uint8_t* sa = smem + (t % SE) * C::A_BYTES;
+        uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;
         const int k0 = t * BK;
         u32x4 va[C::A_INS], vb[C::B_INS];
 #pragma unroll
@@ -223,10 +230,10 @@ ge_tile2_kernel(KernelArgs p_all) {
                 vb[i] = load_chunk<ESZ>(gB, p.ldb, k0 + rowB_cp[i], K, min(chB_cp[i], nlast), N);
         }
 #pragma unroll
-        for (int i = 0; i < C::A_INS; ++i) *(u32x4*)(st + (wave * C::A_INS + i) * 1024 + lane * 16) = va[i];
+        for (int i = 0; i < C::A_INS; ++i) *(u32x4*)(sa + (wave * C::A_INS + i) * 1024 + lane * 16) = va[i];
 #pragma unroll
         for (int i = 0; i < C::B_INS; ++i)
-            *(u32x4*)(st + C::A_BYTES + (wave * C::B_INS + i) * 1024 + lane * 16) = vb[i];
+            *(u32x4*)(sb + (wave * C::B_INS + i) * 1024 + lane * 16) = vb[i];
     };
 
     auto issue = [&](int t) {
@@ -271,18 +278,18 @@ ge_tile2_kernel(KernelArgs p_all) {
                 if constexpr (OPB == GE_OP_T) {
                     const int row = wn * C::TN + f * 32 + r32;
                     const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
-                    offB[f][kk][e] = C::A_BYTES + row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
+                    offB[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
                 } else if constexpr (ESZ == 2) {
                     const int G = lane >> 4, i = lane & 15;
                     const int k = 16 * kk + 8 * (G >> 1) + 4 * e + (i >> 2);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 4 * (i & 3);
                     offB[f][kk][e] =
-                        C::A_BYTES + k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k, C::KN_CPR)) << 4) + ((n & 4) << 1);
+                        k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k, C::KN_CPR)) << 4) + ((n & 4) << 1);
                 } else {
                     const int G = lane >> 4, i = lane & 15;
                     const int k = 64 * kk + 32 * (G >> 1) + 8 * e + (i >> 1);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 8 * (i & 1);
-                    offB[f][kk][e] = C::A_BYTES + k * C::KN_ROWB +
+                    offB[f][kk][e] = k * C::KN_ROWB +
                                      (((n >> 4) ^ swz_kn8(k, C::KN_CPR)) << 4) + (n & 8);
                 }
             }
@@ -292,7 +299,7 @@ ge_tile2_kernel(KernelArgs p_all) {
     auto read16 = [&](const uint8_t* a) { return *(const u32x4*)a; };
     // fragment f of B (or of A) for k sub-step kk of the step held in `stage`
     auto load_fragB = [&](int stage, int kk, int f, Frag (&bfr)[C::FN]) {
-        const uint8_t* st = smem + stage * C::STAGE;
+        const uint8_t* st = smem + SE * C::A_BYTES + stage * C::B_BYTES;   // B stage
         if constexpr (OPB == GE_OP_T && ESZ == 2) {
             bfr[f] = read16(st + offB[f][kk][0]);
         } else if constexpr (OPB == GE_OP_T) {
@@ -318,7 +325,7 @@ ge_tile2_kernel(KernelArgs p_all) {
         }
     };
     auto load_fragA = [&](int stage, int kk, int f, Frag (&af)[C::FM]) {
-        const uint8_t* st = smem + stage * C::STAGE;
+        const uint8_t* st = smem + stage * C::A_BYTES;   // A stage
         if constexpr (ESZ == 2) {
             af[f] = read16(st + offA[f][kk][0]);
         } else {
@@ -415,12 +422,13 @@ ge_tile2_kernel(KernelArgs p_all) {
         };
         auto commit = [&](int t, const u32x4 (&ra)[C::A_INS], const u32x4 (&rb)[C::B_INS]) {
             if (t >= KT) return;
-            uint8_t* st = smem + (t % 2) * C::STAGE;
+            uint8_t* st = smem + (t % 2) * C::A_BYTES;
+            uint8_t* stb = smem + SE * C::A_BYTES + (t % 2) * C::B_BYTES;
 #pragma unroll
             for (int i = 0; i < C::A_INS; ++i) *(u32x4*)(st + (wave * C::A_INS + i) * 1024 + lane * 16) = ra[i];
 #pragma unroll
             for (int i = 0; i < C::B_INS; ++i)
-                *(u32x4*)(st + C::A_BYTES + (wave * C::B_INS + i) * 1024 + lane * 16) = rb[i];
+                *(u32x4*)(stb + (wave * C::B_INS + i) * 1024 + lane * 16) = rb[i];
         };
         auto barrier = [&]() {
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads and writes done
@@ -504,17 +512,29 @@ ge_tile2_kernel(KernelArgs p_all) {
             interleave();
         }
     };
-    for (int kt = 0; kt < KT - 1; ++kt) {
-        inner(kt % SE);
+    auto step_body = [&](int kt, int stage) {
+        inner(stage);
         wait_step(min(SE - 2, KT - 2 - kt));
         if (kt + SE < KT) issue(kt + SE);
         // the copies stay ahead of the reads below; the last sub-step's
         // MFMAs interleave with the reads of step kt + 1's first fragments
         __builtin_amdgcn_sched_barrier(0);
-        load_frags((kt + 1) % SE, 0, a0, b0);
+        load_frags((stage + 1) % SE, 0, a0, b0);
         reads_first();
         mfmas(a1, b1);   // the last sub-step (NKK - 1 is odd)
         interleave();
+    };
+    if constexpr (SE == 2) {
+        // two steps per iteration, so that each stage's LDS base is a
+        // constant the fragment reads take as an immediate offset
+        int kt = 0;
+        for (; kt + 2 <= KT - 1; kt += 2) {
+            step_body(kt, 0);
+            step_body(kt + 1, 1);
+        }
+        if (kt < KT - 1) step_body(kt, 0);
+    } else {
+        for (int kt = 0; kt < KT - 1; ++kt) step_body(kt, kt % SE);
     }
     if (KT > 0) {
         inner((KT - 1) % SE);
