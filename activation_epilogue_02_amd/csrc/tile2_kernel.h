@@ -17,9 +17,9 @@
 //    plain s_barrier (no memory fence, which would drain every copy).
 //  * LDS holds the A stages first, then the B stages, so consecutive stages
 //    of one operand are A_BYTES (or B_BYTES) apart -- 32 KiB at 256 x 256 --
-//    within the 16-bit immediate offset of the LDS reads; with two stages the
-//    main loop takes two steps per iteration, and each stage's base becomes
-//    such an immediate instead of a per-read address add.
+//    within the 16-bit immediate offset of the LDS reads; the main loop takes
+//    one step per stage per iteration, so each stage's base becomes such an
+//    immediate instead of a per-read address add.
 //  * Since the LDS address of a lane is fixed by the lane id, the layout is
 //    chosen on the global side: lane (row R, slot s) fetches chunk
 //    s ^ g(R) of its row, which XOR-swizzles the 16-byte chunks of each LDS
@@ -524,17 +524,15 @@ ge_tile2_kernel(KernelArgs p_all) {
         mfmas(a1, b1);   // the last sub-step (NKK - 1 is odd)
         interleave();
     };
-    if constexpr (SE == 2) {
-        // two steps per iteration, so that each stage's LDS base is a
-        // constant the fragment reads take as an immediate offset
+    {
+        // SE steps per iteration, so that each stage's LDS base is a
+        // constant the fragment reads can take as an immediate offset
         int kt = 0;
-        for (; kt + 2 <= KT - 1; kt += 2) {
-            step_body(kt, 0);
-            step_body(kt + 1, 1);
+        for (; kt + SE <= KT - 1; kt += SE) {
+#pragma unroll
+            for (int u = 0; u < SE; ++u) step_body(kt + u, u);
         }
-        if (kt < KT - 1) step_body(kt, 0);
-    } else {
-        for (int kt = 0; kt < KT - 1; ++kt) step_body(kt, kt % SE);
+        for (int u = 0; kt < KT - 1; ++kt, ++u) step_body(kt, u);
     }
     if (KT > 0) {
         inner((KT - 1) % SE);
