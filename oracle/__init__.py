@@ -78,6 +78,8 @@ def lib():
         L.orc_gemm_entries.argtypes = [i64, ctypes.c_int, vp, i64, ctypes.c_int,
                                        vp, i64, ctypes.c_int, dbl, dbl, i64,
                                        vp, vp, vp]
+        L.orc_gemm_abs.argtypes = L.orc_gemm.argtypes
+        L.orc_gemm_abs_entries.argtypes = L.orc_gemm_entries.argtypes
         L.orc_bias.argtypes = [i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp]
         L.orc_bias_entries.argtypes = [i64, vp, vp, vp, ctypes.c_int,
                                        ctypes.c_int, vp, vp]
@@ -129,12 +131,7 @@ def encode(x, dtype: str) -> np.ndarray:
 
 
 # ---- O1..O4 ------------------------------------------------------------------
-def gemm(A: np.ndarray, ta: str, B: np.ndarray, tb: str, op_b: int = 0,
-         sa: float = 1.0, sb: float = 1.0, m=None, n=None, k=None,
-         lda=None, ldb=None) -> np.ndarray:
-    """O1: C = sa*sb * A @ B in float64 (p ascending).  A: m x k row-major
-    codes (2-D array, or 1-D with m, k, lda).  B: k x n (op_b=0) or n x k
-    (op_b=1) row-major codes."""
+def _gemm_call(fn, what, A, ta, B, tb, op_b, sa, sb, m, n, k, lda, ldb):
     A = _codes(A, ta)
     B = _codes(B, tb)
     if A.ndim == 2:
@@ -146,29 +143,56 @@ def gemm(A: np.ndarray, ta: str, B: np.ndarray, tb: str, op_b: int = 0,
         else:
             kb, n = B.shape
         if kb != k:
-            raise ValueError("oracle gemm: inner dimensions differ")
+            raise ValueError(f"oracle {what}: inner dimensions differ")
         ldb = B.shape[1]
     C = np.empty((m, n), dtype=np.float64)
-    _check(lib().orc_gemm(m, n, k, DTYPES[ta], _ptr(A), lda, DTYPES[tb], _ptr(B),
-                          ldb, int(op_b), float(sa), float(sb), _ptr(C)), "gemm")
+    _check(fn(m, n, k, DTYPES[ta], _ptr(A), lda, DTYPES[tb], _ptr(B),
+              ldb, int(op_b), float(sa), float(sb), _ptr(C)), what)
     return C
 
 
-def gemm_entries(A_rows: np.ndarray, ta: str, slot: np.ndarray, cols: np.ndarray,
-                 B: np.ndarray, tb: str, op_b: int = 0, sa: float = 1.0,
-                 sb: float = 1.0) -> np.ndarray:
-    """O1 at selected entries: C[row slot[t] of A_rows][cols[t]]."""
+def gemm(A: np.ndarray, ta: str, B: np.ndarray, tb: str, op_b: int = 0,
+         sa: float = 1.0, sb: float = 1.0, m=None, n=None, k=None,
+         lda=None, ldb=None) -> np.ndarray:
+    """O1: C = sa*sb * A @ B in float64 (p ascending).  A: m x k row-major
+    codes (2-D array, or 1-D with m, k, lda).  B: k x n (op_b=0) or n x k
+    (op_b=1) row-major codes."""
+    return _gemm_call(lib().orc_gemm, "gemm", A, ta, B, tb, op_b, sa, sb, m, n, k, lda, ldb)
+
+
+def gemm_abs(A: np.ndarray, ta: str, B: np.ndarray, tb: str, op_b: int = 0,
+             sa: float = 1.0, sb: float = 1.0, m=None, n=None, k=None,
+             lda=None, ldb=None) -> np.ndarray:
+    """|sa*sb| * |A| @ |B|: the magnitude term of the dot-product rounding
+    error bound (Higham, section 3.1), same arguments as gemm."""
+    return _gemm_call(lib().orc_gemm_abs, "gemm_abs", A, ta, B, tb, op_b, sa, sb, m, n, k, lda, ldb)
+
+
+def _entries_call(fn, what, A_rows, ta, slot, cols, B, tb, op_b, sa, sb):
     A_rows = _codes(A_rows, ta)
     B = _codes(B, tb)
     k = A_rows.shape[1]
     slot = np.ascontiguousarray(slot, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     out = np.empty(slot.shape[0], dtype=np.float64)
-    _check(lib().orc_gemm_entries(k, DTYPES[ta], _ptr(A_rows), A_rows.shape[1],
-                                  DTYPES[tb], _ptr(B), B.shape[1], int(op_b),
-                                  float(sa), float(sb), slot.shape[0], _ptr(slot),
-                                  _ptr(cols), _ptr(out)), "gemm_entries")
+    _check(fn(k, DTYPES[ta], _ptr(A_rows), A_rows.shape[1], DTYPES[tb], _ptr(B), B.shape[1], int(op_b),
+              float(sa), float(sb), slot.shape[0], _ptr(slot), _ptr(cols), _ptr(out)), what)
     return out
+
+
+def gemm_entries(A_rows: np.ndarray, ta: str, slot: np.ndarray, cols: np.ndarray,
+                 B: np.ndarray, tb: str, op_b: int = 0, sa: float = 1.0,
+                 sb: float = 1.0) -> np.ndarray:
+    """O1 at selected entries: C[row slot[t] of A_rows][cols[t]]."""
+    return _entries_call(lib().orc_gemm_entries, "gemm_entries", A_rows, ta, slot, cols, B, tb, op_b, sa, sb)
+
+
+def gemm_abs_entries(A_rows: np.ndarray, ta: str, slot: np.ndarray, cols: np.ndarray,
+                     B: np.ndarray, tb: str, op_b: int = 0, sa: float = 1.0,
+                     sb: float = 1.0) -> np.ndarray:
+    """gemm_abs at selected entries (arguments as gemm_entries)."""
+    return _entries_call(lib().orc_gemm_abs_entries, "gemm_abs_entries", A_rows, ta, slot, cols, B, tb,
+                         op_b, sa, sb)
 
 
 def bias_pass(C: np.ndarray, bias: np.ndarray, tbias: str, axis: str) -> np.ndarray:

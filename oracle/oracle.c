@@ -176,18 +176,27 @@ static double b_at(int tb, const void* B, int64_t ldb, int op_b, int64_t p, int6
     return op_b ? dec_at(tb, B, j * ldb + p) : dec_at(tb, B, p * ldb + j);
 }
 
-int orc_gemm(int64_t m, int64_t n, int64_t k,
-             int ta, const void* A, int64_t lda,
-             int tb, const void* B, int64_t ldb, int op_b,
-             double sa, double sb, double* C /* m x n, dense */)
+/* absval = 0: the product itself.  absval = 1: the same sums over the
+ * absolute values of the operands, |sa*sb| * sum_p |A[i][p]| * |B[p][j]| --
+ * the magnitude term of the standard forward error bound of a dot product
+ * computed in floating point (Higham, "Accuracy and Stability of Numerical
+ * Algorithms", section 3.1: |fl(x.y) - x.y| <= gamma_n * |x|.|y|), which the
+ * parity tests use to bound each output element's rounding error. */
+static double opnd(double v, int absval) { return absval ? fabs(v) : v; }
+
+static int gemm_impl(int64_t m, int64_t n, int64_t k,
+                     int ta, const void* A, int64_t lda,
+                     int tb, const void* B, int64_t ldb, int op_b,
+                     double sa, double sb, int absval, double* C)
 {
     if (m < 0 || n < 0 || k < 0) return -1;
+    const double s = absval ? fabs(sa * sb) : sa * sb;
     /* decode B once (column access pattern), A per row */
     double* Bd = (double*)malloc(sizeof(double) * (size_t)(k * n > 0 ? k * n : 1));
     if (!Bd) return -2;
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < k; ++p)
-        for (int64_t j = 0; j < n; ++j) Bd[p * n + j] = b_at(tb, B, ldb, op_b, p, j);
+        for (int64_t j = 0; j < n; ++j) Bd[p * n + j] = opnd(b_at(tb, B, ldb, op_b, p, j), absval);
     int err = 0;
 #pragma omp parallel
     {
@@ -199,14 +208,14 @@ int orc_gemm(int64_t m, int64_t n, int64_t k,
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int64_t i = 0; i < m; ++i) {
-                for (int64_t p = 0; p < k; ++p) arow[p] = dec_at(ta, A, i * lda + p);
+                for (int64_t p = 0; p < k; ++p) arow[p] = opnd(dec_at(ta, A, i * lda + p), absval);
                 for (int64_t j = 0; j < n; ++j) acc[j] = 0.0;
                 for (int64_t p = 0; p < k; ++p) {         /* p ascending */
                     const double a = arow[p];
                     const double* brow = Bd + p * n;
                     for (int64_t j = 0; j < n; ++j) acc[j] += a * brow[j];
                 }
-                for (int64_t j = 0; j < n; ++j) C[i * n + j] = (sa * sb) * acc[j];
+                for (int64_t j = 0; j < n; ++j) C[i * n + j] = s * acc[j];
             }
         }
         free(arow);
@@ -216,23 +225,59 @@ int orc_gemm(int64_t m, int64_t n, int64_t k,
     return err;
 }
 
+int orc_gemm(int64_t m, int64_t n, int64_t k,
+             int ta, const void* A, int64_t lda,
+             int tb, const void* B, int64_t ldb, int op_b,
+             double sa, double sb, double* C /* m x n, dense */)
+{
+    return gemm_impl(m, n, k, ta, A, lda, tb, B, ldb, op_b, sa, sb, 0, C);
+}
+
+/* |sa*sb| * |A|.|B| (see gemm_impl). */
+int orc_gemm_abs(int64_t m, int64_t n, int64_t k,
+                 int ta, const void* A, int64_t lda,
+                 int tb, const void* B, int64_t ldb, int op_b,
+                 double sa, double sb, double* G /* m x n, dense */)
+{
+    return gemm_impl(m, n, k, ta, A, lda, tb, B, ldb, op_b, sa, sb, 1, G);
+}
+
 /* O1 on selected entries only, for problems too large to compute whole.
  * A_rows holds some rows of A (leading dimension lda); entry t is
- * C[row of A_rows[slot[t]]][col[t]].  Same arithmetic as orc_gemm. */
+ * C[row of A_rows[slot[t]]][col[t]].  Same arithmetic as orc_gemm (absval 0)
+ * or orc_gemm_abs (absval 1). */
+static int entries_impl(int64_t k, int ta, const void* A_rows, int64_t lda,
+                        int tb, const void* B, int64_t ldb, int op_b,
+                        double sa, double sb, int absval, int64_t cnt,
+                        const int64_t* slot, const int64_t* col, double* out)
+{
+    if (k < 0 || cnt < 0) return -1;
+    const double s = absval ? fabs(sa * sb) : sa * sb;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < cnt; ++t) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < k; ++p)              /* p ascending */
+            acc += opnd(dec_at(ta, A_rows, slot[t] * lda + p), absval) *
+                   opnd(b_at(tb, B, ldb, op_b, p, col[t]), absval);
+        out[t] = s * acc;
+    }
+    return 0;
+}
+
 int orc_gemm_entries(int64_t k, int ta, const void* A_rows, int64_t lda,
                      int tb, const void* B, int64_t ldb, int op_b,
                      double sa, double sb, int64_t cnt,
                      const int64_t* slot, const int64_t* col, double* out)
 {
-    if (k < 0 || cnt < 0) return -1;
-#pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t t = 0; t < cnt; ++t) {
-        double acc = 0.0;
-        for (int64_t p = 0; p < k; ++p)              /* p ascending */
-            acc += dec_at(ta, A_rows, slot[t] * lda + p) * b_at(tb, B, ldb, op_b, p, col[t]);
-        out[t] = (sa * sb) * acc;
-    }
-    return 0;
+    return entries_impl(k, ta, A_rows, lda, tb, B, ldb, op_b, sa, sb, 0, cnt, slot, col, out);
+}
+
+int orc_gemm_abs_entries(int64_t k, int ta, const void* A_rows, int64_t lda,
+                         int tb, const void* B, int64_t ldb, int op_b,
+                         double sa, double sb, int64_t cnt,
+                         const int64_t* slot, const int64_t* col, double* out)
+{
+    return entries_impl(k, ta, A_rows, lda, tb, B, ldb, op_b, sa, sb, 1, cnt, slot, col, out);
 }
 
 /* ---- O2: bias broadcast ---------------------------------------------------

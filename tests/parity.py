@@ -2,11 +2,25 @@
 inputs, run the CPU oracle on the very same bytes read back from the device,
 and compare.
 
-Tolerances (relative Frobenius error of D against the unrounded float64
-oracle result):  fp32 output with fp32/fp16/bf16 inputs 1e-5; fp16/bf16
-output 5e-3; fp8-e4m3 inputs 5e-2.  The ReLU mask must match bit for bit
-except where |pre-activation| < 1e-3*sqrt(k), where the fp32 accumulation
-order may flip the sign.
+Two gates, both applied to every compared output element:
+
+* the relative Frobenius error of D against the unrounded float64 oracle
+  result: fp32 output 1e-5; fp16/bf16 output 5e-3.  fp8-e4m3 inputs are held
+  to the same output-dtype tolerance here, because the oracle is the exact
+  product of the quantised codes (the contract's looser 5e-2 bounds the error
+  against the unquantised draw, which is reported, not gated);
+* a bound on each element: the standard forward error bound of a dot product
+  in fp32 (Higham, "Accuracy and Stability of Numerical Algorithms", section
+  3.1: |fl(a.b) - a.b| <= gamma_n |a|.|b|, gamma_n = n u / (1 - n u)) with
+  u = 2^-23 (which covers directed as well as nearest rounding), carried
+  through the bias add and the activation (its Lipschitz constant, plus an
+  allowance for the hardware exp2 / reciprocal evaluation of GELU and Tanh),
+  then the output rounding u_out |Y|.  |a|.|b| comes from the oracle's
+  gemm_abs on the same codes.  A localised error -- one tile, one row's bias,
+  a small-|Y| region -- fails this even where the norm would hide it.
+
+The ReLU mask must match bit for bit except where |pre-activation| <
+1e-3*sqrt(k), where the fp32 accumulation order may flip the sign.
 """
 from __future__ import annotations
 
@@ -24,11 +38,66 @@ ESZ = synth.ELEM_SIZE
 
 
 def tolerance(in_dt: str, out_dt: str) -> float:
-    if in_dt == "e4m3":
-        return 5e-2
+    """Relative Frobenius tolerance.  fp8 inputs: the output dtype's (the
+    oracle is exact on the codes; see the module docstring)."""
     if out_dt == "f32":
         return 1e-5
     return 5e-3
+
+
+# contract tolerance for fp8 inputs against the unquantised inputs (reported)
+FP8_CONTRACT_TOL = 5e-2
+
+# ---- the per-element bound --------------------------------------------------------
+U32 = 2.0 ** -23                     # fp32 unit roundoff, any rounding direction
+U_OUT = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# below the output's smallest normal (or subnormal) a rounding or a flush to
+# zero may cost this much absolutely
+TINY = {"f32": 2.0 ** -125, "f16": 2.0 ** -24, "bf16": 2.0 ** -125}
+# Lipschitz constants of the activations: max |GELU'(x)| of the tanh form is
+# 1.1289 (at x ~ 2.4); ReLU, identity and tanh are 1-Lipschitz
+LIPSCHITZ = {"gelu_bias": 1.13, "gelu_aux_bias": 1.13}
+# allowance for the hardware evaluation of GELU / GELU' / tanh in fp32
+# (v_exp_f32, v_rcp_f32, the device tanhf), per unit of (1 + |x|)
+ACT_EVAL = 2.0 ** -16
+
+
+def gamma(n: int) -> float:
+    return n * U32 / (1.0 - n * U32)
+
+
+def elem_bound(w, Y, P_or_C1, G, extra_mag, C_prod=None, unfused=False, grad_f=None, aux_pre=None):
+    """Largest |D - Y| the arithmetic allows at each element.
+
+    G: |s| |A|.|B| at the same elements; extra_mag: |beta C| + |bias| (the
+    other terms of the pre-activation); C_prod: the scaled product alone (the
+    unfused pair rounds it to D's dtype before the second kernel); grad_f: the
+    backward factor of DRELU/DGELU; aux_pre: DGELU's decoded aux P."""
+    u_out = U_OUT[w.out_dtype]
+    n_ops = max(w.k, 1) + 8
+    E = gamma(n_ops) * (G + extra_mag)
+    if unfused and C_prod is not None:
+        E = E + u_out * (np.abs(C_prod) + gamma(n_ops) * G)
+    ep = w.epilog
+    if ep in ("drelu", "drelu_bgrad"):
+        Ey = E
+    elif ep in ("dgelu", "dgelu_bgrad"):
+        Ey = 1.13 * E + np.abs(P_or_C1) * ACT_EVAL * (1.0 + np.abs(aux_pre)) ** 2 + U32 * np.abs(Y)
+    else:
+        L = LIPSCHITZ.get(ep, 1.0)
+        Ey = L * E
+        if ep in ("gelu_bias", "gelu_aux_bias", "tanh_bias"):
+            Ey = Ey + ACT_EVAL * (1.0 + np.abs(P_or_C1))
+    return u_out * np.abs(Y) + (1.0 + u_out) * Ey + TINY[w.out_dtype]
+
+
+def check_elems(D, Y, bound, what, desc):
+    bad = np.abs(D - Y) > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5].tolist()
+        worst = float(np.max(np.abs(D - Y) / bound))
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside the per-element bound "
+                             f"(worst {worst:.2f}x the bound; first at {idx}): {desc}")
 
 
 def codes(t: torch.Tensor) -> np.ndarray:
@@ -169,27 +238,53 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
         g.free()
 
 
-def oracle_full(w: synth.Workload, r: Result):
-    """The oracle's plain sequence on the bytes the library consumed."""
+def oracle_parts(w: synth.Workload, r: Result) -> Result:
+    """The oracle's plain sequence on the bytes the library consumed, with
+    the intermediate values the checks need: C (the scaled product), C1 (plus
+    beta*C), P (plus bias), Y (the expected output), M (the mask words), G
+    (|s| |A|.|B|), extra (|beta C| + |bias| per element) and, for the
+    backward epilogues, the aux values they read."""
     a_dt, d_dt = w.in_dtype, w.out_dtype
     Ac = codes(r.A).ravel()
     Bc = codes(r.B).ravel()
     sa = float(r.sa.item()) if r.sa is not None else 1.0
     sb = float(r.sb.item()) if r.sb is not None else 1.0
     C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+    G = oracle.gemm_abs(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+    C1 = C
+    extra = np.zeros_like(C)
     if getattr(r, "cin", None) is not None and r.beta != 0.0:
-        C = oracle.add_beta_c(C, r.beta, codes(r.cin), d_dt)
+        C1 = oracle.add_beta_c(C, r.beta, codes(r.cin), d_dt)
+        extra = extra + np.abs(C1 - C)
+    out = Result(C=C, C1=C1, G=G, extra=extra, M=None, aux_pre=None)
     if base_grad(w.epilog) == "drelu":
-        return oracle.drelu_pass(C, codes(r.aux)), C, None
+        out.Y = oracle.drelu_pass(C1, codes(r.aux))
+        out.P = C1
+        return out
     if base_grad(w.epilog) == "dgelu":
-        return oracle.dgelu_pass(C, codes(r.aux), d_dt), C, None
+        aux_c = codes(r.aux)
+        out.Y = oracle.dgelu_pass(C1, aux_c, d_dt)
+        out.P = C1
+        out.aux_pre = oracle.decode(np.ascontiguousarray(aux_c[:, : w.n]), d_dt)
+        return out
     if w.epilog == "none":
-        P = C
+        P = C1
     else:
-        P = oracle.bias_pass(C, codes(r.bias), d_dt, w.axis)
-    Y = oracle.act_pass(P, w.epilog)
-    M = oracle.mask_pass(P, r.ldw) if w.epilog == "relu_aux_bias" else None
-    return Y, P, M
+        P = oracle.bias_pass(C1, codes(r.bias), d_dt, w.axis)
+        out.extra = out.extra + np.abs(P - C1)
+    out.P = P
+    out.Y = oracle.act_pass(P, w.epilog)
+    out.M = oracle.mask_pass(P, r.ldw) if w.epilog == "relu_aux_bias" else None
+    return out
+
+
+def oracle_full(w: synth.Workload, r: Result):
+    """(Y, P, M) of the oracle's plain sequence; for the backward epilogues
+    (Y, C, None)."""
+    o = oracle_parts(w, r)
+    if w.epilog in GRAD_EPILOGS:
+        return o.Y, o.C1, None
+    return o.Y, o.P, o.M
 
 
 def decode_output(w: synth.Workload, r: Result) -> np.ndarray:
@@ -197,14 +292,27 @@ def decode_output(w: synth.Workload, r: Result) -> np.ndarray:
     return oracle.decode(np.ascontiguousarray(Dc[:, : w.n]), w.out_dtype)
 
 
+def is_unfused(r: Result) -> bool:
+    return "unfused=1" in r.desc
+
+
 def check_full(w: synth.Workload, r: Result, tol: Optional[float] = None):
-    """Compare every output element, the untouched padding and the mask."""
-    Y, P, M = oracle_full(w, r)
+    """Compare every output element (relative Frobenius error and the
+    per-element bound), the untouched padding and the mask."""
+    o = oracle_parts(w, r)
+    Y, P, M = o.Y, o.P, o.M
     Dd = decode_output(w, r)
     assert np.isfinite(Dd).all(), f"non-finite outputs ({np.isnan(Dd).sum()} NaN): {r.desc}"
     tol = tolerance(w.in_dtype, w.out_dtype) if tol is None else tol
     err = rel_fro(Dd, Y)
     assert err <= tol, f"rel-Frobenius error {err:.3e} > {tol:.1e}: {r.desc}"
+    bound = elem_bound(w, Y, P, o.G, o.extra, C_prod=o.C, unfused=is_unfused(r), aux_pre=o.aux_pre)
+    check_elems(Dd, Y, bound, "D", r.desc)
+    if base_grad(w.epilog) == "drelu":
+        # a cleared mask bit selects an exact zero, whatever the product
+        # (Y == 0 with a non-zero product can only come from a cleared bit)
+        cleared = (Y == 0.0) & (o.C1 != 0.0)
+        assert (Dd[cleared] == 0.0).all(), f"DRELU: a masked entry is not zero: {r.desc}"
     # padding columns of D are never written
     if r.ldd > w.n:
         pad = codes(r.D)[:, w.n:]
@@ -215,24 +323,35 @@ def check_full(w: synth.Workload, r: Result, tol: Optional[float] = None):
     if M is not None:
         check_mask(w, codes(r.aux), M, P)
     if w.epilog == "gelu_aux_bias":
-        check_pre_aux(w, r, P, tol)
+        check_pre_aux(w, r, P, tol, o)
     if w.epilog in BGRAD_EPILOGS:
-        check_bgrad(w, r, Y, tol)
+        check_bgrad(w, r, Y, tol, bound)
     return err
 
 
-def check_bgrad(w, r, Y, tol):
+def check_bgrad(w, r, Y, tol, bound=None):
     """The bias gradient written to the bias pointer against the oracle's O8
-    on the unrounded backward result."""
+    on the unrounded backward result; per entry, the sum of the summed
+    elements' bounds plus the fp32 summation's own rounding."""
     want = oracle.bgrad_pass(Y, w.axis)
     got = oracle.decode(np.ascontiguousarray(codes(r.bias)), w.out_dtype)
     assert np.isfinite(got).all(), f"bias gradient not written everywhere: {r.desc}"
     err = rel_fro(got, want)
     assert err <= tol, f"bias gradient rel-Frobenius {err:.3e} > {tol:.1e}: {r.desc}"
+    if bound is not None:
+        ax = 1 if w.axis == "row" else 0
+        length = w.n if w.axis == "row" else w.m
+        u_out = U_OUT[w.out_dtype]
+        # the elements' own errors before their rounding (the unfused pair
+        # sums the rounded D, the fused kernel the fp32 values), then the sum
+        per_elem = bound if is_unfused(r) else bound - u_out * np.abs(Y)
+        Eg = per_elem.sum(axis=ax) + gamma(length + 8) * (np.abs(Y) + per_elem).sum(axis=ax)
+        gb = u_out * np.abs(want) + (1.0 + u_out) * Eg + TINY[w.out_dtype]
+        check_elems(got, want, gb, "bias gradient", r.desc)
     return err
 
 
-def check_pre_aux(w, r, P, tol):
+def check_pre_aux(w, r, P, tol, o=None):
     """GELU_AUX_BIAS: the aux matrix holds P in D's dtype; its padding
     columns are never written."""
     Ac = codes(r.aux)
@@ -240,6 +359,10 @@ def check_pre_aux(w, r, P, tol):
     assert np.isfinite(Pd).all(), "non-finite pre-activation aux"
     err = rel_fro(Pd, P)
     assert err <= tol, f"aux pre-activation rel-Frobenius {err:.3e} > {tol:.1e}: {r.desc}"
+    if o is not None:
+        pw = synth.dataclasses.replace(w, epilog="bias")   # P's bound: no activation
+        check_elems(Pd, P, elem_bound(pw, P, P, o.G, o.extra, C_prod=o.C, unfused=is_unfused(r)),
+                    "aux pre-activation", r.desc)
     if Ac.shape[1] > w.n:
         pad = np.ascontiguousarray(Ac[:, w.n:])
         dec = pad if w.out_dtype == "f32" else oracle.decode(pad, w.out_dtype)
@@ -294,6 +417,9 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     Ce = oracle.gemm_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej,
                              np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
                              w.op_b, sa, sb)
+    Ge = oracle.gemm_abs_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej,
+                                 np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
+                                 w.op_b, sa, sb)
     grad = w.epilog in GRAD_EPILOGS
     Pe = Ce if (w.epilog == "none" or grad) else oracle.bias_entries(Ce, ei, ej, bias_c, d_dt, w.axis)
     Ye = grad_entries(w, r, Ce, ei, ej) if grad else oracle.act_pass(Pe, w.epilog)
@@ -305,6 +431,8 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     Ar = np.ascontiguousarray(A_rows[rslots][:, : w.k])
     Cr = oracle.gemm(Ar, a_dt, np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
                      w.op_b, sa, sb)
+    Gr = oracle.gemm_abs(Ar, a_dt, np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
+                         w.op_b, sa, sb)
     ri = np.repeat(rows, w.n)
     rj = np.tile(np.arange(w.n), len(rows))
     if w.epilog == "none" or grad:
@@ -324,6 +452,22 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     err_e = rel_fro(De, Ye)
     err_r = rel_fro(Dr, Yr)
     assert err_e <= tol and err_r <= tol, f"rel-Frobenius {err_e:.3e} / {err_r:.3e} > {tol:.1e}: {r.desc}"
+    # the per-element bound at the sampled entries and on the full rows
+    unf = is_unfused(r)
+    if grad:
+        pre_e = pre_r = None
+        if base_grad(w.epilog) == "dgelu":
+            aux_e = codes(r.aux.index_select(0, torch.from_numpy(ei).to(r.aux.device)))[np.arange(len(ej)), ej]
+            pre_e = oracle.decode(np.ascontiguousarray(aux_e), d_dt)
+            pre_r = oracle.decode(np.ascontiguousarray(
+                codes(r.aux.index_select(0, torch.from_numpy(rows).to(r.aux.device)))[:, : w.n]), d_dt)
+        be = elem_bound(w, Ye, Ce, Ge, np.zeros_like(Ce), C_prod=Ce, unfused=unf, aux_pre=pre_e)
+        br = elem_bound(w, Yr, Cr, Gr, np.zeros_like(Cr), C_prod=Cr, unfused=unf, aux_pre=pre_r)
+    else:
+        be = elem_bound(w, Ye, Pe, Ge, np.abs(Pe - Ce), C_prod=Ce, unfused=unf)
+        br = elem_bound(w, Yr, Pr, Gr, np.abs(Pr - Cr), C_prod=Cr, unfused=unf)
+    check_elems(De, Ye, be, "D (sampled entries)", r.desc)
+    check_elems(Dr, Yr, br, "D (full rows)", r.desc)
     if exact:
         want_e = oracle.encode(Ye, d_dt) if d_dt != "f32" else Ye.astype(np.float32)
         assert np.array_equal(De_all[np.arange(len(ej)), ej], want_e), "integer case not bit-exact"
@@ -345,6 +489,13 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
         band = 1e-3 * math.sqrt(w.k)
         bad = (bits.astype(bool) != (Pe > 0)) & (np.abs(Pe) >= band)
         assert not bad.any(), f"{int(bad.sum())} sampled mask bits differ outside the band"
+        if exact:
+            # integer inputs: P is exact, so every bit equals (P > 0), ties
+            # (P == 0 -> 0) included, and the case must contain ties
+            ties = int((Pr == 0).sum() + (Pe == 0).sum())
+            assert ties > 50, f"only {ties} sampled entries with P == 0"
+            assert band_mis == 0, f"{band_mis} mask bits of the full rows differ from (P > 0)"
+            assert np.array_equal(bits.astype(bool), Pe > 0), "sampled mask bits differ from (P > 0)"
     return err_e, err_r, band_mis
 
 

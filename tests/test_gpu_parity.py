@@ -285,3 +285,58 @@ def test_split_k_tile_unfused_and_repeated_calls():
         check_full(w, r)
     r = run_library(w, inp, path=1, tile=14, split_k=8, unfused=1)
     check_full(w, r)
+
+
+# ---- the mask's tie rule: P == 0 gives bit 0 ---------------------------------------
+def int_inputs(w, lo=-2, hi=2, blo=-8, bhi=8, seed=31):
+    """Small-integer operands and bias: every fp32 partial sum and the
+    pre-activation are exact in any order, so P == 0 happens often and the
+    mask must equal (P > 0) everywhere, ties included."""
+    inp = synth.make_inputs(w, a_dist=("int", lo, hi), b_dist=("int", lo, hi), bias_dist=("int", blo, bhi))
+    if w.in_dtype == "e4m3":
+        g = torch.Generator().manual_seed(seed)
+        inp.A = torch.randint(lo, hi + 1, (w.m, w.k), generator=g).float().to(torch.float8_e4m3fn)
+        shape = (w.n, w.k) if w.op_b else (w.k, w.n)
+        inp.B = torch.randint(lo, hi + 1, shape, generator=g).float().to(torch.float8_e4m3fn)
+        inp.scale_a = torch.ones(1)
+        inp.scale_b = torch.ones(1)
+    return inp
+
+
+def assert_mask_exact_with_ties(w, r):
+    from parity import oracle_full
+    Y, P, M = oracle_full(w, r)
+    ties = int((P == 0.0).sum())
+    assert ties > 50, f"only {ties} entries with P == 0: the case does not test the tie rule"
+    got = codes(r.aux)
+    assert np.array_equal(got, M), (
+        f"{int((np.unpackbits(got.view(np.uint8)) != np.unpackbits(M.view(np.uint8))).sum())} mask bits "
+        f"differ from (P > 0) ({ties} ties): {r.desc}")
+    assert np.array_equal(codes(r.D)[:, : w.n], oracle.encode(Y, "bf16").reshape(Y.shape)), r.desc
+
+
+@pytest.mark.parametrize("tile,a", [(1, "bf16"), (11, "bf16"), (13, "bf16"), (15, "bf16"),
+                                    (15, "e4m3"), (11, "e4m3"), (14, "bf16")])
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_relu_aux_tie_rule_tiles(tile, a, op_b):
+    w = wl(300, 520, 200 if a == "bf16" else 456, a, "bf16", "relu_aux_bias", "row", op_b, seed=tile)
+    r = run_library(w, int_inputs(w), path=1, tile=tile, split_k=3 if tile == 14 else 0)
+    assert f"tile_id={tile} " in r.desc
+    assert_mask_exact_with_ties(w, r)
+
+
+@pytest.mark.parametrize("split", [0, 4])
+def test_relu_aux_tie_rule_smallm(split):
+    w = wl(16, 520, 1024, "bf16", "bf16", "relu_aux_bias", "col", 1)
+    r = run_library(w, int_inputs(w, -1, 1), path=2, split_k=split)
+    assert "path=smallm" in r.desc
+    assert_mask_exact_with_ties(w, r)
+
+
+def test_relu_aux_tie_rule_unfused():
+    # the pair rounds the product to bf16 first: integers up to 256 in
+    # magnitude stay exact (|C| <= 200 * 4 = 800 would not, so k is small)
+    w = wl(300, 520, 16, "bf16", "bf16", "relu_aux_bias", "row", 0)
+    r = run_library(w, int_inputs(w), unfused=1)
+    assert "unfused=1" in r.desc
+    assert_mask_exact_with_ties(w, r)

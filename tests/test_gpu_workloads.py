@@ -42,3 +42,16 @@ def test_c4_shape_integer_bit_exact():
     check_sampled(w, r, 77, exact=True)
     del r
     torch.cuda.empty_cache()
+
+
+def test_c4_shape_relu_aux_tie_rule_integer():
+    """RELU_AUX_BIAS at the 8192^3 shape with integer inputs: P is exact, so
+    every sampled mask bit must equal (P > 0), the P == 0 ties included."""
+    w = synth.WORKLOADS["C4"]
+    inp = synth.make_inputs(w, device="cuda", a_dist=("int", -1, 1), b_dist=("int", -1, 1),
+                            bias_dist=("int", -40, 40))
+    r = run_library(w, inp, poison=False)
+    del inp
+    check_sampled(w, r, 78, exact=True)
+    del r
+    torch.cuda.empty_cache()

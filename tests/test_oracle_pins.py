@@ -231,6 +231,65 @@ def test_p8_tanh_form_close_to_erf_form():
     assert 2.4 < abs(xs[np.abs(d).argmax()]) < 3.0
 
 
+def test_p8_gelu_forms_match_library_routines():
+    """Both GELU forms at fixed points against independent library routines:
+    the erf form is x * Phi(x) with Phi the standard normal CDF (scipy's
+    ndtr), and both forms are PyTorch's float64 GELU (its default is the erf
+    form, approximate='tanh' the tanh form the pages' Linear+GELU uses).  A
+    wrong argument scale (erf(x/2) for erf(x/sqrt 2)), a wrong cubic
+    coefficient or a misplaced sqrt(2/pi) moves values by far more than the
+    1e-13 allowed."""
+    from scipy.special import ndtr
+    xs = np.concatenate([np.linspace(-8.0, 8.0, 641), [-2.7, -1.0, -0.5, 0.25, 1.0, 1.96, 3.0]])
+    t = torch.tensor(xs, dtype=torch.float64)
+    erf_lib = torch.nn.functional.gelu(t).numpy()
+    tanh_lib = torch.nn.functional.gelu(t, approximate="tanh").numpy()
+    for x, e, th in zip(xs, erf_lib, tanh_lib):
+        ge = oracle.act1(x, "gelu_erf")
+        gt = oracle.act1(x, "gelu_bias")
+        assert abs(ge - x * ndtr(x)) <= 1e-13 * max(1.0, abs(x)), x
+        assert abs(ge - e) <= 1e-13 * max(1.0, abs(x)), x
+        assert abs(gt - th) <= 1e-13 * max(1.0, abs(x)), x
+
+
+def test_p8_gelu_deriv_matches_autograd():
+    """GELU' of the tanh form against PyTorch's float64 autograd of its tanh
+    GELU (a library derivative, independent of the oracle's product- and
+    chain-rule expression)."""
+    xs = np.linspace(-8.0, 8.0, 321)
+    t = torch.tensor(xs, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.gelu(t, approximate="tanh").sum().backward()
+    for x, gref in zip(xs, t.grad.numpy()):
+        assert abs(oracle.gelu_deriv(x) - gref) <= 1e-13, x
+
+
+# ---- the magnitude term of the element-wise error bound ---------------------------
+def test_gemm_abs_pins():
+    """|A|.|B| (the magnitude term of the dot-product error bound): equal to
+    the product for non-negative operands, unchanged by flipping the signs of
+    rows of A or of B, never below |A.B| (triangle inequality), numpy's
+    float64 matmul of the absolute values on a random case, and the scale
+    enters as its absolute value."""
+    rng = np.random.default_rng(3)
+    A = f32(rng.standard_normal((7, 11)))
+    B = f32(rng.standard_normal((11, 5)))
+    G = oracle.gemm_abs(A, "f32", B, "f32")
+    assert np.array_equal(G, np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64)))
+    Ap, Bp = f32(np.abs(A)), f32(np.abs(B))
+    assert np.array_equal(oracle.gemm_abs(Ap, "f32", Bp, "f32"), oracle.gemm(Ap, "f32", Bp, "f32"))
+    flipA = f32(A * np.where(np.arange(7) % 2 == 0, -1.0, 1.0)[:, None])
+    flipB = f32(B * np.where(np.arange(11) % 3 == 0, -1.0, 1.0)[:, None])
+    assert np.array_equal(oracle.gemm_abs(flipA, "f32", flipB, "f32"), G)
+    assert (np.abs(oracle.gemm(A, "f32", B, "f32")) <= G).all()
+    assert np.allclose(oracle.gemm_abs(A, "f32", B, "f32", sa=-2.0, sb=0.5), G, rtol=0, atol=0)
+    # the transposed layout of B and the entry form agree with the whole form
+    Bt = f32(B.T)
+    assert np.array_equal(oracle.gemm_abs(A, "f32", Bt, "f32", op_b=1), G)
+    rows, cols = np.array([0, 3, 6, 6]), np.array([4, 0, 2, 4])
+    e = oracle.gemm_abs_entries(A, "f32", rows, cols, B, "f32")
+    assert np.array_equal(e, G[rows, cols])
+
+
 # ---- P9: e4m3 codec ---------------------------------------------------------------------
 def test_p9_e4m3_spec_points():
     spec = json.load(open(os.path.join(GOLDEN, "e4m3_spec.json")))
