@@ -79,6 +79,11 @@ def lib():
                                        vp, i64, ctypes.c_int, dbl, dbl, i64,
                                        vp, vp, vp]
         L.orc_gemm_abs.argtypes = L.orc_gemm.argtypes
+        L.orc_gemm_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64,
+                                  ctypes.c_int, vp, i64, ctypes.c_int, vp, i64, dbl, dbl, vp]
+        L.orc_gemm_mx_abs.argtypes = L.orc_gemm_mx.argtypes
+        L.orc_dec_e8m0.restype = dbl
+        L.orc_dec_e8m0.argtypes = [ctypes.c_uint8]
         L.orc_gemm_abs_entries.argtypes = L.orc_gemm_entries.argtypes
         L.orc_bias.argtypes = [i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, vp]
         L.orc_bias_entries.argtypes = [i64, vp, vp, vp, ctypes.c_int,
@@ -166,6 +171,39 @@ def gemm_abs(A: np.ndarray, ta: str, B: np.ndarray, tb: str, op_b: int = 0,
     """|sa*sb| * |A| @ |B|: the magnitude term of the dot-product rounding
     error bound (Higham, section 3.1), same arguments as gemm."""
     return _gemm_call(lib().orc_gemm_abs, "gemm_abs", A, ta, B, tb, op_b, sa, sb, m, n, k, lda, ldb)
+
+
+def _gemm_mx_call(fn, what, A, ta, SA, B, tb, SB, op_b, sa, sb):
+    A = _codes(A, ta)
+    B = _codes(B, tb)
+    SA = np.ascontiguousarray(SA, dtype=np.uint8)
+    SB = np.ascontiguousarray(SB, dtype=np.uint8)
+    m, k = A.shape
+    n = B.shape[0] if op_b else B.shape[1]
+    kb = (k + 31) // 32
+    if SA.shape[0] != m or SB.shape[0] != n or SA.shape[1] < kb or SB.shape[1] < kb:
+        raise ValueError(f"oracle {what}: block scales must be m x >=ceil(k/32) and n x >=ceil(k/32)")
+    C = np.empty((m, n), dtype=np.float64)
+    _check(fn(m, n, k, DTYPES[ta], _ptr(A), A.shape[1], _ptr(SA), SA.shape[1], DTYPES[tb], _ptr(B),
+              B.shape[1], int(op_b), _ptr(SB), SB.shape[1], float(sa), float(sb), _ptr(C)), what)
+    return C
+
+
+def gemm_mx(A, ta, SA, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
+    """O1x: the product with one E8M0 scale per 32 K values: SA (m x
+    >=ceil(k/32) bytes) for the rows of A, SB (n x >=ceil(k/32) bytes) for the
+    columns of B (K blocks contiguous per column, whichever layout B has)."""
+    return _gemm_mx_call(lib().orc_gemm_mx, "gemm_mx", A, ta, SA, B, tb, SB, op_b, sa, sb)
+
+
+def gemm_mx_abs(A, ta, SA, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
+    """gemm_mx over absolute values (the error bound's magnitude term)."""
+    return _gemm_mx_call(lib().orc_gemm_mx_abs, "gemm_mx_abs", A, ta, SA, B, tb, SB, op_b, sa, sb)
+
+
+def dec_e8m0(e: int) -> float:
+    """An E8M0 scale: 2^(e - 127), NaN for 0xFF."""
+    return lib().orc_dec_e8m0(int(e))
 
 
 def _entries_call(fn, what, A_rows, ta, slot, cols, B, tb, op_b, sa, sb):

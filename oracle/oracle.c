@@ -280,6 +280,67 @@ int orc_gemm_abs_entries(int64_t k, int ta, const void* A_rows, int64_t lda,
     return entries_impl(k, ta, A_rows, lda, tb, B, ldb, op_b, sa, sb, 1, cnt, slot, col, out);
 }
 
+/* ---- O1x: the product with per-block scales (block-scaled fp8) ------------
+ * The nvmath page names FP8 among the supported input types and, in its
+ * closing paragraph, low-precision formats as where the fused epilogue is
+ * going.  Beyond one scale per tensor, the OCP Microscaling (MX) format
+ * gives every run of 32 consecutive elements along K its own scale: an E8M0
+ * value, an 8-bit biased exponent with no sign and no mantissa, scale =
+ * 2^(e - 127), the code 0xFF being NaN.  With SA one scale per (row i of A,
+ * block b = p / 32) and SB one per (column j of B, block b):
+ *
+ *   C[i][j] = sa*sb * sum_p  (dec(A[i][p]) * 2^(SA[i][p/32] - 127))
+ *                          * (dec(B[p][j]) * 2^(SB[j][p/32] - 127))
+ *
+ * SA is m x ceil(k/32) bytes with row stride ldsa; SB is n x ceil(k/32)
+ * bytes (the blocks of column j contiguous, whichever layout B has) with
+ * row stride ldsb.  absval = 1 gives the same sum over absolute values (the
+ * magnitude term of the error bound, see gemm_impl). */
+double orc_dec_e8m0(uint8_t e)
+{
+    if (e == 0xFFu) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+static int gemm_mx_impl(int64_t m, int64_t n, int64_t k,
+                        int ta, const void* A, int64_t lda, const uint8_t* SA, int64_t ldsa,
+                        int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB, int64_t ldsb,
+                        double sa, double sb, int absval, double* C)
+{
+    if (m < 0 || n < 0 || k < 0) return -1;
+    const int64_t kb = (k + 31) / 32;
+    if (ldsa < kb || ldsb < kb) return -1;
+    const double s = absval ? fabs(sa * sb) : sa * sb;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int64_t p = 0; p < k; ++p) {           /* p ascending */
+                const double a = dec_at(ta, A, i * lda + p) * orc_dec_e8m0(SA[i * ldsa + p / 32]);
+                const double b = b_at(tb, B, ldb, op_b, p, j) * orc_dec_e8m0(SB[j * ldsb + p / 32]);
+                acc += opnd(a, absval) * opnd(b, absval);
+            }
+            C[i * n + j] = s * acc;
+        }
+    }
+    return err;
+}
+
+int orc_gemm_mx(int64_t m, int64_t n, int64_t k, int ta, const void* A, int64_t lda, const uint8_t* SA,
+                int64_t ldsa, int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB, int64_t ldsb,
+                double sa, double sb, double* C)
+{
+    return gemm_mx_impl(m, n, k, ta, A, lda, SA, ldsa, tb, B, ldb, op_b, SB, ldsb, sa, sb, 0, C);
+}
+
+int orc_gemm_mx_abs(int64_t m, int64_t n, int64_t k, int ta, const void* A, int64_t lda, const uint8_t* SA,
+                    int64_t ldsa, int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB, int64_t ldsb,
+                    double sa, double sb, double* G)
+{
+    return gemm_mx_impl(m, n, k, ta, A, lda, SA, ldsa, tb, B, ldb, op_b, SB, ldsb, sa, sb, 1, G);
+}
+
 /* ---- O2: bias broadcast ---------------------------------------------------
  * ROW: the bias has one value per output row (shape (m,) or (m,1)) and is
  * added to every column ([epilog page], paragraph on epilog_inputs: the bias

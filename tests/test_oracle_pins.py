@@ -512,3 +512,77 @@ def test_add_beta_c_exact_cases(dt):
     assert np.array_equal(oracle.add_beta_c(Z, 2.5, codes, dt), 2.5 * Cin[:, :n].astype(np.float64))
     d = oracle.add_beta_c(Z, 3.0, codes, dt) - oracle.add_beta_c(Z, 1.0, codes, dt)
     assert np.array_equal(d, 2.0 * Cin[:, :n].astype(np.float64))
+
+
+# ---- O1x: block-scaled fp8 (one E8M0 scale per 32 K values) --------------------------
+def e4m3_codes_of_ints(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e8m0_codec_from_the_format_definition():
+    """E8M0 (OCP Microscaling formats): an unsigned 8-bit exponent, bias 127,
+    no mantissa; 0xFF is NaN."""
+    assert oracle.dec_e8m0(127) == 1.0
+    assert oracle.dec_e8m0(128) == 2.0 and oracle.dec_e8m0(126) == 0.5
+    assert oracle.dec_e8m0(0) == 2.0 ** -127 and oracle.dec_e8m0(254) == 2.0 ** 127
+    assert math.isnan(oracle.dec_e8m0(255))
+
+
+def test_mx_unit_scales_reduce_to_the_per_tensor_product():
+    rng = np.random.default_rng(11)
+    m, n, k = 7, 9, 100                      # a ragged last block of 4
+    A = e4m3_codes_of_ints(rng.integers(-6, 7, (m, k)))
+    for op_b in (0, 1):
+        B = e4m3_codes_of_ints(rng.integers(-6, 7, (n, k) if op_b else (k, n)))
+        ones_a = np.full((m, 4), 127, np.uint8)
+        ones_b = np.full((n, 4), 127, np.uint8)
+        C = oracle.gemm_mx(A, "e4m3", ones_a, B, "e4m3", ones_b, op_b, 0.5, 3.0)
+        assert np.array_equal(C, oracle.gemm(A, "e4m3", B, "e4m3", op_b, 0.5, 3.0))
+
+
+def test_mx_power_of_two_scales_exact_on_integer_codes_brute_force():
+    """Integer codes times powers of two are exact in float64, so the whole
+    sum is: compare with exact rational arithmetic on tiny shapes."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    for m, n, k in itertools.product((1, 2, 3), (1, 2, 5), (1, 31, 32, 33, 70)):
+        kb = (k + 31) // 32
+        Ai = rng.integers(-8, 9, (m, k))
+        Bi = rng.integers(-8, 9, (k, n))
+        SA = rng.integers(117, 138, (m, kb)).astype(np.uint8)
+        SB = rng.integers(117, 138, (n, kb)).astype(np.uint8)
+        C = oracle.gemm_mx(e4m3_codes_of_ints(Ai), "e4m3", SA, e4m3_codes_of_ints(Bi), "e4m3", SB)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(int(Ai[i, p]) * int(Bi[p, j])) *
+                            Fraction(2) ** (int(SA[i, p // 32]) + int(SB[j, p // 32]) - 254) for p in range(k))
+                assert C[i, j] == float(exact), (m, n, k, i, j)
+
+
+def test_mx_block_index_and_layouts():
+    """Raising one scale of row i, block b by one (x2) adds exactly block b's
+    share of row i; B given n x k with the same SB gives the same product; a
+    NaN scale (0xFF) poisons only the row it belongs to; the absolute form
+    bounds the product."""
+    rng = np.random.default_rng(13)
+    m, n, k = 4, 6, 96
+    Ai = rng.integers(-5, 6, (m, k))
+    Bi = rng.integers(-5, 6, (k, n))
+    A, Bn, Bt = e4m3_codes_of_ints(Ai), e4m3_codes_of_ints(Bi), e4m3_codes_of_ints(Bi.T)
+    SA = rng.integers(120, 135, (m, 3)).astype(np.uint8)
+    SB = rng.integers(120, 135, (n, 3)).astype(np.uint8)
+    C = oracle.gemm_mx(A, "e4m3", SA, Bn, "e4m3", SB, 0)
+    assert np.array_equal(C, oracle.gemm_mx(A, "e4m3", SA, Bt, "e4m3", SB, 1))
+    SA2 = SA.copy()
+    SA2[2, 1] += 1
+    C2 = oracle.gemm_mx(A, "e4m3", SA2, Bn, "e4m3", SB, 0)
+    share = np.array([sum(Ai[2, p] * Bi[p, j] * 2.0 ** (int(SA[2, 1]) + int(SB[j, 1]) - 254)
+                          for p in range(32, 64)) for j in range(n)])
+    assert np.array_equal(C2[2] - C[2], share)
+    assert np.array_equal(np.delete(C2, 2, 0), np.delete(C, 2, 0))
+    SAn = SA.copy()
+    SAn[1, 0] = 0xFF
+    Cn = oracle.gemm_mx(A, "e4m3", SAn, Bn, "e4m3", SB, 0)
+    assert np.isnan(Cn[1]).all() and np.isfinite(np.delete(Cn, 1, 0)).all()
+    G = oracle.gemm_mx_abs(A, "e4m3", SA, Bn, "e4m3", SB, 0)
+    assert (np.abs(C) <= G).all()
