@@ -143,12 +143,19 @@ bool smallm_supported(const ge_desc& d) {
 // split's serial device-scope round trips (partial store, arrival count,
 // reload) only pay off when the column blocks alone leave CUs idle.  Hence:
 // the largest power of two that keeps the grid within one round and each of
-// the 8 waves at four or more 32-wide K steps.
-int smallm_auto_split(int64_t tiles_n, int64_t steps) {
-    constexpr int64_t kCUs = 256, kWaves = 8, kMinStepsPerWave = 4;
+// the 8 waves at two or more 64-wide K spans.
+int smallm_auto_split(int64_t tiles_n, int64_t spans) {
+    constexpr int64_t kCUs = 256, kWaves = 8, kMinSpansPerWave = 2;
     int split = 1;
-    while (tiles_n * split * 2 <= kCUs && steps >= split * 2 * kWaves * kMinStepsPerWave) split *= 2;
+    while (tiles_n * split * 2 <= kCUs && spans >= split * 2 * kWaves * kMinSpansPerWave) split *= 2;
     return split;
+}
+
+// GE_LOG=1 in the environment: every successful plan prints its
+// description (path, tile, grid, split, workspace) to stderr.
+bool plan_log() {
+    const char* e = getenv("GE_LOG");
+    return e && e[0] == '1';
 }
 
 bool test_fail_launch() {
@@ -204,6 +211,12 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
                                       : (int64_t)round_up((size_t)d.n, 128) / 32;
     if (q.ldaux > INT32_MAX) return GE_ERR_SHAPE;
 
+    // a batch takes product z's bias at z * len values: with a column bias
+    // whose n values are not a whole number of 16-byte chunks, every other
+    // product's bias would start misaligned for the kernels' 16-byte loads
+    if (d.batch > 1 && bias_axis == GE_BIAS_COL && has_bias(epilog) && (d.n * elem_size(d.d_type)) % 16 != 0)
+        return GE_ERR_ALIGN;
+
     // the small-m kernel serves the inference epilogues only
     const bool smallm_epilog = epilog <= GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_TANH_BIAS;
     int path = pr.path;
@@ -218,10 +231,11 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.tile_id = 0;
         q.tiles_m = 1;
         q.tiles_n = (int32_t)ceil_div(d.n, 16);
-        const int64_t steps = ceil_div(d.k, 32);
-        int split = pr.split_k > 0 ? pr.split_k : smallm_auto_split(q.tiles_n, steps);
-        if (split > steps) split = steps > 0 ? (int)steps : 1;
-        q.k_per_split = (int32_t)(ceil_div(steps, split) * 32);
+        // K slices of whole 64-element spans (the kernel's load unit)
+        const int64_t spans = ceil_div(d.k, 64);
+        int split = pr.split_k > 0 ? pr.split_k : smallm_auto_split(q.tiles_n, spans);
+        if (split > spans) split = spans > 0 ? (int)spans : 1;
+        q.k_per_split = (int32_t)(ceil_div(spans, split) * 64);
         split = q.k_per_split > 0 ? (int)ceil_div(d.k, q.k_per_split) : 1;
         q.split_k = split;
         q.group_m = 1;
@@ -300,6 +314,11 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     q.planned = true;
     q.pref = pr;
     *h = q;
+    if (plan_log()) {
+        char line[512];
+        gemm_epilog_describe(h, line, sizeof line);
+        fprintf(stderr, "gemm_epilog: plan %s\n", line);
+    }
     return GE_OK;
 }
 
@@ -472,8 +491,8 @@ int gemm_epilog_autotune(ge_handle h, const void* A, const void* B, const void* 
     int cand[kNumTiles + 8];
     int nc = 0;
     if (orig.path == PATH_SMALLM) {
-        const int64_t steps = ceil_div(orig.d.k, 32);
-        for (int s = 1; s <= 64 && s <= (steps > 0 ? steps : 1); s *= 2) cand[nc++] = s;
+        const int64_t spans = ceil_div(orig.d.k, 64);
+        for (int s = 1; s <= 64 && s <= (spans > 0 ? spans : 1); s *= 2) cand[nc++] = s;
     } else {
         for (int i = 0; i < kNumTiles; ++i) cand[nc++] = kTiles[i].id;
     }

@@ -9,22 +9,33 @@
 //
 // Design:
 //  * One workgroup per 16 output columns (16 rows of W) and K slice; its
-//    waves split the slice further.  Lane (r = lane % 16, q = lane / 16)
-//    streams 16-byte chunks of W row n0 + r straight from global memory into
-//    the A operand of v_mfma_f32_16x16x32_{f16,bf16}; the matching chunk of
-//    x row r (L2-resident, read by every workgroup) is the B operand.  Each
-//    lane's chunks for one MFMA step cover 32 consecutive K values of its row
-//    together with the other three q lanes, so each step reads 64 contiguous
-//    bytes per W row.
-//  * Loads are issued `kUnroll` steps ahead of the MFMAs that consume them
-//    (all of a wave's share of W at the batch-16 Linear shape), so the HBM
-//    latency is paid once rather than once per batch.
+//    waves split the slice further, in spans of 64 K values (128 bytes of a
+//    W row).  W is streamed straight from global memory into registers in
+//    whole 128-byte lines: for each span, two load instructions cover the
+//    16 rows, instruction j giving lane l the 16-byte chunk l/8 of row
+//    8j + l%8 (8 lines per instruction).  The MFMA
+//    v_mfma_f32_16x16x32_{f16,bf16} wants lane (r = lane % 16, q = lane / 16)
+//    to hold row r, so a lane holds its own row's chunk 2q + r/8 in register
+//    r/8 and row r^8's chunk in the other register.  Four MFMAs per span,
+//    each with the lanes of one half zeroed, add the matching chunks of x
+//    (the B operand: x row r, chunks 2q and 2q+1, L2-resident): two into the
+//    lane's own row's sums and two into row r^8's, which a lane exchange
+//    (lanes l and l^32 hold rows 4q+i and 4(q^2)+i) adds back at the end.
+//    The MFMA work doubles, but the matrix cores are idle here anyway, while
+//    half-line W requests (16 rows x 64 bytes per instruction) measured 8%
+//    slower on the batch-16 Linear.
+//  * All of a wave's loads (up to 8 spans of W and x, the whole share at the
+//    batch-16 Linear shape) go out before its MFMAs, so the HBM latency is
+//    paid once rather than once per span.
 //  * The waves' partial 16 x 16 blocks are reduced in LDS in a fixed order.
-//    With split_k > 1 the per-slice sums go to an fp32 workspace and the last
-//    workgroup to arrive for a column block (arrival counter, then a device-
-//    scope fence) adds the slices in slice order, so results are
-//    deterministic; it re-arms the counter for the next launch.  The bias,
-//    activation, mask and the single store run once, after the full K sum.
+//    With split_k > 1 each slice publishes its sum to an fp32 workspace with
+//    device-scope atomic stores, waits until they have completed (vmcnt(0)),
+//    then counts its arrival with a device-scope atomic add; the workgroup
+//    that sees the last count reads every slice back with device-scope
+//    atomic loads and adds them in slice order, so results are
+//    deterministic, and re-arms the counter.  No cache-wide fence is used.
+//    The bias, activation, mask and the single store run once, after the
+//    full K sum.
 #include <type_traits>
 
 #include "ge_device.h"
@@ -32,7 +43,10 @@
 namespace ge {
 
 constexpr int kSmWaves = 8;
-constexpr int kUnroll = 16;
+
+// zeros read in place of the bias by the epilogues that add none
+__device__ const uint32_t kSmZeros[4] = {0u, 0u, 0u, 0u};
+constexpr int kUnroll = 8;   // spans of 64 K values per load batch
 
 template <int DIN, int DOUT>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -68,78 +82,109 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_a
     const int n0 = nblk * 16;
     const int M = p.m, N = p.n, K = p.k;
 
-    // this wave's K range: the slice split evenly over the waves, in steps of 32
+    // this wave's K range: the slice split evenly over the waves, in spans
+    // of 64 (the slice starts on a span boundary: k_per_split is a multiple
+    // of 64)
     const int ks = slice * p.k_per_split;
     const int ke = min(K, ks + p.k_per_split);
-    const int steps_total = (ke - ks + 31) / 32;
-    const int per_wave = (steps_total + kSmWaves - 1) / kSmWaves;
+    const int spans_total = (ke - ks + 63) / 64;
+    const int per_wave = (spans_total + kSmWaves - 1) / kSmWaves;
     // Every workgroup reads all of x, so the waves of different workgroups
     // take the K sub-ranges in a rotated order: at any moment neighbouring
     // workgroups read different parts of x rather than all hitting the same
     // L2 lines.  Each output column's summation order is still fixed.
     const int wslot = (wave + nblk) % kSmWaves;
-    const int s_begin = min(steps_total, wslot * per_wave);
-    const int s_end = min(steps_total, s_begin + per_wave);
-    const int s_full = min(s_end, (ke - ks) / 32);   // steps lying wholly below ke
+    const int s_begin = min(spans_total, wslot * per_wave);
+    const int s_end = min(spans_total, s_begin + per_wave);
+    const int s_full = min(s_end, (ke - ks) / 64);   // spans lying wholly below ke
 
     // Rows beyond n (of W) or m (of x) only feed outputs that are never
     // stored, so their addresses are clamped to the last valid row: the
-    // full steps then need no bounds checks at all.
-    const uint16_t* wrow = (const uint16_t*)p.B + (int64_t)min(n0 + r, N - 1) * p.ldb + ks + q * 8;
-    const uint16_t* xrow = (const uint16_t*)p.A + (int64_t)min(r, M - 1) * p.lda + ks + q * 8;
+    // full spans then need no bounds checks at all.
+    const int wr = lane & 7, wc = lane >> 3;   // full-line loads: row 8j + wr, chunk wc
+    const uint16_t* w0row = (const uint16_t*)p.B + (int64_t)min(n0 + wr, N - 1) * p.ldb + ks + wc * 8;
+    const uint16_t* w1row = (const uint16_t*)p.B + (int64_t)min(n0 + 8 + wr, N - 1) * p.ldb + ks + wc * 8;
+    const uint16_t* xrow = (const uint16_t*)p.A + (int64_t)min(r, M - 1) * p.lda + ks + q * 16;
 
-    // the epilogue's bias values (wave 0 runs the epilogue): fetched now so
-    // that their latency hides under the W stream instead of adding to the
-    // end of the kernel
+    // the epilogue's bias values: fetched now so that their latency hides
+    // under the W stream instead of adding to the end of the kernel.  The
+    // loads are unconditional, with clamped indices (values for columns
+    // beyond n or rows beyond m feed outputs that are never stored): a load
+    // under a per-element branch makes the compiler wait for it on the spot,
+    // which held every wave's W stream back by the bias loads' latency.
+    // (The raw elements are kept and converted in the epilogue, so that
+    // nothing uses them before then.)
     const int ep = p.epilog;
     const bool has_bias = epilog_has_bias(ep);
-    float bpre[4] = {0.f, 0.f, 0.f, 0.f};
-    if (wave == 0 && has_bias) {
+    // (No branch either: without a bias the loads read zeros from kSmZeros,
+    // so nothing has to be merged, and waited for, where the paths join.)
+    // (Both candidates cast to the global address space: a select between a
+    // generic pointer and the device array would make these flat loads,
+    // which the compiler then waits for everywhere.)
+    typedef typename Elem<DOUT>::T BiasT;
+    typedef __attribute__((address_space(1))) const BiasT GlobalBiasT;
+    GlobalBiasT* bp = has_bias ? (GlobalBiasT*)p.bias : (GlobalBiasT*)kSmZeros;
+    BiasT braw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + 4 * q + i;
-            if (p.axis == GE_BIAS_COL) {
-                if (n < N) bpre[i] = load_scalar<DOUT>(p.bias, n);
-            } else if (r < M) {
-                bpre[i] = load_scalar<DOUT>(p.bias, r);
-            }
-        }
-    }
+    for (int i = 0; i < 4; ++i)
+        braw[i] = bp[!has_bias ? 0 : p.axis == GE_BIAS_COL ? min(n0 + 4 * q + i, N - 1) : min(r, M - 1)];
+    __builtin_amdgcn_sched_barrier(0);   // issued here, not sunk to the epilogue
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // accd: sums of the lane's own row (labels 4q + i); accs: of row r ^ 8
+    f32x4 accd = {0.f, 0.f, 0.f, 0.f}, accs = {0.f, 0.f, 0.f, 0.f};
+    const bool rlo = r < 8;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto span_mfmas = [&](const u32x4& w0, const u32x4& w1, const u32x4& xe, const u32x4& xo) {
+        accd = mfma16<DIN, DOUT>(rlo ? w0 : zero, xe, accd);   // rows 0-7, even chunks
+        accd = mfma16<DIN, DOUT>(rlo ? zero : w1, xo, accd);   // rows 8-15, odd chunks
+        accs = mfma16<DIN, DOUT>(rlo ? w1 : zero, xe, accs);   // rows 8-15 (as r^8), even chunks
+        accs = mfma16<DIN, DOUT>(rlo ? zero : w0, xo, accs);   // rows 0-7 (as r^8), odd chunks
+    };
     int s0 = s_begin;
-    // U steps at once: all loads first (the scheduler would otherwise
-    // trickle them out two per MFMA), then the MFMAs
+    // U spans at once: all loads first (the scheduler would otherwise
+    // trickle them out between the MFMAs), then the MFMAs
     auto batch = [&](auto u_const) {
         constexpr int U = decltype(u_const)::value;
-        u32x4 wv[U], xv[U];
+        u32x4 w0[U], w1[U], xe[U], xo[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            wv[u] = __builtin_nontemporal_load((const u32x4*)(wrow + (s0 + u) * 32));
-            xv[u] = *(const u32x4*)(xrow + (s0 + u) * 32);
+            const int off = (s0 + u) * 64;
+            w0[u] = __builtin_nontemporal_load((const u32x4*)(w0row + off));
+            w1[u] = __builtin_nontemporal_load((const u32x4*)(w1row + off));
+            xe[u] = *(const u32x4*)(xrow + off);
+            xo[u] = *(const u32x4*)(xrow + off + 8);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // span by span, so that each waits only for its own loads
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc = mfma16<DIN, DOUT>(wv[u], xv[u], acc);
+        for (int u = 0; u < U; ++u) {
+            span_mfmas(w0[u], w1[u], xe[u], xo[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         s0 += U;
     };
     while (s0 + kUnroll <= s_full) batch(std::integral_constant<int, kUnroll>{});
     // the rest in descending power-of-two batches, never one load at a time
-    // unless a single step is left
-    if (s0 + 8 <= s_full) batch(std::integral_constant<int, 8>{});
+    // unless a single span is left
     if (s0 + 4 <= s_full) batch(std::integral_constant<int, 4>{});
     if (s0 + 2 <= s_full) batch(std::integral_constant<int, 2>{});
     if (s0 < s_full) batch(std::integral_constant<int, 1>{});
     if (s_full >= s_begin && s_full < s_end) {
-        // the ragged last step of the slice, if it falls in this wave's
+        // the ragged last span of the slice, if it falls in this wave's
         // range: elements at k >= ke are zero in both operands (0 * NaN
         // would not vanish)
-        const int col = s_full * 32;
-        const int lim = ke - ks - q * 8;
-        const u32x4 wv = sm_load_masked(wrow, col, lim);
-        const u32x4 xv = sm_load_masked(xrow, col, lim);
-        acc = mfma16<DIN, DOUT>(wv, xv, acc);
+        const int col = s_full * 64;
+        const int lim = ke - ks;
+        const u32x4 w0 = sm_load_masked(w0row - wc * 8, col + wc * 8, lim);
+        const u32x4 w1 = sm_load_masked(w1row - wc * 8, col + wc * 8, lim);
+        const u32x4 xe = sm_load_masked(xrow - q * 16, col + q * 16, lim);
+        const u32x4 xo = sm_load_masked(xrow - q * 16, col + q * 16 + 8, lim);
+        span_mfmas(w0, w1, xe, xo);
     }
+    // row r^8's sums live in lane l^32 (labels 4q + i and 4(q^2) + i)
+    f32x4 acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = accd[i] + __shfl_xor(accs[i], 32);
     // acc: lane holds rows n0 + 4q + i (i = 0..3) of column m = r of y^T
     red[wave][lane] = acc;
     __syncthreads();
@@ -197,7 +242,11 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_a
         const int n = n0 + 4 * q + i;
         float cb = 0.0f;   // the added input term beta * C
         if (beta != 0.0f && mok && n < N) cb = beta * load_scalar<DOUT>(p.cin, (int64_t)m * p.ldc + n);
-        const float x = (sum[i] * s + cb) + bpre[i];
+        float bv = 0.0f;
+        if constexpr (DOUT == GE_F32) bv = braw[i];
+        else if constexpr (DOUT == GE_BF16) bv = bf16_bits_to_f32(braw[i]);
+        else bv = f16_bits_to_f32(braw[i]);
+        const float x = (sum[i] * s + cb) + bv;
         if (want_aux && x > 0.0f && n < N) bits |= 1u << (4 * q + i);
         v[i] = activate(ep, x);
     }

@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--workload", default="C5a")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--no-small-m", action="store_true",
+                   help="skip the nested batch-16 Linear record of the default run")
     p.add_argument("--rotate", type=int, default=None,
                    help="copies of the operands cycled through (defeats the 256 MiB MALL "
                         "for HBM-bound workloads); default 16 for the batch-16 Linear, else 1")
@@ -90,13 +92,13 @@ def traffic_for(workload: str):
 # ---- profile digest (host only) ------------------------------------------------------
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -d {d}/prof_{wll}_trace -o run --output-format csv "
-             "-- python3 bench.py --workload {wl} --steps {steps} --warmup 2 --no-cpu-baseline",
+             "-- python3 bench.py --workload {wl} --steps {steps} --warmup 2 --no-cpu-baseline --no-small-m",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_{wll}_fetch -o run --output-format csv "
              "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused "
-             "--no-graph",
+             "--no-graph --no-small-m",
     "write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_{wll}_write -o run --output-format csv "
              "-- python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-unfused "
-             "--no-graph",
+             "--no-graph --no-small-m",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE -d {d}/prof_copy_fetch -o run --output-format csv "
                   "-- python3 bench.py --copy-calibration 1024 --steps 3",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE -d {d}/prof_copy_write -o run --output-format csv "
@@ -288,35 +290,54 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
                       f"{t_total:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the op shards by rows of A or columns of B with no exchange step; see DESIGN.md)",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.digest:
-        digest(args.digest, args.workload)
-        return
-    import torch
+def roofline(w, ms_per_step, kern_ms, hbm_bound):
+    """(roofline dict, value, unit) of a workload: GB/s of its algorithmic
+    bytes against the HBM peak for the batch-16 Linear, else TFLOP/s against
+    the dense MFMA peak of its input dtype."""
+    alg_bytes = w.algorithmic_bytes()
+    if hbm_bound:
+        value = alg_bytes / (ms_per_step / 1e3) / 1e9
+        achieved = alg_bytes / (kern_ms / 1e3) / 1e9
+        return ({"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(achieved / PEAK_HBM_GBS, 4)}, value, "GB/s")
+    value = w.flops / (ms_per_step / 1e3) / 1e12
+    achieved = w.flops / (kern_ms / 1e3) / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    return ({"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(achieved / peak, 4)}, value, "TFLOP/s")
 
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration, max(args.steps, 1))
-        return
+
+def elementwise_bytes(w) -> int:
+    """Algorithmic bytes of the unfused pair's second kernel: the stored
+    product read back and D written (D's dtype), the bias, and the aux (mask
+    written or read, or the pre-activation written or read)."""
+    eo = synth_elem(w.out_dtype)
+    nb = (w.m if w.axis == "row" else w.n) * eo if w.epilog not in ("none", "drelu", "dgelu") else 0
+    aux = 0
+    if w.epilog in ("relu_aux_bias", "drelu", "drelu_bgrad"):
+        aux = w.m * (((w.n + 127) // 128) * 16)
+    elif w.epilog in ("gelu_aux_bias", "dgelu", "dgelu_bgrad"):
+        aux = w.m * w.n * eo
+    return 2 * w.m * w.n * eo + nb + aux
+
+
+def synth_elem(dt):
+    import synth
+    return synth.ELEM_SIZE[dt]
+
+
+def run_workload(w, args, dev, with_unfused=True, tile=0, split_k=0, autotune=False):
+    """Plan and time one workload: W eager warm-up steps, then K steps
+    between two synchronisations (by default replayed as one captured HIP
+    graph), HIP events on the launch stream around them; the unfused pair and
+    the product alone (its first kernel) timed in the same process."""
+    import torch
 
     import synth
     from activation_epilogue_02_amd import binding as B
 
-    if not os.path.exists(B.LIB_PATH):
-        import __graft_entry__
-        __graft_entry__.build()
-
-    w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     hbm_bound = w.m <= 16
     rot = args.rotate if args.rotate is not None else (16 if hbm_bound else 1)
-
     inp = synth.make_inputs(w, device="cuda")
     copies = [inp]
     for r in range(1, rot):
@@ -332,29 +353,27 @@ def main():
 
     t0 = time.perf_counter()
     g = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-    g.plan(w.epilog, w.axis, tile=args.tile, split_k=args.split_k)
+    g.plan(w.epilog, w.axis, tile=tile, split_k=split_k)
     plan_us = (time.perf_counter() - t0) * 1e6
     outs = [g.alloc_outputs(dev) for _ in range(rot)]
-    tuned_ms = None
-    if args.autotune:
+    if autotune:
         D0, aux0, ws0 = outs[0]
-        tuned_ms = B.gemm_epilog_autotune(g.h, copies[0].A, copies[0].B, bias[0], D0,
-                                          aux_in[0] if grad else aux0, copies[0].scale_a, copies[0].scale_b,
-                                          ws0, iters=3, stream=torch.cuda.current_stream().cuda_stream)
+        B.gemm_epilog_autotune(g.h, copies[0].A, copies[0].B, bias[0], D0, aux_in[0] if grad else aux0,
+                               copies[0].scale_a, copies[0].scale_b, ws0, iters=3,
+                               stream=torch.cuda.current_stream().cuda_stream)
         outs = [g.alloc_outputs(dev) for _ in range(rot)]   # the tuned plan's workspace
     desc = g.describe()
-
     stream = torch.cuda.current_stream()
 
-    def step(i, h=g, outputs=outs):
+    def step(i, h=g, outputs=outs, with_aux_in=True):
         c = copies[i % rot]
         D, aux, ws = outputs[i % rot]
-        if grad:
+        if grad and with_aux_in:
             aux = aux_in[i % rot]
         # the stream current at call time: the capture stream while a graph
         # is being recorded
-        B.gemm_epilog_execute(h.h, c.A, c.B, bias[i % rot], D, aux, c.scale_a, c.scale_b, ws,
-                              None if ws is None else ws.numel(),
+        B.gemm_epilog_execute(h.h, c.A, c.B, bias[i % rot] if with_aux_in else None, D, aux,
+                              c.scale_a, c.scale_b, ws, None if ws is None else ws.numel(),
                               torch.cuda.current_stream().cuda_stream)
 
     def timed(fn):
@@ -401,44 +420,91 @@ def main():
     kern_ms = sum(durs) / len(durs)
 
     unfused = None
-    if not args.no_unfused and w.epilog != "none":
+    if with_unfused and w.epilog != "none":
         gu = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-        gu.plan(w.epilog, w.axis, unfused=1, tile=args.tile, split_k=args.split_k)
+        gu.plan(w.epilog, w.axis, unfused=1, tile=tile, split_k=split_k)
         outs_u = [gu.alloc_outputs(dev) for _ in range(rot)]
         wall_u, durs_u = timed(lambda i: step(i, gu, outs_u))
+        # the pair's first kernel alone: the product with no epilogue
+        gp = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
+        gp.plan("none", w.axis, tile=tile, split_k=split_k)
+        outs_p = [gp.alloc_outputs(dev) for _ in range(rot)]
+        _, durs_p = timed(lambda i: step(i, gp, outs_p, with_aux_in=False))
         # the fused kernel once more after the pair, so that the comparison
         # brackets the pair in time (clocks and temperature drift)
         _, durs2 = timed(step)
         kf = 0.5 * (kern_ms + sum(durs2) / len(durs2))
         ku = sum(durs_u) / len(durs_u)
+        kp = sum(durs_p) / len(durs_p)
+        ew_ms = ku - kp
+        ew_b = elementwise_bytes(w)
         unfused = {"ms_per_step": round(wall_u * 1e3 / args.steps, 4), "kernel_pair_ms": round(ku, 4),
                    "fused_kernel_ms": round(kf, 4), "fused_speedup": round(ku / kf, 4),
+                   "product_only_ms": round(kp, 4),
+                   "elementwise_ms": round(ew_ms, 4),
+                   "elementwise_GBs": round(ew_b / (ew_ms * 1e-3) / 1e9, 1) if ew_ms > 0 else None,
+                   "elementwise_hbm_frac": round(ew_b / (ew_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                   if ew_ms > 0 else None,
                    "plan": gu.describe()}
-        del outs_u
+        del outs_u, outs_p
         gu.free()
+        gp.free()
+    g.free()
+    return {"ms_per_step": ms_per_step, "kern_ms": kern_ms, "hbm_bound": hbm_bound, "desc": desc,
+            "plan_us": plan_us, "rot": rot, "unfused": unfused, "inp": inp, "aux_in0": aux_in[0]}
 
-    alg_bytes = w.algorithmic_bytes()
-    if hbm_bound:
-        value = alg_bytes / (ms_per_step / 1e3) / 1e9
-        metric_unit = "GB/s"
-        achieved = alg_bytes / (kern_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        value = w.flops / (ms_per_step / 1e3) / 1e12
-        metric_unit = "TFLOP/s"
-        achieved = w.flops / (kern_ms / 1e3) / 1e12
-        peak = PEAK_TFLOPS[w.in_dtype]
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the op shards by rows of A or columns of B with no exchange step; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.digest:
+        digest(args.digest, args.workload)
+        return
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
+
+    import synth
+    from activation_epilogue_02_amd import binding as B
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    res = run_workload(w, args, dev, with_unfused=not args.no_unfused, tile=args.tile, split_k=args.split_k,
+                       autotune=args.autotune)
+    ms_per_step, kern_ms, hbm_bound = res["ms_per_step"], res["kern_ms"], res["hbm_bound"]
+    roof, value, metric_unit = roofline(w, ms_per_step, kern_ms, hbm_bound)
     roof["traffic"] = traffic_for(args.workload)
     roof["kernel_ms"] = round(kern_ms, 4)
-    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["algorithmic_bytes_per_launch"] = w.algorithmic_bytes()
     roof["flops_per_launch"] = w.flops
+
+    # the HBM half of the metric: the batch-16 Linear, timed in the same run
+    # (kernel duration from HIP events, 16 rotating operand copies)
+    small_m = None
+    if args.workload != "C3" and not args.no_small_m:
+        w3 = synth.WORKLOADS["C3"]
+        r3 = run_workload(w3, args, dev, with_unfused=not args.no_unfused)
+        roof3, _, _ = roofline(w3, r3["ms_per_step"], r3["kern_ms"], True)
+        small_m = {"workload": w3.name, "kernel_us": round(r3["kern_ms"] * 1e3, 3),
+                   "achieved_GBs": roof3["achieved"], "peak_GBs": PEAK_HBM_GBS, "hbm_frac": roof3["frac"],
+                   "us_per_step": round(r3["ms_per_step"] * 1e3, 3), "plan": r3["desc"],
+                   "operand_copies": r3["rot"], "unfused": r3["unfused"],
+                   "traffic": traffic_for("C3")}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, metric_unit, aux_in[0])
+        cpu = cpu_baseline(w, res["inp"], args.cpu_seconds, metric_unit, res["aux_in0"])
 
     out = {
         "metric": "fused GEMM+bias+act TFLOP/s and % MFMA peak; HBM GB/s at batch 16",
@@ -457,18 +523,18 @@ def main():
                   "K steps replayed as one captured HIP graph, HIP events around the replay",
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "epilog": w.epilog,
                    "bias_axis": w.axis, "op_b": w.op_b, "out_dtype": w.out_dtype,
-                   "operand_copies": rot, "plan": desc, "plan_us": round(plan_us, 1),
+                   "operand_copies": res["rot"], "plan": res["desc"], "plan_us": round(res["plan_us"], 1),
                    "autotuned": bool(args.autotune)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "unfused": unfused,
+        "unfused": res["unfused"],
+        "small_m": small_m,
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
         "hip": torch.version.hip,
         "kernel_src_hash": kernel_src_hash(),
     }
     print(json.dumps(out), flush=True)
-    g.free()
 
 
 if __name__ == "__main__":

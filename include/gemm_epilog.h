@@ -203,7 +203,9 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
  * TANH_BIAS); the automatic path takes the tile kernel for the others.
  * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis, or the
  * small-m path forced with a training-side epilogue), GE_ERR_SHAPE (an
- * unknown tile id or split in p). */
+ * unknown tile id or split in p), GE_ERR_ALIGN (batch > 1 with a COL bias
+ * read by the epilogue and n * element size not a multiple of 16 bytes:
+ * product b's bias, b*n values in, would not be 16-byte aligned). */
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* p);
 
 /* Bytes of device workspace execute() needs: 0 for most fused launches; the

@@ -38,8 +38,12 @@ ESZ = synth.ELEM_SIZE
 
 
 def tolerance(in_dt: str, out_dt: str) -> float:
-    """Relative Frobenius tolerance.  fp8 inputs: the output dtype's (the
-    oracle is exact on the codes; see the module docstring)."""
+    """Relative Frobenius tolerance.  fp8 inputs: 5e-3 for every output dtype
+    (the oracle is exact on the codes, see the module docstring; the fp8
+    matrix-core instruction itself sums its 64-product blocks to about 1.5e-5
+    relative, measured, so fp32 output cannot be held to 1e-5 there)."""
+    if in_dt == "e4m3":
+        return 5e-3
     if out_dt == "f32":
         return 1e-5
     return 5e-3
@@ -66,6 +70,23 @@ def gamma(n: int) -> float:
     return n * U32 / (1.0 - n * U32)
 
 
+# The fp8 matrix-core instruction (32x32x64 f8f6f4) sums each block of 64
+# products more coarsely than an fp32 sum would (measured on MI355X, the same
+# elements on every tile: 1.5e-5 relative Frobenius error at k = 136 with
+# fp32 output; single elements up to 1.74 * 2^-16 of their |A|.|B| at k = 8,
+# 31 and 96, i.e. within one block); the blocks are then accumulated in fp32.
+# The bound takes 2^-14 of |A|.|B| per block (2.3 times the worst measured)
+# plus fp32 accumulation over the ceil(k/64) blocks.
+FP8_BLOCK_U = 2.0 ** -14
+
+
+def product_gamma(w) -> float:
+    """Relative (to |s| |A|.|B|) error bound of the product's accumulation."""
+    if w.in_dtype == "e4m3":
+        return FP8_BLOCK_U + gamma(-(-max(w.k, 1) // 64) + 8)
+    return gamma(max(w.k, 1) + 8)
+
+
 def elem_bound(w, Y, P_or_C1, G, extra_mag, C_prod=None, unfused=False, grad_f=None, aux_pre=None):
     """Largest |D - Y| the arithmetic allows at each element.
 
@@ -75,9 +96,10 @@ def elem_bound(w, Y, P_or_C1, G, extra_mag, C_prod=None, unfused=False, grad_f=N
     backward factor of DRELU/DGELU; aux_pre: DGELU's decoded aux P."""
     u_out = U_OUT[w.out_dtype]
     n_ops = max(w.k, 1) + 8
-    E = gamma(n_ops) * (G + extra_mag)
+    gp = product_gamma(w)
+    E = gp * G + gamma(8) * (G + extra_mag)
     if unfused and C_prod is not None:
-        E = E + u_out * (np.abs(C_prod) + gamma(n_ops) * G)
+        E = E + u_out * (np.abs(C_prod) + gp * G)
     ep = w.epilog
     if ep in ("drelu", "drelu_bgrad"):
         Ey = E

@@ -383,7 +383,7 @@ def test_smallm_split_workspace():
 ])
 def test_smallm_auto_split(m, n, k, split):
     """Without a preference the small-m path splits K while the grid stays
-    within one workgroup per CU and each wave keeps >= 4 K steps."""
+    within one workgroup per CU and each wave keeps >= 2 spans of 64 K values."""
     h = B.gemm_epilog_create(B.make_desc(m, n, k, "bf16", "bf16", 1))
     try:
         B.gemm_epilog_plan(h, "bias", "col")
@@ -409,3 +409,22 @@ def test_status_strings():
 def test_package_api_names():
     for n in header_functions():
         assert hasattr(ge, n), n
+
+
+def test_batched_column_bias_alignment():
+    """A batched COL bias read by the epilogue needs n * element size to be a
+    multiple of 16 bytes (product b's bias starts b*n values in); a ROW bias,
+    a single product and the gradient outputs do not."""
+    def plan_status(n, batch, ep, axis):
+        h = B.gemm_epilog_create(B.make_desc(64, n, 40, "bf16", "bf16", ldd=(n + 7) // 8 * 8,
+                                             ldb=(n + 7) // 8 * 8, batch=batch))
+        try:
+            return status_of(B.gemm_epilog_plan, h, ep, axis)
+        finally:
+            B.gemm_epilog_free(h)
+    assert plan_status(201, 3, "bias", "col") == B.GE_ERR_ALIGN
+    assert plan_status(201, 3, "gelu_bias", "col") == B.GE_ERR_ALIGN
+    assert plan_status(200, 3, "bias", "col") == B.GE_OK
+    assert plan_status(201, 1, "bias", "col") == B.GE_OK
+    assert plan_status(201, 3, "bias", "row") == B.GE_OK
+    assert plan_status(201, 3, "dgelu_bgrad", "col") == B.GE_OK

@@ -96,7 +96,7 @@ def test_batched_small_m_split(split):
 
 @pytest.mark.parametrize("ep", ["gelu_aux_bias", "dgelu_bgrad", "relu_aux_bias"])
 def test_batched_unfused_pair(ep):
-    w = wl(130, 260, 96, "bf16", "bf16", ep, "col", 0, seed=4)
+    w = wl(130, 264, 96, "bf16", "bf16", ep, "col", 0, seed=4)
     for r in run_batched(w, 3, unfused=1):
         check_full(w, r)
 
@@ -106,3 +106,23 @@ def test_batched_empty_sum_gradient_zeroes_every_product():
     for r in run_batched(w, 3, path=1):
         got = oracle.decode(np.ascontiguousarray(codes(r.bias)), "bf16")
         assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_batched_split_k_tile():
+    """The split-K 64 x 64 tile in a batch: products in the grid's y, K slices
+    in z, per-product partials and arrival counters."""
+    w = wl(150, 136, 4100, "bf16", "bf16", "relu_aux_bias", "row", 0, seed=6)
+    rs = run_batched(w, 3, path=1, tile=14, split_k=3)
+    assert "tile_id=14 " in rs[0].desc and "split_k=3 " in rs[0].desc, rs[0].desc
+    for r in rs:
+        check_full(w, r)
+
+
+def test_batched_ragged_n_with_row_bias_and_col_gradient():
+    """n = 201 (bf16 rows of 402 bytes): a row bias is read one value per
+    row, and a column bias gradient is written one value at a time, so both
+    take any n in a batch."""
+    for ep, axis in (("relu_aux_bias", "row"), ("dgelu_bgrad", "col")):
+        w = wl(70, 201, 136, "bf16", "bf16", ep, axis, 0, seed=8)
+        for r in run_batched(w, 3, path=1):
+            check_full(w, r)
