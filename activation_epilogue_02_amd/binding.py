@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libgemm_epilog.so")
 
 # ---- ABI constants (mirror include/gemm_epilog.h) ----------------------------
 GE_OK, GE_ERR_NULL, GE_ERR_SHAPE, GE_ERR_DTYPE, GE_ERR_EPILOG, GE_ERR_ALIGN, \
-    GE_ERR_STATE, GE_ERR_WORKSPACE, GE_ERR_HIP, GE_ERR_ALLOC = range(10)
+    GE_ERR_STATE, GE_ERR_WORKSPACE, GE_ERR_HIP, GE_ERR_ALLOC, GE_ERR_STATIC_LIMIT = range(11)
+GE_STATIC_WORKSPACE_BYTES = 16 << 20
 GE_F32, GE_F16, GE_BF16, GE_F8_E4M3 = 0, 1, 2, 3
 GE_OP_N, GE_OP_T = 0, 1
 GE_EPILOG_NONE, GE_EPILOG_BIAS, GE_EPILOG_RELU_BIAS, GE_EPILOG_RELU_AUX_BIAS, \
@@ -84,9 +85,11 @@ def lib():
         L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp,
                                            ctypes.POINTER(ctypes.c_float)]
         L.gemm_epilog_execute_c.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gemm_epilog_execute_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
-                  "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c"):
+                  "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c",
+                  "gemm_epilog_execute_static"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,6 +159,19 @@ def gemm_epilog_execute(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=N
                                      _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
                                      workspace_bytes, stream or None),
            "gemm_epilog_execute")
+
+
+def gemm_epilog_execute_static(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,
+                               stream=None) -> None:
+    """execute with the library's own fixed workspace array (no workspace
+    argument; nothing is allocated)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    _check(lib().gemm_epilog_execute_static(h, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux),
+                                            _ptr(scale_a), _ptr(scale_b), stream or None),
+           "gemm_epilog_execute_static")
 
 
 def gemm_epilog_free(h: Optional[int]) -> None:

@@ -11,11 +11,41 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "ge_params.h"
 
 using namespace ge;
+
+// ---- the workspace the library holds itself (gemm_epilog_execute_static) -----
+// One fixed array per GPU in the library's code object, held until the
+// process ends, for callers that cannot allocate.  Host code never uses the
+// array's name as a device address (it is a host-side stand-in): the first
+// call on a device asks the runtime for that device's copy
+// (hipGetSymbolAddress with the device current) and every call passes that
+// address to the kernels.
+static __device__ __align__(256) uint8_t scratch[GE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up once per device).
+int scratch_of_current_device(void** p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return GE_ERR_HIP;
+        g_scratch_ptr[dev] = q;
+    }
+    *p = g_scratch_ptr[dev];
+    return GE_OK;
+}
+}  // namespace
 
 struct ge_plan_s {
     ge_desc d;
@@ -337,10 +367,11 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
 }
 
 // execute and execute_c: cin (NULL = no added term) is C in D's dtype with
-// row stride ldc, scaled by the device scalar *beta
+// row stride ldc, scaled by the device scalar *beta.  static_ws: the
+// workspace is the library's own array (execute_static), not the caller's.
 static int execute_impl(ge_handle h, const void* A, const void* B, const void* cin, int64_t ldc, const float* beta,
                         const void* bias, void* D, void* aux, const float* scale_a, const float* scale_b,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream, bool static_ws = false) {
     if (!h) return GE_ERR_NULL;
     if (!h->planned) return GE_ERR_STATE;
     const ge_desc& d = h->d;
@@ -359,8 +390,18 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
         return GE_ERR_ALIGN;
     const size_t need = h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad;
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GE_ERR_WORKSPACE;
+    if (static_ws) {
+        if (need > (size_t)GE_STATIC_WORKSPACE_BYTES) return GE_ERR_STATIC_LIMIT;
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+        return GE_ERR_WORKSPACE;
+    }
     if (test_fail_launch()) return GE_ERR_HIP;
+    if (static_ws && need > 0) {
+        // validation is done: only now the first HIP call
+        const int st = scratch_of_current_device(&workspace);
+        if (st != GE_OK) return st;
+        workspace_bytes = (size_t)GE_STATIC_WORKSPACE_BYTES;
+    }
     if (d.m == 0 || d.n == 0) {
         // empty output; a bias gradient over no rows (or columns) is zero
         if (is_bgrad(h->epilog) && bias_len > 0) {
@@ -459,6 +500,11 @@ int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void*
     return execute_impl(h, A, B, C, ldc, beta, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes, stream);
 }
 
+int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                               const float* scale_a, const float* scale_b, void* stream) {
+    return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, nullptr, 0, stream, true);
+}
+
 int gemm_epilog_free(ge_handle h) {
     delete h;
     return GE_OK;
@@ -476,6 +522,9 @@ const char* gemm_epilog_status_string(int s) {
     case GE_ERR_WORKSPACE: return "GE_ERR_WORKSPACE: workspace missing or too small";
     case GE_ERR_HIP: return "GE_ERR_HIP: kernel launch failed";
     case GE_ERR_ALLOC: return "GE_ERR_ALLOC: host allocation failed";
+    case GE_ERR_STATIC_LIMIT:
+        return "GE_ERR_STATIC_LIMIT: the plan needs more workspace than the library's fixed array "
+               "(GE_STATIC_WORKSPACE_BYTES)";
     }
     return "unknown status";
 }

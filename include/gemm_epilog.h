@@ -68,8 +68,14 @@ enum {
     GE_ERR_STATE = 6,     /* execute on a handle that has not been planned      */
     GE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than workspace_size      */
     GE_ERR_HIP = 8,       /* the kernel launch failed (HIP error)               */
-    GE_ERR_ALLOC = 9      /* host memory for the handle could not be allocated  */
+    GE_ERR_ALLOC = 9,     /* host memory for the handle could not be allocated  */
+    GE_ERR_STATIC_LIMIT = 10 /* execute_static: the plan needs more workspace than
+                                GE_STATIC_WORKSPACE_BYTES                         */
 };
+
+/* Size of the workspace array the library holds on each GPU for
+ * gemm_epilog_execute_static (16 MiB). */
+#define GE_STATIC_WORKSPACE_BYTES (16u << 20)
 
 /* ---- element types ---------------------------------------------------------
  * fp16 = IEEE binary16; bf16 = bfloat16; e4m3 = OCP 8-bit float E4M3 (max
@@ -271,6 +277,31 @@ int gemm_epilog_execute(ge_handle h, const void* A, const void* B, const void* b
 int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void* C, int64_t ldc,
                           const float* beta, const void* bias, void* D, void* aux, const float* scale_a,
                           const float* scale_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/* execute for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same kernels as gemm_epilog_execute, with the workspace taken from an
+ * array the library itself holds on each GPU (GE_STATIC_WORKSPACE_BYTES, a
+ * file-scope device array, resident until the process ends) instead of a
+ * caller buffer.  The caller still passes every input and output.
+ *   - Nothing is allocated or freed, by the library or anything it calls.
+ *   - The array serves the current device (hipGetDevice); `stream` must
+ *     belong to it.  The first call on a device looks up that device's copy
+ *     of the array (one hipGetSymbolAddress, after all validation); later
+ *     calls reuse the address.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's contents; what must start at zero (split-K arrival counters) is
+ *     cleared by a kernel on `stream` at each call.  Calls on one stream are
+ *     ordered; calls that overlap in time on one GPU (different streams, or
+ *     different threads) race on the array and must not be made.
+ * Arguments and errors as for gemm_epilog_execute (there is no workspace
+ * argument), plus GE_ERR_STATIC_LIMIT when gemm_epilog_workspace_size exceeds
+ * GE_STATIC_WORKSPACE_BYTES (e.g. the unfused pair's intermediate of a large
+ * product), and GE_ERR_HIP when the array's device address cannot be had.
+ * A plan whose workspace size is 0 never touches the array. */
+int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias,
+                               void* D, void* aux, const float* scale_a, const float* scale_b,
+                               void* stream);
 
 /* Release the handle (NULL is accepted).  Host-only. */
 int gemm_epilog_free(ge_handle h);

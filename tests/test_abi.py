@@ -401,7 +401,7 @@ def test_smallm_auto_split(m, n, k, split):
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert B.gemm_epilog_status_string(s).startswith("GE_")
     assert B.gemm_epilog_status_string(123) == "unknown status"
 
@@ -409,6 +409,30 @@ def test_status_strings():
 def test_package_api_names():
     for n in header_functions():
         assert hasattr(ge, n), n
+
+
+def test_execute_static_validation():
+    """The fixed-workspace execute validates like execute and refuses plans
+    whose workspace exceeds the library's array, all before any HIP call."""
+    h = B.gemm_epilog_create(desc())
+    try:
+        ex = lambda *a: status_of(B.gemm_epilog_execute_static, h, *a)
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATE          # not planned
+        B.gemm_epilog_plan(h, "relu_aux_bias", "row")
+        assert ex(None, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_NULL
+        assert ex(FAKE, FAKE, FAKE, FAKE, None) == B.GE_ERR_EPILOG
+        assert ex(FAKE + 2, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_ALIGN
+    finally:
+        B.gemm_epilog_free(h)
+    # an unfused pair whose intermediate (4096 x 4096 bf16 = 32 MiB) exceeds
+    # the 16 MiB array
+    big = B.gemm_epilog_create(B.make_desc(4096, 4096, 64, "bf16", "bf16"))
+    try:
+        B.gemm_epilog_plan(big, "bias", "row", B.ge_pref(0, 1, 0, 0))
+        assert B.gemm_epilog_workspace_size(big) > B.GE_STATIC_WORKSPACE_BYTES
+        assert status_of(B.gemm_epilog_execute_static, big, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_STATIC_LIMIT
+    finally:
+        B.gemm_epilog_free(big)
 
 
 def test_batched_column_bias_alignment():
