@@ -21,14 +21,14 @@ LIB_PATH = os.path.join(_HERE, "libgemm_epilog.so")
 GE_OK, GE_ERR_NULL, GE_ERR_SHAPE, GE_ERR_DTYPE, GE_ERR_EPILOG, GE_ERR_ALIGN, \
     GE_ERR_STATE, GE_ERR_WORKSPACE, GE_ERR_HIP, GE_ERR_ALLOC, GE_ERR_STATIC_LIMIT = range(11)
 GE_STATIC_WORKSPACE_BYTES = 16 << 20
-GE_F32, GE_F16, GE_BF16, GE_F8_E4M3 = 0, 1, 2, 3
+GE_F32, GE_F16, GE_BF16, GE_F8_E4M3, GE_MXF8_E4M3 = 0, 1, 2, 3, 4
 GE_OP_N, GE_OP_T = 0, 1
 GE_EPILOG_NONE, GE_EPILOG_BIAS, GE_EPILOG_RELU_BIAS, GE_EPILOG_RELU_AUX_BIAS, \
     GE_EPILOG_GELU_BIAS, GE_EPILOG_GELU_AUX_BIAS, GE_EPILOG_DRELU, GE_EPILOG_DGELU, \
     GE_EPILOG_DRELU_BGRAD, GE_EPILOG_DGELU_BGRAD, GE_EPILOG_TANH_BIAS = range(11)
 GE_BIAS_ROW, GE_BIAS_COL = 0, 1
 
-DTYPE_CODE = {"f32": GE_F32, "f16": GE_F16, "bf16": GE_BF16, "e4m3": GE_F8_E4M3,
+DTYPE_CODE = {"f32": GE_F32, "f16": GE_F16, "bf16": GE_BF16, "e4m3": GE_F8_E4M3, "mxf8": GE_MXF8_E4M3,
               torch.float32: GE_F32, torch.float16: GE_F16, torch.bfloat16: GE_BF16,
               torch.float8_e4m3fn: GE_F8_E4M3}
 EPILOG_CODE = {"none": GE_EPILOG_NONE, "bias": GE_EPILOG_BIAS, "relu_bias": GE_EPILOG_RELU_BIAS,
@@ -38,8 +38,13 @@ EPILOG_CODE = {"none": GE_EPILOG_NONE, "bias": GE_EPILOG_BIAS, "relu_bias": GE_E
                "dgelu_bgrad": GE_EPILOG_DGELU_BGRAD, "tanh_bias": GE_EPILOG_TANH_BIAS}
 AXIS_CODE = {"row": GE_BIAS_ROW, "col": GE_BIAS_COL}
 TORCH_DTYPE = {GE_F32: torch.float32, GE_F16: torch.float16, GE_BF16: torch.bfloat16,
-               GE_F8_E4M3: torch.float8_e4m3fn}
-ELEM_SIZE = {GE_F32: 4, GE_F16: 2, GE_BF16: 2, GE_F8_E4M3: 1}
+               GE_F8_E4M3: torch.float8_e4m3fn, GE_MXF8_E4M3: torch.float8_e4m3fn}
+ELEM_SIZE = {GE_F32: 4, GE_F16: 2, GE_BF16: 2, GE_F8_E4M3: 1, GE_MXF8_E4M3: 1}
+
+
+def mx_scale_ld(k: int) -> int:
+    """Row stride in bytes of the MX block-scale arrays (GE_MX_SCALE_LD)."""
+    return ((k + 31) // 32 + 15) // 16 * 16
 
 
 class ge_desc(ctypes.Structure):
@@ -86,10 +91,11 @@ def lib():
                                            ctypes.POINTER(ctypes.c_float)]
         L.gemm_epilog_execute_c.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gemm_epilog_execute_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gemm_epilog_execute_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
                   "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c",
-                  "gemm_epilog_execute_static"):
+                  "gemm_epilog_execute_static", "gemm_epilog_execute_mx"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,6 +165,24 @@ def gemm_epilog_execute(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=N
                                      _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
                                      workspace_bytes, stream or None),
            "gemm_epilog_execute")
+
+
+def gemm_epilog_execute_mx(h: int, A, B, a_scales, b_scales, bias, D, aux=None, scale_a=None, scale_b=None,
+                           workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """execute for block-scaled fp8 handles: a_scales (m x mx_scale_ld(k)
+    bytes) and b_scales (n x mx_scale_ld(k) bytes) hold one E8M0 scale per 32
+    K values of each row of A and each column of B."""
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if isinstance(workspace, torch.Tensor) else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    _check(lib().gemm_epilog_execute_mx(h, _ptr(A), _ptr(B), _ptr(a_scales), _ptr(b_scales), _ptr(bias), _ptr(D),
+                                        _ptr(aux), _ptr(scale_a), _ptr(scale_b), _ptr(workspace), workspace_bytes,
+                                        stream or None),
+           "gemm_epilog_execute_mx")
 
 
 def gemm_epilog_execute_static(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,

@@ -74,6 +74,7 @@ int elem_size(int t) {
     case GE_F16: return 2;
     case GE_BF16: return 2;
     case GE_F8_E4M3: return 1;
+    case GE_MXF8_E4M3: return 1;
     }
     return 0;
 }
@@ -84,7 +85,8 @@ bool dtype_combo_ok(int a, int b, int d) {
     case GE_F32: return d == GE_F32;
     case GE_F16: return d == GE_F16 || d == GE_F32;
     case GE_BF16: return d == GE_BF16 || d == GE_F32;
-    case GE_F8_E4M3: return d == GE_BF16 || d == GE_F16 || d == GE_F32;
+    case GE_F8_E4M3:
+    case GE_MXF8_E4M3: return d == GE_BF16 || d == GE_F16 || d == GE_F32;
     }
     return false;
 }
@@ -125,6 +127,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int choose_tile(int64_t m, int64_t n, int a_type) {
     const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
     const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    // block-scaled fp8: the one tile the block-scaled MFMA compiles into
+    // without register spills
+    if (a_type == GE_MXF8_E4M3) return 8;
     if (a_type == GE_F8_E4M3) {
         // fp8 rows are 128 bytes per step: a 256 x 256 stage is 64 KiB, so
         // only two stages fit and the registers spill; 256 x 128 keeps three
@@ -155,8 +160,9 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
 }
 
 // The pipelined kernel takes 16-bit and fp8 inputs (its 64 x 64 tile only
-// 16-bit ones).
+// 16-bit ones); block-scaled fp8 runs on its 128 x 128 tile only.
 bool tile_supports(const TileShape* t, int a_type) {
+    if (a_type == GE_MXF8_E4M3) return t->id == 8;
     if (t->kernel == 1) return true;
     if (t->id == 13 || t->id == 14) return a_type == GE_F16 || a_type == GE_BF16;
     return a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
@@ -371,10 +377,16 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
 // workspace is the library's own array (execute_static), not the caller's.
 static int execute_impl(ge_handle h, const void* A, const void* B, const void* cin, int64_t ldc, const float* beta,
                         const void* bias, void* D, void* aux, const float* scale_a, const float* scale_b,
-                        void* workspace, size_t workspace_bytes, void* stream, bool static_ws = false) {
+                        void* workspace, size_t workspace_bytes, void* stream, bool static_ws = false,
+                        const void* mx_a = nullptr, const void* mx_b = nullptr) {
     if (!h) return GE_ERR_NULL;
     if (!h->planned) return GE_ERR_STATE;
     const ge_desc& d = h->d;
+    // block-scaled fp8: the scales come with execute_mx, and only with it
+    const bool mx = d.a_type == GE_MXF8_E4M3;
+    if (!mx && (mx_a || mx_b)) return GE_ERR_DTYPE;
+    if (mx && ((!mx_a && d.m * d.k > 0) || (!mx_b && d.n * d.k > 0))) return GE_ERR_NULL;
+    if (!aligned(mx_a, 16) || !aligned(mx_b, 16)) return GE_ERR_ALIGN;
     // a pointer may be NULL only when its buffer holds no elements
     if ((!A && d.m * d.k > 0) || (!B && d.k * d.n > 0) || (!D && d.m * d.n > 0)) return GE_ERR_NULL;
     const int64_t bias_len = h->axis == GE_BIAS_ROW ? d.m : d.n;
@@ -468,10 +480,15 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         k1.D = ws;
     }
     int err;
-    if (h->path == PATH_SMALLM)
+    if (h->path == PATH_SMALLM) {
         err = launch_smallm(d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
-    else
+    } else if (mx) {
+        const MxArgs mxa = {(const uint8_t*)mx_a, (const uint8_t*)mx_b, (int32_t)GE_MX_SCALE_LD(d.k),
+                            (int32_t)ceil_div(d.k, 32)};
+        err = launch_tile_mx(h->tile_id, d.d_type, d.op_b, k1, mxa, h->grid, stream);
+    } else {
         err = launch_tile(h->tile_id, d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
+    }
     if (err != 0) return GE_ERR_HIP;
     if (h->unfused) {
         // kernel 2: D = act(C + bias) (+ mask)
@@ -498,6 +515,15 @@ int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void*
     if (!h) return GE_ERR_NULL;
     if (!beta || (!C && h->d.m * h->d.n > 0)) return GE_ERR_NULL;
     return execute_impl(h, A, B, C, ldc, beta, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes, stream);
+}
+
+int gemm_epilog_execute_mx(ge_handle h, const void* A, const void* B, const void* a_scales, const void* b_scales,
+                           const void* bias, void* D, void* aux, const float* scale_a, const float* scale_b,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h) return GE_ERR_NULL;
+    if (h->d.a_type != GE_MXF8_E4M3) return GE_ERR_DTYPE;
+    return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
+                        stream, false, a_scales, b_scales);
 }
 
 int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,

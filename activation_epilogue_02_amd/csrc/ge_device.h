@@ -142,6 +142,15 @@ __device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's word
+// lands at M0 + 4*l; the global address must be 4-byte aligned.
+__device__ __forceinline__ void copy_to_lds4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }

@@ -68,6 +68,19 @@ __host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z
     return q;
 }
 
+// Block scales of MX (block-scaled) fp8 operands, a second kernel argument of
+// the MX instantiations of the pipelined tile kernel: one E8M0 byte per 32
+// consecutive K values, for each row of A (sa: m rows) and each column of B
+// (sb: n rows, whichever layout B has), rows of `ld` bytes (a multiple of
+// 16); kb = ceil(k / 32) blocks are valid in a row.  Product z of a batch
+// reads sa + z*m*ld and sb + z*n*ld.
+struct MxArgs {
+    const uint8_t* sa;
+    const uint8_t* sb;
+    int32_t ld;
+    int32_t kb;
+};
+
 // Kernel families.
 enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 
@@ -113,6 +126,11 @@ constexpr int tile2_stages(const TileShape& t, int elem_size) {
 // Launch one fused (or NONE-epilogue) tile-kernel GEMM.  Returns a hipError_t.
 int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs& args,
                 unsigned grid, void* stream);
+
+// Launch the MX instantiation of a pipelined tile (fp8 elements with block
+// scales).  Returns a hipError_t.
+int launch_tile_mx(int tile_id, int d_type, int op_b, const KernelArgs& args, const MxArgs& mx,
+                   unsigned grid, void* stream);
 
 // Launch the small-m streaming kernel.
 int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid,

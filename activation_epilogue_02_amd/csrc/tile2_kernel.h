@@ -84,7 +84,7 @@ __device__ __forceinline__ int swz_kn8(int k, int cpr) {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB>
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool MX = false>
 struct Tile2Cfg {
     static constexpr int NW = WM * WN, NT = NW * 64;
     static constexpr int ESZ = Elem<DIN>::size;
@@ -96,13 +96,20 @@ struct Tile2Cfg {
     static constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
     static constexpr int A_BYTES = BM * ROWB;
     static constexpr int B_BYTES = BK * BN * ESZ;     // same for both B layouts
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    // MX block scales: each wave stages the 4 E8M0 bytes of a step (128 K
+    // values) for each of its TM rows of A and TN columns of B, one 4-byte
+    // direct copy (64 lanes) per 64 rows or columns
+    static constexpr int SCA = MX ? (BM / WM) / 64 : 0;
+    static constexpr int SCB = MX ? (BN / WN) / 64 : 0;
+    static constexpr int SC_WAVE = (SCA + SCB) * 256;   // bytes per wave per stage
+    static constexpr int SC_BYTES = NW * SC_WAVE;
+    static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
     // stages that fit; the register-staged copy uses two (its lookahead is
     // in registers)
     static constexpr int SE = REG ? 2 : (S * STAGE <= 160 * 1024 ? S : (160 * 1024) / STAGE);
     static constexpr int A_INS = A_BYTES / 1024 / NW;   // 1 KiB copies per wave per step
     static constexpr int B_INS = B_BYTES / 1024 / NW;
-    static constexpr int VM_PER_STEP = A_INS + B_INS;
+    static constexpr int VM_PER_STEP = A_INS + B_INS + SCA + SCB;
     static constexpr int KN_ROWB = BN * ESZ;          // bytes per [k][n] LDS row
     static constexpr int KN_CPR = KN_ROWB / 16;       // 16-byte chunks per [k][n] row
     static constexpr int KN_RPI = 1024 / KN_ROWB;     // [k][n] rows per 1 KiB copy
@@ -120,6 +127,8 @@ struct Tile2Cfg {
     static_assert(SE >= 2, "LDS budget");
     static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
     static_assert(NKK % 2 == 0, "fragment sets alternate over an even number of sub-steps");
+    static_assert(!MX || (ESZ == 1 && !REG && (BM / WM) % 64 == 0 && (BN / WN) % 64 == 0),
+                  "MX scales: fp8 elements, direct copies, wave tiles of whole 64-row groups");
     static_assert((SE - 1) * VM_PER_STEP < 64, "vmcnt range");
 };
 
@@ -130,12 +139,11 @@ __device__ __forceinline__ int swz_row(int row) {
     else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
 }
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false>
-__global__ void __launch_bounds__(WM* WN * 64)
-ge_tile2_kernel(KernelArgs p_all) {
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT, bool MX>
+__device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs& mx_all) {
     const KernelArgs p = batch_slice<Elem<DIN>::size, Elem<DOUT>::size>(   // this product of a batch
         p_all, blockIdx.y, OPB == GE_OP_N ? p_all.k : p_all.n);
-    using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB>;
+    using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB, MX>;
     constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
     using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SE * C::STAGE];
@@ -197,15 +205,42 @@ ge_tile2_kernel(KernelArgs p_all) {
     const int64_t stepA = (int64_t)BK * ESZ;
     const int64_t stepB = (OPB == GE_OP_T) ? (int64_t)BK * ESZ : (int64_t)BK * p.ldb * ESZ;
 
-    // direct copy c (A copies first, then B) of full K step t into stage t % SE
+    // MX block scales: lane l of scale copy c fetches, at step t, the 4 bytes
+    // 4t .. 4t+3 (blocks of 32 K values) of row wm*TM + 64c + l of A, or of
+    // column wn*TN + 64c + l of B; rows and columns past the edge are clamped
+    // (their outputs are never stored)
+    const uint8_t* srcSA[C::SCA > 0 ? C::SCA : 1];
+    const uint8_t* srcSB[C::SCB > 0 ? C::SCB : 1];
+    if constexpr (MX) {
+        const uint8_t* sa = mx_all.sa + (int64_t)blockIdx.y * p.m * mx_all.ld;
+        const uint8_t* sb = mx_all.sb + (int64_t)blockIdx.y * p.n * mx_all.ld;
+#pragma unroll
+        for (int c = 0; c < C::SCA; ++c)
+            srcSA[c] = sa + (int64_t)min(m0 + wm * C::TM + 64 * c + lane, max(M - 1, 0)) * mx_all.ld;
+#pragma unroll
+        for (int c = 0; c < C::SCB; ++c)
+            srcSB[c] = sb + (int64_t)min(n0 + wn * C::TN + 64 * c + lane, max(N - 1, 0)) * mx_all.ld;
+    }
+    // this wave's scale words of the step held in `stage`
+    auto sc_base = [&](int stage) {
+        return smem + SE * (C::A_BYTES + C::B_BYTES) + stage * C::SC_BYTES + wave * C::SC_WAVE;
+    };
+
+    // direct copy c (A copies first, then B, then the MX scale words) of full
+    // K step t into stage t % SE
     auto copy_one = [&](int t, int c) {
         uint8_t* sa = smem + (t % SE) * C::A_BYTES;                      // A stages first,
         uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;    // then B stages
         if (c < C::A_INS)
             copy_to_lds16(srcA[c] + (int64_t)t * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
-        else
+        else if (c < C::A_INS + C::B_INS)
             copy_to_lds16(srcB[c - C::A_INS] + (int64_t)t * stepB,
                           lds_addr(sb + (wave * C::B_INS + c - C::A_INS) * 1024));
+        else if constexpr (MX) {
+            const int sc = c - C::A_INS - C::B_INS;   // scale copy: A rows first, then B columns
+            const uint8_t* src = sc < C::SCA ? srcSA[sc] : srcSB[sc - C::SCA];
+            copy_to_lds4(src + 4 * t, lds_addr(sc_base(t % SE) + sc * 256));
+        }
     };
     // issue the direct copies of full K step t into stage t % SE
     auto issue_direct = [&](int t) {
@@ -234,6 +269,21 @@ ge_tile2_kernel(KernelArgs p_all) {
 #pragma unroll
         for (int i = 0; i < C::B_INS; ++i)
             *(u32x4*)(sb + (wave * C::B_INS + i) * 1024 + lane * 16) = vb[i];
+        if constexpr (MX) {
+            // blocks at or past ceil(k/32) hold no data (their elements were
+            // zeroed above) and their bytes may be anything, NaN codes
+            // included: they become 127 (a factor of 1)
+            uint32_t keep = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * t + j < mx_all.kb) keep |= 0xffu << (8 * j);
+#pragma unroll
+            for (int sc = 0; sc < C::SCA + C::SCB; ++sc) {
+                const uint8_t* src = sc < C::SCA ? srcSA[sc] : srcSB[sc - C::SCA];
+                const uint32_t w = *(const uint32_t*)(src + 4 * t);
+                *(uint32_t*)(sc_base(t % SE) + sc * 256 + lane * 4) = (w & keep) | (0x7f7f7f7fu & ~keep);
+            }
+        }
     };
 
     auto issue = [&](int t) {
@@ -250,7 +300,12 @@ ge_tile2_kernel(KernelArgs p_all) {
     // Per-lane LDS read offsets within a stage.  Any assignment of K values
     // to (lane half, operand element) is valid as long as A and B use the
     // same one.  16-bit: sub-step kk, lane half h reads k 16kk + 8h .. +7.
-    // fp8: sub-step kk, lane half h reads k 64kk + 32h .. +31.
+    // fp8: sub-step kk, lane half h reads k 64kk + 16h .. +15 into its bytes
+    // 0-15 and k 64kk + 32 + 16h .. +15 into bytes 16-31.  That is the
+    // assignment the block-scaled instruction needs: it scales bytes 0-15 of
+    // every lane by the E8M0 value of the row's lane half 0 and bytes 16-31 by
+    // that of lane half 1 (measured), so each 32-value K block of the
+    // instruction must be the two lane halves' 16-byte pieces.
     int offA[C::FM][C::NKK][C::NRA];
 #pragma unroll
     for (int f = 0; f < C::FM; ++f) {
@@ -259,15 +314,16 @@ ge_tile2_kernel(KernelArgs p_all) {
         for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
             for (int e = 0; e < C::NRA; ++e) {
-                const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
+                const int chunk = ESZ == 1 ? 4 * kk + h + 2 * e : 2 * kk + h;
                 offA[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
             }
     }
     // B given n x k: as A.  B given k x n, transposing reads:
     //  16-bit, read e of 2: group G, lane i: k = 16kk + 8(G/2) + 4e + i/4,
     //          n = wave col + 32f + 16(G%2) + 4(i%4);
-    //  fp8, read e of 4:    group G, lane i: k = 64kk + 32(G/2) + 8e + i/2,
-    //          n = wave col + 32f + 16(G%2) + 8(i%2).
+    //  fp8, read e of 4:    group G, lane i: k = 64kk + 16(G/2) + 32(e/2) +
+    //          8(e%2) + i/2, n = wave col + 32f + 16(G%2) + 8(i%2)
+    //          (the lane halves' K pieces as for A).
     int offB[C::FN][C::NKK][C::NRB];
 #pragma unroll
     for (int f = 0; f < C::FN; ++f) {
@@ -277,7 +333,7 @@ ge_tile2_kernel(KernelArgs p_all) {
             for (int e = 0; e < C::NRB; ++e) {
                 if constexpr (OPB == GE_OP_T) {
                     const int row = wn * C::TN + f * 32 + r32;
-                    const int chunk = ESZ == 1 ? 4 * kk + 2 * h + e : 2 * kk + h;
+                    const int chunk = ESZ == 1 ? 4 * kk + h + 2 * e : 2 * kk + h;
                     offB[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
                 } else if constexpr (ESZ == 2) {
                     const int G = lane >> 4, i = lane & 15;
@@ -287,7 +343,7 @@ ge_tile2_kernel(KernelArgs p_all) {
                         k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k, C::KN_CPR)) << 4) + ((n & 4) << 1);
                 } else {
                     const int G = lane >> 4, i = lane & 15;
-                    const int k = 64 * kk + 32 * (G >> 1) + 8 * e + (i >> 1);
+                    const int k = 64 * kk + 16 * (G >> 1) + 32 * (e >> 1) + 8 * (e & 1) + (i >> 1);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 8 * (i & 1);
                     offB[f][kk][e] = k * C::KN_ROWB +
                                      (((n >> 4) ^ swz_kn8(k, C::KN_CPR)) << 4) + (n & 8);
@@ -334,15 +390,32 @@ ge_tile2_kernel(KernelArgs p_all) {
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
     };
-    // all fragments of one k sub-step (kk) of the step held in `stage`
-    auto load_frags = [&](int stage, int kk, Frag (&af)[C::FM], Frag (&bfr)[C::FN]) {
+    // MX: the scale word of this lane's row (A) or column (B) for the step
+    // held in `stage`, shifted so that its byte 0 is the scale of the lane's
+    // block: sub-step kk, lane half h reads the 32 K values of block 2kk + h
+    // (the MFMA's lane half h is its K block h; op_sel then stays 0)
+    auto load_scale = [&](int stage, int kk, int slot) -> uint32_t {
+        const uint32_t w = *(const uint32_t*)(sc_base(stage) + slot * 4);
+        return w >> (8 * h + 16 * kk);
+    };
+    // all fragments (and MX scale words) of one k sub-step (kk) of the step
+    // held in `stage`
+    auto load_frags = [&](int stage, int kk, Frag (&af)[C::FM], Frag (&bfr)[C::FN], uint32_t (&sca)[C::FM],
+                          uint32_t (&scb)[C::FN]) {
 #pragma unroll
         for (int f = 0; f < C::FN; ++f) load_fragB(stage, kk, f, bfr);
 #pragma unroll
         for (int f = 0; f < C::FM; ++f) load_fragA(stage, kk, f, af);
+        if constexpr (MX) {
+#pragma unroll
+            for (int f = 0; f < C::FM; ++f) sca[f] = load_scale(stage, kk, f * 32 + r32);
+#pragma unroll
+            for (int f = 0; f < C::FN; ++f) scb[f] = load_scale(stage, kk, C::SCA * 64 + f * 32 + r32);
+        }
     };
     // MFMA number idx (B fragment idx / FM, A fragment idx % FM) of a sub-step
-    auto mfma_one = [&](int idx, const Frag (&af)[C::FM], const Frag (&bfr)[C::FN]) {
+    auto mfma_one = [&](int idx, const Frag (&af)[C::FM], const Frag (&bfr)[C::FN], const uint32_t (&sca)[C::FM],
+                        const uint32_t (&scb)[C::FN]) {
         const int i = idx / C::FM, j = idx % C::FM;
         if constexpr (DIN == GE_BF16)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -350,13 +423,17 @@ ge_tile2_kernel(KernelArgs p_all) {
         else if constexpr (DIN == GE_F16)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(f16x8, bfr[i]), __builtin_bit_cast(f16x8, af[j]), acc[i][j], 0, 0, 0);
+        else if constexpr (MX)   // E4M3 operands with E8M0 block scales: src0 = B's, src1 = A's
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[i], af[j], acc[i][j], 0, 0, 0,
+                                                                         (int)scb[i], 0, (int)sca[j]);
         else   // OCP E4M3 operands (format code 0 for both), no block scales
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[i], af[j], acc[i][j], 0, 0, 0, 0,
                                                                          0, 0);
     };
-    auto mfmas = [&](const Frag (&af)[C::FM], const Frag (&bfr)[C::FN]) {
+    auto mfmas = [&](const Frag (&af)[C::FM], const Frag (&bfr)[C::FN], const uint32_t (&sca)[C::FM],
+                     const uint32_t (&scb)[C::FN]) {
 #pragma unroll
-        for (int idx = 0; idx < C::FM * C::FN; ++idx) mfma_one(idx, af, bfr);
+        for (int idx = 0; idx < C::FM * C::FN; ++idx) mfma_one(idx, af, bfr, sca, scb);
     };
     // Scheduling order for a region holding one sub-step's MFMAs and the
     // next sub-step's fragment reads: LDS read and MFMA alternate, so the
@@ -365,7 +442,7 @@ ge_tile2_kernel(KernelArgs p_all) {
     // alternate with, and the reads simply go first.
     auto interleave = [&]() {
         constexpr int NMF = C::FM * C::FN;
-        constexpr int NDS = C::FM * C::NRA + C::FN * C::NRB;
+        constexpr int NDS = C::FM * C::NRA + C::FN * C::NRB + (MX ? C::FM + C::FN : 0);
         if constexpr (NMF >= 4) {
 #pragma unroll
             for (int i = 0; i < (NMF > NDS ? NMF : NDS); ++i) {
@@ -441,20 +518,21 @@ ge_tile2_kernel(KernelArgs p_all) {
         fetch(2, ra0, rb0);
         fetch(3, ra1, rb1);
         Frag a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+        uint32_t sa0[C::FM], sb0[C::FN], sa1[C::FM], sb1[C::FN];
         if (KT > 0) {
             barrier();
-            load_frags(0, 0, a0, b0);
+            load_frags(0, 0, a0, b0, sa0, sb0);
         }
         auto body = [&](int kt, u32x4 (&ra)[C::A_INS], u32x4 (&rb)[C::B_INS]) {
-            load_frags(kt % 2, 1, a1, b1);
+            load_frags(kt % 2, 1, a1, b1, sa1, sb1);
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(a0, b0);
+            mfmas(a0, b0, sa0, sb0);
             barrier();
             commit(kt + 2, ra, rb);   // into stage kt % 2, free since the barrier
             fetch(kt + 4, ra, rb);
-            load_frags((kt + 1) % 2, 0, a0, b0);
+            load_frags((kt + 1) % 2, 0, a0, b0, sa0, sb0);
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(a1, b1);
+            mfmas(a1, b1, sa1, sb1);
         };
         int kt = 0;
         for (; kt + 2 <= KT - 1; kt += 2) {
@@ -466,9 +544,9 @@ ge_tile2_kernel(KernelArgs p_all) {
             ++kt;
         }
         if (KT > 0) {
-            load_frags((KT - 1) % 2, 1, a1, b1);
-            mfmas(a0, b0);
-            mfmas(a1, b1);
+            load_frags((KT - 1) % 2, 1, a1, b1, sa1, sb1);
+            mfmas(a0, b0, sa0, sb0);
+            mfmas(a1, b1, sa1, sb1);
         }
     } else {
     // ---- main loop ----
@@ -481,9 +559,10 @@ ge_tile2_kernel(KernelArgs p_all) {
     for (int t = 0; t < SE; ++t)
         if (t < KT) issue(t);
     Frag a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    uint32_t sa0[C::FM], sb0[C::FN], sa1[C::FM], sb1[C::FN];   // MX scale words of each set
     if (KT > 0) {
         wait_step(min(SE - 1, KT - 1));
-        load_frags(0, 0, a0, b0);
+        load_frags(0, 0, a0, b0, sa0, sb0);
     }
     // (the last step is peeled off so that the loop body always passes the
     // barrier: a merged path would make the compiler's wait analysis hold
@@ -501,13 +580,13 @@ ge_tile2_kernel(KernelArgs p_all) {
             // do not need it (the scheduler would otherwise sink the last
             // reads to the end of the block and stall the next MFMAs on them)
             if (kk % 2 == 0) {
-                load_frags(stage, kk + 1, a1, b1);
+                load_frags(stage, kk + 1, a1, b1, sa1, sb1);
                 reads_first();
-                mfmas(a0, b0);
+                mfmas(a0, b0, sa0, sb0);
             } else {
-                load_frags(stage, kk + 1, a0, b0);
+                load_frags(stage, kk + 1, a0, b0, sa0, sb0);
                 reads_first();
-                mfmas(a1, b1);
+                mfmas(a1, b1, sa1, sb1);
             }
             interleave();
         }
@@ -519,9 +598,9 @@ ge_tile2_kernel(KernelArgs p_all) {
         // the copies stay ahead of the reads below; the last sub-step's
         // MFMAs interleave with the reads of step kt + 1's first fragments
         __builtin_amdgcn_sched_barrier(0);
-        load_frags((stage + 1) % SE, 0, a0, b0);
+        load_frags((stage + 1) % SE, 0, a0, b0, sa0, sb0);
         reads_first();
-        mfmas(a1, b1);   // the last sub-step (NKK - 1 is odd)
+        mfmas(a1, b1, sa1, sb1);   // the last sub-step (NKK - 1 is odd)
         interleave();
     };
     {
@@ -536,7 +615,7 @@ ge_tile2_kernel(KernelArgs p_all) {
     }
     if (KT > 0) {
         inner((KT - 1) % SE);
-        mfmas(a1, b1);
+        mfmas(a1, b1, sa1, sb1);
     }
     }   // copy mode
 
@@ -698,6 +777,40 @@ ge_tile2_kernel(KernelArgs p_all) {
             }
         }
     }
+}
+
+// The kernels: the plain instantiations take the argument block alone (a
+// larger by-value block once pushed the accumulators into scratch memory);
+// the MX ones (fp8 elements with block scales) take the scales besides.
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false>
+__global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all) {
+    tile2_body<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB, SPLIT, false>(p_all, MxArgs{nullptr, nullptr, 0, 0});
+}
+
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, int RB>
+__global__ void __launch_bounds__(WM* WN * 64) ge_tile2_mx_kernel(KernelArgs p_all, MxArgs mx) {
+    tile2_body<DIN, DOUT, OPB, BM, BN, WM, WN, S, false, RB, false, true>(p_all, mx);
+}
+
+typedef void (*TileMxFn)(KernelArgs, MxArgs);
+
+// MX instantiations: the 128 x 128 tile with four waves of 64 x 64 (tile 8).
+// (The larger tiles were compiled too: with the block-scaled MFMA the
+// compiler spills 500-1500 bytes per lane in every one of them -- the same
+// code with the unscaled instruction does not -- so they are left out.)
+template <int DOUT, int OPB>
+TileMxFn pick_tile2_mx(int tile_id) {
+    if (tile_id == 8) return ge_tile2_mx_kernel<GE_F8_E4M3, DOUT, OPB, 128, 128, 2, 2, 4, 64>;
+    return nullptr;
+}
+
+TileMxFn pick_tile2_mx_f8_bf16(int op_b, int tile_id);
+TileMxFn pick_tile2_mx_f8_f16(int op_b, int tile_id);
+TileMxFn pick_tile2_mx_f8_f32(int op_b, int tile_id);
+
+template <int DOUT>
+TileMxFn pick_op2_mx(int op_b, int tile_id) {
+    return op_b == GE_OP_T ? pick_tile2_mx<DOUT, GE_OP_T>(tile_id) : pick_tile2_mx<DOUT, GE_OP_N>(tile_id);
 }
 
 template <int DIN, int DOUT, int OPB>

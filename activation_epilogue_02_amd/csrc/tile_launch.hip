@@ -33,4 +33,19 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
     return (int)hipGetLastError();
 }
 
+int launch_tile_mx(int tile_id, int d_type, int op_b, const KernelArgs& args, const MxArgs& mx, unsigned grid,
+                   void* stream) {
+    const TileShape* t = nullptr;
+    for (int i = 0; i < kNumTiles; ++i)
+        if (kTiles[i].id == tile_id) t = &kTiles[i];
+    if (!t) return (int)hipErrorInvalidDeviceFunction;
+    TileMxFn fn = nullptr;
+    if (d_type == GE_BF16) fn = pick_tile2_mx_f8_bf16(op_b, tile_id);
+    else if (d_type == GE_F16) fn = pick_tile2_mx_f8_f16(op_b, tile_id);
+    else if (d_type == GE_F32) fn = pick_tile2_mx_f8_f32(op_b, tile_id);
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    hipLaunchKernelGGL(fn, dim3(grid, args.batch, 1), dim3(t->wm * t->wn * 64), 0, (hipStream_t)stream, args, mx);
+    return (int)hipGetLastError();
+}
+
 }  // namespace ge

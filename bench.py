@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "e4m3": 5000.0, "mxf8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "activation_epilogue_02_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -243,6 +243,8 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
             return t.numpy()
         if t.dtype == torch.float8_e4m3fn:
             return t.view(torch.uint8).numpy()
+        if t.dtype == torch.uint8:
+            return t.numpy()
         return t.view(torch.int16).numpy().view(np.uint16)
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
@@ -252,6 +254,8 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
         aux_c = aux_in.detach().cpu().contiguous()
         aux_c = aux_c.numpy().view(np.uint32) if mask_in else raw(aux_c)
     Bc = raw(inp.B)
+    mx = w.in_dtype == "mxf8"
+    SBc = raw(inp.mx_b) if mx else None
     bias = raw(inp.bias).reshape(-1)
     sa = float(inp.scale_a.item()) if inp.scale_a is not None else 1.0
     sb = float(inp.scale_b.item()) if inp.scale_b is not None else 1.0
@@ -263,7 +267,10 @@ def cpu_baseline(w, inp, seconds: float, unit: str, aux_in=None):
         rows = min(rows, w.m - start)
         A_rows = raw(inp.A[start:start + rows])
         t0 = time.perf_counter()
-        C = oracle.gemm(A_rows, w.in_dtype, Bc, w.in_dtype, w.op_b, sa, sb)
+        if mx:
+            C = oracle.gemm_mx(A_rows, "e4m3", raw(inp.mx_a[start:start + rows]), Bc, "e4m3", SBc, w.op_b)
+        else:
+            C = oracle.gemm(A_rows, w.in_dtype, Bc, w.in_dtype, w.op_b, sa, sb)
         if grad:
             Y = (oracle.drelu_pass(C, aux_c[start:start + rows]) if mask_in
                  else oracle.dgelu_pass(C, aux_c[start:start + rows], w.out_dtype))
@@ -372,6 +379,11 @@ def run_workload(w, args, dev, with_unfused=True, tile=0, split_k=0, autotune=Fa
             aux = aux_in[i % rot]
         # the stream current at call time: the capture stream while a graph
         # is being recorded
+        if w.in_dtype == "mxf8":
+            B.gemm_epilog_execute_mx(h.h, c.A, c.B, c.mx_a, c.mx_b, bias[i % rot] if with_aux_in else None,
+                                     D, aux, c.scale_a, c.scale_b, ws, None if ws is None else ws.numel(),
+                                     torch.cuda.current_stream().cuda_stream)
+            return
         B.gemm_epilog_execute(h.h, c.A, c.B, bias[i % rot] if with_aux_in else None, D, aux,
                               c.scale_a, c.scale_b, ws, None if ws is None else ws.numel(),
                               torch.cuda.current_stream().cuda_stream)

@@ -81,8 +81,16 @@ enum {
  * fp16 = IEEE binary16; bf16 = bfloat16; e4m3 = OCP 8-bit float E4M3 (max
  * 448, no infinities), the fp8 format of gfx950's matrix cores.  All products
  * accumulate in fp32 (the 32-bit compute type of the cuBLASLt page,
- * paragraph 3). */
-typedef enum { GE_F32 = 0, GE_F16 = 1, GE_BF16 = 2, GE_F8_E4M3 = 3 } ge_dtype;
+ * paragraph 3).
+ * GE_MXF8_E4M3: E4M3 elements in MX block-scaled form (OCP Microscaling):
+ * every run of 32 consecutive K values of a row of A, or of a column of B,
+ * shares one E8M0 scale (an unsigned 8-bit exponent, scale = 2^(e - 127),
+ * 0xFF = NaN); the element's value is its E4M3 value times that scale.  The
+ * nvmath page names FP8 among the input types and, in its closing
+ * paragraph, low-precision formats as where the fused epilogue is heading.
+ * Such handles are executed with gemm_epilog_execute_mx, which takes the
+ * scales. */
+typedef enum { GE_F32 = 0, GE_F16 = 1, GE_BF16 = 2, GE_F8_E4M3 = 3, GE_MXF8_E4M3 = 4 } ge_dtype;
 
 typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op;
 
@@ -144,6 +152,7 @@ typedef enum { GE_BIAS_ROW = 0, GE_BIAS_COL = 1 } ge_bias_axis;
  *   F16  inputs -> d_type F16 or F32
  *   BF16 inputs -> d_type BF16 or F32
  *   E4M3 inputs -> d_type BF16, F16 or F32
+ *   MXF8_E4M3 inputs -> d_type BF16, F16 or F32 (the 128 x 128 tile)
  * bias_type must equal d_type (for every epilogue): there is no implicit
  * conversion (nvmath page, paragraph on dtype agreement).
  * batch: 0 or 1 for one product; B > 1 (at most 65535) for B independent
@@ -302,6 +311,28 @@ int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void*
 int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias,
                                void* D, void* aux, const float* scale_a, const float* scale_b,
                                void* stream);
+
+/* execute for GE_MXF8_E4M3 handles (block-scaled fp8).  Arguments as for
+ * execute, plus the block scales:
+ *   a_scales  device, m rows of GE_MX_SCALE_LD(k) bytes: byte b of row i is
+ *             the E8M0 scale of A[i][32b .. 32b+31]
+ *   b_scales  device, n rows of GE_MX_SCALE_LD(k) bytes: byte b of row j is
+ *             the scale of B's column j at K values 32b .. 32b+31, whichever
+ *             layout B has (for B given n x k, its rows' scales)
+ * Only the first ceil(k/32) bytes of a row are read; the rest is padding
+ * that keeps every row 16-byte aligned.  With batch > 1, product z reads
+ * a_scales + z*m*ld and b_scales + z*n*ld.  scale_a and scale_b keep their
+ * meaning (a further per-tensor factor, NULL = 1).
+ * Errors: those of execute, GE_ERR_DTYPE (the handle is not MXF8_E4M3),
+ * GE_ERR_NULL (a scale array NULL while its operand holds elements),
+ * GE_ERR_ALIGN (a scale array not 16-byte aligned).  execute, execute_c,
+ * execute_static and autotune on an MXF8_E4M3 handle return GE_ERR_NULL
+ * (the scales are missing). */
+#define GE_MX_SCALE_LD(k) ((((k) + 31) / 32 + 15) / 16 * 16)
+int gemm_epilog_execute_mx(ge_handle h, const void* A, const void* B, const void* a_scales,
+                           const void* b_scales, const void* bias, void* D, void* aux,
+                           const float* scale_a, const float* scale_b, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Release the handle (NULL is accepted).  Host-only. */
 int gemm_epilog_free(ge_handle h);

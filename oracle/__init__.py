@@ -82,6 +82,9 @@ def lib():
         L.orc_gemm_mx.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64,
                                   ctypes.c_int, vp, i64, ctypes.c_int, vp, i64, dbl, dbl, vp]
         L.orc_gemm_mx_abs.argtypes = L.orc_gemm_mx.argtypes
+        L.orc_gemm_mx_entries.argtypes = [i64, ctypes.c_int, vp, i64, vp, i64, ctypes.c_int, vp, i64,
+                                          ctypes.c_int, vp, i64, dbl, dbl, i64, vp, vp, vp]
+        L.orc_gemm_mx_abs_entries.argtypes = L.orc_gemm_mx_entries.argtypes
         L.orc_dec_e8m0.restype = dbl
         L.orc_dec_e8m0.argtypes = [ctypes.c_uint8]
         L.orc_gemm_abs_entries.argtypes = L.orc_gemm_entries.argtypes
@@ -199,6 +202,33 @@ def gemm_mx(A, ta, SA, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
 def gemm_mx_abs(A, ta, SA, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
     """gemm_mx over absolute values (the error bound's magnitude term)."""
     return _gemm_mx_call(lib().orc_gemm_mx_abs, "gemm_mx_abs", A, ta, SA, B, tb, SB, op_b, sa, sb)
+
+
+def _mx_entries_call(fn, what, A_rows, ta, SA_rows, slot, cols, B, tb, SB, op_b, sa, sb):
+    A_rows = _codes(A_rows, ta)
+    B = _codes(B, tb)
+    SA_rows = np.ascontiguousarray(SA_rows, dtype=np.uint8)
+    SB = np.ascontiguousarray(SB, dtype=np.uint8)
+    slot = np.ascontiguousarray(slot, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(slot.shape[0], dtype=np.float64)
+    _check(fn(A_rows.shape[1], DTYPES[ta], _ptr(A_rows), A_rows.shape[1], _ptr(SA_rows), SA_rows.shape[1],
+              DTYPES[tb], _ptr(B), B.shape[1], int(op_b), _ptr(SB), SB.shape[1], float(sa), float(sb),
+              slot.shape[0], _ptr(slot), _ptr(cols), _ptr(out)), what)
+    return out
+
+
+def gemm_mx_entries(A_rows, ta, SA_rows, slot, cols, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
+    """O1x at selected entries: C[row slot[t] of A_rows][cols[t]], with
+    SA_rows the scale rows of A_rows."""
+    return _mx_entries_call(lib().orc_gemm_mx_entries, "gemm_mx_entries", A_rows, ta, SA_rows, slot, cols, B,
+                            tb, SB, op_b, sa, sb)
+
+
+def gemm_mx_abs_entries(A_rows, ta, SA_rows, slot, cols, B, tb, SB, op_b=0, sa=1.0, sb=1.0) -> np.ndarray:
+    """gemm_mx_abs at selected entries."""
+    return _mx_entries_call(lib().orc_gemm_mx_abs_entries, "gemm_mx_abs_entries", A_rows, ta, SA_rows, slot,
+                            cols, B, tb, SB, op_b, sa, sb)
 
 
 def dec_e8m0(e: int) -> float:

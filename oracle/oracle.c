@@ -341,6 +341,46 @@ int orc_gemm_mx_abs(int64_t m, int64_t n, int64_t k, int ta, const void* A, int6
     return gemm_mx_impl(m, n, k, ta, A, lda, SA, ldsa, tb, B, ldb, op_b, SB, ldsb, sa, sb, 1, G);
 }
 
+/* O1x at selected entries (problems too large to compute whole): A_rows
+ * holds some rows of A with their scale rows in SA_rows; entry t is
+ * C[row slot[t] of A_rows][col[t]].  Same arithmetic as gemm_mx_impl. */
+static int mx_entries_impl(int64_t k, int ta, const void* A_rows, int64_t lda, const uint8_t* SA_rows,
+                           int64_t ldsa, int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB,
+                           int64_t ldsb, double sa, double sb, int absval, int64_t cnt, const int64_t* slot,
+                           const int64_t* col, double* out)
+{
+    if (k < 0 || cnt < 0) return -1;
+    const double s = absval ? fabs(sa * sb) : sa * sb;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < cnt; ++t) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < k; ++p) {               /* p ascending */
+            const double a = dec_at(ta, A_rows, slot[t] * lda + p) * orc_dec_e8m0(SA_rows[slot[t] * ldsa + p / 32]);
+            const double b = b_at(tb, B, ldb, op_b, p, col[t]) * orc_dec_e8m0(SB[col[t] * ldsb + p / 32]);
+            acc += opnd(a, absval) * opnd(b, absval);
+        }
+        out[t] = s * acc;
+    }
+    return 0;
+}
+
+int orc_gemm_mx_entries(int64_t k, int ta, const void* A_rows, int64_t lda, const uint8_t* SA_rows, int64_t ldsa,
+                        int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB, int64_t ldsb, double sa,
+                        double sb, int64_t cnt, const int64_t* slot, const int64_t* col, double* out)
+{
+    return mx_entries_impl(k, ta, A_rows, lda, SA_rows, ldsa, tb, B, ldb, op_b, SB, ldsb, sa, sb, 0, cnt, slot,
+                           col, out);
+}
+
+int orc_gemm_mx_abs_entries(int64_t k, int ta, const void* A_rows, int64_t lda, const uint8_t* SA_rows,
+                            int64_t ldsa, int tb, const void* B, int64_t ldb, int op_b, const uint8_t* SB,
+                            int64_t ldsb, double sa, double sb, int64_t cnt, const int64_t* slot,
+                            const int64_t* col, double* out)
+{
+    return mx_entries_impl(k, ta, A_rows, lda, SA_rows, ldsa, tb, B, ldb, op_b, SB, ldsb, sa, sb, 1, cnt, slot,
+                           col, out);
+}
+
 /* ---- O2: bias broadcast ---------------------------------------------------
  * ROW: the bias has one value per output row (shape (m,) or (m,1)) and is
  * added to every column ([epilog page], paragraph on epilog_inputs: the bias

@@ -21,8 +21,9 @@ from typing import Optional
 import torch
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "e4m3": torch.float8_e4m3fn}
-ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+               "e4m3": torch.float8_e4m3fn, "mxf8": torch.float8_e4m3fn}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1, "mxf8": 1}
+E4M3_EMAX = 8   # exponent of E4M3's largest power of two (448 = 1.75 * 2^8)
 E4M3_MAX = 448.0
 
 
@@ -62,6 +63,8 @@ class Workload:
         elif self.epilog in ("gelu_aux_bias", "dgelu", "dgelu_bgrad"):
             aux = self.m * self.n * eo
         scales = 8 if self.in_dtype == "e4m3" else 0
+        if self.in_dtype == "mxf8":   # one byte per 32 K values of every row of A and column of B
+            scales = (self.m + self.n) * ((self.k + 31) // 32)
         return (self.m * self.k + self.k * self.n) * ea + nb + self.m * self.n * eo + aux + scales
 
 
@@ -85,6 +88,10 @@ WORKLOADS = {
                     ("normal", 1 / math.sqrt(16384)), ("normal", 0.1)),
     "C5b": Workload("C5b", "fp8-e4m3 RELU_BIAS 65536x8192x16384", 65536, 8192, 16384, "e4m3", "bf16",
                     "relu_bias", "row", 0, 1005, ("normal", 1 / math.sqrt(16384)),
+                    ("normal", 1 / math.sqrt(16384)), ("normal", 0.1)),
+    # block-scaled fp8 (MX: one E8M0 scale per 32 K values) at the H200 shape
+    "F2a": Workload("F2a", "mxfp8 RELU_BIAS 65536x8192x16384", 65536, 8192, 16384, "mxf8", "bf16",
+                    "relu_bias", "row", 0, 1010, ("normal", 1 / math.sqrt(16384)),
                     ("normal", 1 / math.sqrt(16384)), ("normal", 0.1)),
     # training-side epilogues at the square 8192^3 shape: the GELU forward
     # that keeps its pre-activation, and the two backward products (the
@@ -139,6 +146,35 @@ def quantise_e4m3(x: torch.Tensor):
     return q, s.reshape(1).to(torch.float32)
 
 
+def mx_scale_ld(k: int) -> int:
+    """Row stride in bytes of an MX block-scale array: ceil(k/32) scales,
+    rounded up to 16 bytes."""
+    return ((k + 31) // 32 + 15) // 16 * 16
+
+
+def quantise_mx(x: torch.Tensor):
+    """MX block quantisation along the last axis (OCP Microscaling, E4M3
+    elements): each run of 32 values shares the E8M0 scale 2^(e - 127) with
+    e - 127 = floor(log2(amax of the run)) - 8 (8 being E4M3's largest
+    exponent); the elements are x / scale rounded to E4M3, saturating at 448.
+    An all-zero run gets e = 127.  Returns (codes as float8_e4m3fn, scales as
+    uint8 rows of mx_scale_ld(k) bytes, padding 127)."""
+    rows, k = x.shape
+    kb = (k + 31) // 32
+    xp = torch.zeros((rows, kb * 32), dtype=torch.float32, device=x.device)
+    xp[:, :k] = x
+    blocks = xp.reshape(rows, kb, 32)
+    amax = blocks.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - E4M3_EMAX,
+                    torch.zeros_like(amax))
+    e = torch.clamp(e, -127, 127)
+    q = torch.clamp(blocks / torch.exp2(e)[:, :, None], -E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    codes = q.reshape(rows, kb * 32)[:, :k].contiguous()
+    scales = torch.full((rows, mx_scale_ld(k)), 127, dtype=torch.uint8, device=x.device)
+    scales[:, :kb] = (e + 127).to(torch.uint8)
+    return codes, scales
+
+
 @dataclasses.dataclass
 class Inputs:
     A: torch.Tensor
@@ -146,6 +182,8 @@ class Inputs:
     bias: Optional[torch.Tensor]
     scale_a: Optional[torch.Tensor]
     scale_b: Optional[torch.Tensor]
+    mx_a: Optional[torch.Tensor] = None   # MX block scales of A's rows (m x mx_scale_ld(k), uint8)
+    mx_b: Optional[torch.Tensor] = None   # of B's columns (n x mx_scale_ld(k), uint8)
 
 
 def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
@@ -159,7 +197,19 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
     nbias = w.m if w.axis == "row" else w.n
     bias = _draw(gen, (nbias,), bias_dist or w.bias_dist, device)
     sa = sb = None
-    if w.in_dtype == "e4m3":
+    mxa = mxb = None
+    if w.in_dtype == "mxf8":
+        A, mxa = quantise_mx(a)
+        del a
+        # B's scales follow its columns' K runs, whichever layout B has
+        if w.op_b:
+            B, mxb = quantise_mx(b)
+        else:
+            Bt, mxb = quantise_mx(b.t().contiguous())
+            B = Bt.t().contiguous()
+            del Bt
+        del b
+    elif w.in_dtype == "e4m3":
         A, sa = quantise_e4m3(a)
         del a
         B, sb = quantise_e4m3(b)
@@ -172,7 +222,7 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
     bias = bias.to(TORCH_DTYPE[w.out_dtype])
     if w.axis == "row":
         bias = bias.reshape(w.m, 1)   # the (m,1) form of the nvmath example
-    return Inputs(A.contiguous(), B.contiguous(), bias.contiguous(), sa, sb)
+    return Inputs(A.contiguous(), B.contiguous(), bias.contiguous(), sa, sb, mxa, mxb)
 
 
 def aux_ld_words(n: int) -> int:

@@ -42,7 +42,7 @@ def tolerance(in_dt: str, out_dt: str) -> float:
     (the oracle is exact on the codes, see the module docstring; the fp8
     matrix-core instruction itself sums its 64-product blocks to about 1.5e-5
     relative, measured, so fp32 output cannot be held to 1e-5 there)."""
-    if in_dt == "e4m3":
+    if in_dt in ("e4m3", "mxf8"):
         return 5e-3
     if out_dt == "f32":
         return 1e-5
@@ -82,7 +82,7 @@ FP8_BLOCK_U = 2.0 ** -14
 
 def product_gamma(w) -> float:
     """Relative (to |s| |A|.|B|) error bound of the product's accumulation."""
-    if w.in_dtype == "e4m3":
+    if w.in_dtype in ("e4m3", "mxf8"):
         return FP8_BLOCK_U + gamma(-(-max(w.k, 1) // 64) + 8)
     return gamma(max(w.k, 1) + 8)
 
@@ -133,7 +133,14 @@ def codes(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.uint8).numpy()
     if t.dtype == torch.int32:
         return t.numpy().view(np.uint32)
+    if t.dtype == torch.uint8:
+        return t.numpy()
     raise TypeError(t.dtype)
+
+
+def elem_dt(dt: str) -> str:
+    """The oracle's element dtype (MX fp8 elements are E4M3 codes)."""
+    return "e4m3" if dt == "mxf8" else dt
 
 
 def round_up(x, a):
@@ -212,6 +219,8 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
     bias = inp.bias.to(device).reshape(-1).contiguous() if inp.bias is not None else None
     sa = inp.scale_a.to(device) if inp.scale_a is not None else None
     sb = inp.scale_b.to(device) if inp.scale_b is not None else None
+    mxa = inp.mx_a.to(device).contiguous() if getattr(inp, "mx_a", None) is not None else None
+    mxb = inp.mx_b.to(device).contiguous() if getattr(inp, "mx_b", None) is not None else None
     g = B.GemmEpilog(w.m, w.n, k_b, a_dt, d_dt, w.op_b, lda, ldb, ldd)
     try:
         g.plan(w.epilog, w.axis, path=path, unfused=unfused, tile=tile, split_k=split_k)
@@ -248,11 +257,14 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
             cin_host = cin.detach().cpu().contiguous()
             B.gemm_epilog_execute_c(g.h, A, Bm, C, ldc, beta_t, bias if with_bias else None, D, aux, sa, sb,
                                     ws, None if ws is None else ws.numel(), None)
+        elif a_dt == "mxf8":
+            cin_host = None
+            B.gemm_epilog_execute_mx(g.h, A, Bm, mxa, mxb, bias if with_bias else None, D, aux, sa, sb, ws)
         else:
             cin_host = None
             g.execute(A, Bm, bias if with_bias else None, D, aux, sa, sb, ws)
         torch.cuda.synchronize()
-        return Result(D=D, aux=aux, A=A, B=Bm, bias=bias, sa=sa, sb=sb, lda=lda, ldb=ldb,
+        return Result(D=D, aux=aux, A=A, B=Bm, bias=bias, sa=sa, sb=sb, lda=lda, ldb=ldb, mx_a=mxa, mx_b=mxb,
                       ldd=ldd, desc=desc, cin=cin_host, beta=beta,
                       ldw=(g.aux_ld_bits // 32) if w.epilog in ("relu_aux_bias", "drelu", "drelu_bgrad")
                       else None)
@@ -267,12 +279,19 @@ def oracle_parts(w: synth.Workload, r: Result) -> Result:
     (|s| |A|.|B|), extra (|beta C| + |bias| per element) and, for the
     backward epilogues, the aux values they read."""
     a_dt, d_dt = w.in_dtype, w.out_dtype
-    Ac = codes(r.A).ravel()
-    Bc = codes(r.B).ravel()
     sa = float(r.sa.item()) if r.sa is not None else 1.0
     sb = float(r.sb.item()) if r.sb is not None else 1.0
-    C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
-    G = oracle.gemm_abs(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+    if a_dt == "mxf8":
+        A2 = np.ascontiguousarray(codes(r.A)[:, : w.k])
+        B2 = np.ascontiguousarray(codes(r.B)[:, : (w.k if w.op_b else w.n)])
+        SA, SB = codes(r.mx_a), codes(r.mx_b)
+        C = oracle.gemm_mx(A2, "e4m3", SA, B2, "e4m3", SB, w.op_b, sa, sb)
+        G = oracle.gemm_mx_abs(A2, "e4m3", SA, B2, "e4m3", SB, w.op_b, sa, sb)
+    else:
+        Ac = codes(r.A).ravel()
+        Bc = codes(r.B).ravel()
+        C = oracle.gemm(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
+        G = oracle.gemm_abs(Ac, a_dt, Bc, a_dt, w.op_b, sa, sb, m=w.m, n=w.n, k=w.k, lda=r.lda, ldb=r.ldb)
     C1 = C
     extra = np.zeros_like(C)
     if getattr(r, "cin", None) is not None and r.beta != 0.0:
@@ -436,12 +455,19 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     bias_c = codes(r.bias) if r.bias is not None else None
     # (1) random entries
     slots = np.array([slot_of[int(i)] for i in ei], dtype=np.int64)
-    Ce = oracle.gemm_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej,
-                             np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
-                             w.op_b, sa, sb)
-    Ge = oracle.gemm_abs_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej,
-                                 np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
+    Bk = np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)])
+    if a_dt == "mxf8":
+        SA_rows = codes(r.mx_a.index_select(0, idx))
+        SB = codes(r.mx_b)
+        Ce = oracle.gemm_mx_entries(np.ascontiguousarray(A_rows[:, : w.k]), "e4m3", SA_rows, slots, ej, Bk,
+                                    "e4m3", SB, w.op_b, sa, sb)
+        Ge = oracle.gemm_mx_abs_entries(np.ascontiguousarray(A_rows[:, : w.k]), "e4m3", SA_rows, slots, ej, Bk,
+                                        "e4m3", SB, w.op_b, sa, sb)
+    else:
+        Ce = oracle.gemm_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej, Bk, a_dt,
                                  w.op_b, sa, sb)
+        Ge = oracle.gemm_abs_entries(np.ascontiguousarray(A_rows[:, : w.k]), a_dt, slots, ej, Bk, a_dt,
+                                     w.op_b, sa, sb)
     grad = w.epilog in GRAD_EPILOGS
     Pe = Ce if (w.epilog == "none" or grad) else oracle.bias_entries(Ce, ei, ej, bias_c, d_dt, w.axis)
     Ye = grad_entries(w, r, Ce, ei, ej) if grad else oracle.act_pass(Pe, w.epilog)
@@ -451,10 +477,13 @@ def check_sampled(w: synth.Workload, r: Result, seed: int, tol: Optional[float] 
     # (2) full rows
     rslots = np.array([slot_of[int(i)] for i in rows], dtype=np.int64)
     Ar = np.ascontiguousarray(A_rows[rslots][:, : w.k])
-    Cr = oracle.gemm(Ar, a_dt, np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
-                     w.op_b, sa, sb)
-    Gr = oracle.gemm_abs(Ar, a_dt, np.ascontiguousarray(Bc[:, : (w.k if w.op_b else w.n)]), a_dt,
-                         w.op_b, sa, sb)
+    if a_dt == "mxf8":
+        SAr = np.ascontiguousarray(SA_rows[rslots])
+        Cr = oracle.gemm_mx(Ar, "e4m3", SAr, Bk, "e4m3", SB, w.op_b, sa, sb)
+        Gr = oracle.gemm_mx_abs(Ar, "e4m3", SAr, Bk, "e4m3", SB, w.op_b, sa, sb)
+    else:
+        Cr = oracle.gemm(Ar, a_dt, Bk, a_dt, w.op_b, sa, sb)
+        Gr = oracle.gemm_abs(Ar, a_dt, Bk, a_dt, w.op_b, sa, sb)
     ri = np.repeat(rows, w.n)
     rj = np.tile(np.arange(w.n), len(rows))
     if w.epilog == "none" or grad:

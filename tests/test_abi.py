@@ -452,3 +452,36 @@ def test_batched_column_bias_alignment():
     assert plan_status(201, 1, "bias", "col") == B.GE_OK
     assert plan_status(201, 3, "bias", "row") == B.GE_OK
     assert plan_status(201, 3, "dgelu_bgrad", "col") == B.GE_OK
+
+
+def test_mx_dtype_validation_and_planner():
+    """Block-scaled fp8: bf16/f16/f32 outputs, the 128 x 128 tile only; the
+    scales come with execute_mx, and only with it."""
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "f16")) == B.GE_OK
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "e4m3")) == B.GE_ERR_DTYPE
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "bf16", b_type="e4m3")) == B.GE_ERR_DTYPE
+    h = B.gemm_epilog_create(B.make_desc(4096, 4096, 4096, "mxf8", "bf16"))
+    try:
+        B.gemm_epilog_plan(h, "relu_bias", "row")
+        assert "tile_id=8 " in B.gemm_epilog_describe(h)
+        assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(0, 0, 15, 0)) == B.GE_ERR_SHAPE
+        assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(2, 0, 0, 0)) == B.GE_ERR_SHAPE
+        B.gemm_epilog_plan(h, "relu_bias", "row")
+        ex = lambda *a: status_of(B.gemm_epilog_execute_mx, h, *a)
+        assert ex(FAKE, FAKE, None, FAKE, FAKE, FAKE) == B.GE_ERR_NULL        # A's scales missing
+        assert ex(FAKE, FAKE, FAKE, None, FAKE, FAKE) == B.GE_ERR_NULL        # B's scales missing
+        assert ex(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE) == B.GE_ERR_ALIGN
+        assert ex(FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE) == B.GE_ERR_ALIGN
+        # the per-tensor entry points have no scales to give
+        assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_NULL
+        assert status_of(B.gemm_epilog_execute_static, h, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_NULL
+    finally:
+        B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(64, 48, 64, "e4m3", "bf16"))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert status_of(B.gemm_epilog_execute_mx, h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_DTYPE
+    finally:
+        B.gemm_epilog_free(h)
+    assert B.mx_scale_ld(1) == 16 and B.mx_scale_ld(512) == 16 and B.mx_scale_ld(513) == 32
+    assert B.mx_scale_ld(16384) == 512

@@ -586,3 +586,20 @@ def test_mx_block_index_and_layouts():
     assert np.isnan(Cn[1]).all() and np.isfinite(np.delete(Cn, 1, 0)).all()
     G = oracle.gemm_mx_abs(A, "e4m3", SA, Bn, "e4m3", SB, 0)
     assert (np.abs(C) <= G).all()
+
+
+def test_mx_entries_match_the_whole_product():
+    rng = np.random.default_rng(14)
+    m, n, k = 5, 7, 80
+    A = e4m3_codes_of_ints(rng.integers(-6, 7, (m, k)))
+    for op_b in (0, 1):
+        B = e4m3_codes_of_ints(rng.integers(-6, 7, (n, k) if op_b else (k, n)))
+        SA = rng.integers(118, 136, (m, 16)).astype(np.uint8)
+        SB = rng.integers(118, 136, (n, 16)).astype(np.uint8)
+        C = oracle.gemm_mx(A, "e4m3", SA, B, "e4m3", SB, op_b, 2.0, 0.25)
+        G = oracle.gemm_mx_abs(A, "e4m3", SA, B, "e4m3", SB, op_b, 2.0, 0.25)
+        rows, cols = np.array([0, 4, 2, 2, 1]), np.array([6, 0, 3, 3, 5])
+        assert np.array_equal(oracle.gemm_mx_entries(A, "e4m3", SA, rows, cols, B, "e4m3", SB, op_b, 2.0, 0.25),
+                              C[rows, cols])
+        assert np.array_equal(oracle.gemm_mx_abs_entries(A, "e4m3", SA, rows, cols, B, "e4m3", SB, op_b, 2.0, 0.25),
+                              G[rows, cols])
