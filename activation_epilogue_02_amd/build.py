@@ -28,7 +28,11 @@ SOURCES = ["api.cpp", "tile_launch.hip", "tile_f32.hip", "tile_f16.hip", "tile_b
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-result",
           # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # let `#pragma unroll` unroll the tile epilogue fully: past the
+          # default size limit the loop stays rolled, its accumulator index
+          # becomes dynamic and the accumulators move to scratch memory
+          "-mllvm", "-pragma-unroll-threshold=1000000"]
 
 
 def _compile(src: str) -> str:

@@ -5,6 +5,6 @@
 
 namespace ge {
 
-TileFn pick_tile2_bf16_bf16(int op_b, int tile_id) { return pick_op2<GE_BF16, GE_BF16>(op_b, tile_id); }
+Tile2Fn pick_tile2_bf16_bf16(int op_b, int tile_id) { return pick_op2<GE_BF16, GE_BF16>(op_b, tile_id); }
 
 }  // namespace ge

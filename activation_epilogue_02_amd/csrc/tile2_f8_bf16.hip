@@ -5,6 +5,6 @@
 
 namespace ge {
 
-TileFn pick_tile2_f8_bf16(int op_b, int tile_id) { return pick_op2<GE_F8_E4M3, GE_BF16>(op_b, tile_id); }
+Tile2Fn pick_tile2_f8_bf16(int op_b, int tile_id) { return pick_op2<GE_F8_E4M3, GE_BF16>(op_b, tile_id); }
 
 }  // namespace ge

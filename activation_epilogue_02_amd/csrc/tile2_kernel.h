@@ -139,8 +139,13 @@ __device__ __forceinline__ int swz_row(int row) {
     else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
 }
 
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT, bool MX>
-__device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs& mx_all) {
+// One kernel template for the plain and the block-scaled (MX) instantiations.
+// Its body stays in the __global__ function itself: moved into a force-inlined
+// device function, the same code compiled to 3x the scalar-register spills
+// and 768 bytes of scratch per lane on the 256 x 256 tile (10x slower).
+template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false,
+          bool MX = false>
+__global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all, MxArgs mx_all) {
     const KernelArgs p = batch_slice<Elem<DIN>::size, Elem<DOUT>::size>(   // this product of a batch
         p_all, blockIdx.y, OPB == GE_OP_N ? p_all.k : p_all.n);
     using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB, MX>;
@@ -228,7 +233,7 @@ __device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs
 
     // direct copy c (A copies first, then B, then the MX scale words) of full
     // K step t into stage t % SE
-    auto copy_one = [&](int t, int c) {
+    auto copy_one = [&](int t, int c) __attribute__((always_inline)) {
         uint8_t* sa = smem + (t % SE) * C::A_BYTES;                      // A stages first,
         uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;    // then B stages
         if (c < C::A_INS)
@@ -243,13 +248,16 @@ __device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs
         }
     };
     // issue the direct copies of full K step t into stage t % SE
-    auto issue_direct = [&](int t) {
+    auto issue_direct = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < C::VM_PER_STEP; ++c) copy_one(t, c);
     };
 
     // the ragged last K step t: through registers, elements at k >= K zeroed
-    auto issue_tail = [&](int t) {
+    // (the staging lambdas are forced inline: left to the inliner, the 4-wave
+    // 256 x 256 tile called this path as a function, with KernelArgs copied to
+    // a 2 KiB stack frame in scratch memory)
+    auto issue_tail = [&](int t) __attribute__((always_inline)) {
         uint8_t* sa = smem + (t % SE) * C::A_BYTES;
         uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;
         const int k0 = t * BK;
@@ -286,7 +294,7 @@ __device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs
         }
     };
 
-    auto issue = [&](int t) {
+    auto issue = [&](int t) __attribute__((always_inline)) {
         if (t < KF) issue_direct(t);
         else issue_tail(t);
     };
@@ -779,42 +787,24 @@ __device__ __forceinline__ void tile2_body(const KernelArgs& p_all, const MxArgs
     }
 }
 
-// The kernels: the plain instantiations take the argument block alone (a
-// larger by-value block once pushed the accumulators into scratch memory);
-// the MX ones (fp8 elements with block scales) take the scales besides.
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false>
-__global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all) {
-    tile2_body<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB, SPLIT, false>(p_all, MxArgs{nullptr, nullptr, 0, 0});
-}
-
-template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, int RB>
-__global__ void __launch_bounds__(WM* WN * 64) ge_tile2_mx_kernel(KernelArgs p_all, MxArgs mx) {
-    tile2_body<DIN, DOUT, OPB, BM, BN, WM, WN, S, false, RB, false, true>(p_all, mx);
-}
-
-typedef void (*TileMxFn)(KernelArgs, MxArgs);
 
 // MX instantiations: the 128 x 128 tile with four waves of 64 x 64 (tile 8).
 // (The larger tiles were compiled too: with the block-scaled MFMA the
 // compiler spills 500-1500 bytes per lane in every one of them -- the same
 // code with the unscaled instruction does not -- so they are left out.)
 template <int DOUT, int OPB>
-TileMxFn pick_tile2_mx(int tile_id) {
-    if (tile_id == 8) return ge_tile2_mx_kernel<GE_F8_E4M3, DOUT, OPB, 128, 128, 2, 2, 4, 64>;
+Tile2Fn pick_tile2_mx(int tile_id) {
+    if (tile_id == 8) return ge_tile2_kernel<GE_F8_E4M3, DOUT, OPB, 128, 128, 2, 2, 4, false, 64, false, true>;
     return nullptr;
 }
 
-TileMxFn pick_tile2_mx_f8_bf16(int op_b, int tile_id);
-TileMxFn pick_tile2_mx_f8_f16(int op_b, int tile_id);
-TileMxFn pick_tile2_mx_f8_f32(int op_b, int tile_id);
-
 template <int DOUT>
-TileMxFn pick_op2_mx(int op_b, int tile_id) {
+Tile2Fn pick_op2_mx(int op_b, int tile_id) {
     return op_b == GE_OP_T ? pick_tile2_mx<DOUT, GE_OP_T>(tile_id) : pick_tile2_mx<DOUT, GE_OP_N>(tile_id);
 }
 
 template <int DIN, int DOUT, int OPB>
-TileFn pick_tile2(int tile_id) {
+Tile2Fn pick_tile2(int tile_id) {
     switch (tile_id) {
     case 5: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 2, 4, false, 64>;
     case 6: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 4, false, 64>;
@@ -837,7 +827,7 @@ TileFn pick_tile2(int tile_id) {
 }
 
 template <int DIN, int DOUT>
-TileFn pick_op2(int op_b, int tile_id) {
+Tile2Fn pick_op2(int op_b, int tile_id) {
     return op_b == GE_OP_T ? pick_tile2<DIN, DOUT, GE_OP_T>(tile_id) : pick_tile2<DIN, DOUT, GE_OP_N>(tile_id);
 }
 

@@ -6,6 +6,6 @@
 
 namespace ge {
 
-TileMxFn pick_tile2_mx_f8_f32(int op_b, int tile_id) { return pick_op2_mx<GE_F32>(op_b, tile_id); }
+Tile2Fn pick_tile2_mx_f8_f32(int op_b, int tile_id) { return pick_op2_mx<GE_F32>(op_b, tile_id); }
 
 }  // namespace ge

@@ -461,12 +461,18 @@ TileFn pick_tile_f32(int d_type, int op_b, int tile_id);
 TileFn pick_tile_f16(int d_type, int op_b, int tile_id);
 TileFn pick_tile_bf16(int d_type, int op_b, int tile_id);
 TileFn pick_tile_f8(int d_type, int op_b, int tile_id);
-TileFn pick_tile2_f16_f16(int op_b, int tile_id);
-TileFn pick_tile2_f16_f32(int op_b, int tile_id);
-TileFn pick_tile2_bf16_bf16(int op_b, int tile_id);
-TileFn pick_tile2_bf16_f32(int op_b, int tile_id);
-TileFn pick_tile2_f8_bf16(int op_b, int tile_id);
-TileFn pick_tile2_f8_f16(int op_b, int tile_id);
-TileFn pick_tile2_f8_f32(int op_b, int tile_id);
+// the pipelined kernels take the MX block-scale arguments besides (unused
+// and zero unless the instantiation is a block-scaled one)
+typedef void (*Tile2Fn)(KernelArgs, MxArgs);
+Tile2Fn pick_tile2_f16_f16(int op_b, int tile_id);
+Tile2Fn pick_tile2_f16_f32(int op_b, int tile_id);
+Tile2Fn pick_tile2_bf16_bf16(int op_b, int tile_id);
+Tile2Fn pick_tile2_bf16_f32(int op_b, int tile_id);
+Tile2Fn pick_tile2_f8_bf16(int op_b, int tile_id);
+Tile2Fn pick_tile2_f8_f16(int op_b, int tile_id);
+Tile2Fn pick_tile2_f8_f32(int op_b, int tile_id);
+Tile2Fn pick_tile2_mx_f8_bf16(int op_b, int tile_id);
+Tile2Fn pick_tile2_mx_f8_f16(int op_b, int tile_id);
+Tile2Fn pick_tile2_mx_f8_f32(int op_b, int tile_id);
 
 }  // namespace ge
