@@ -57,7 +57,7 @@ class ge_desc(ctypes.Structure):
 
 class ge_pref(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("unfused", ctypes.c_int32),
-                ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+                ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32), ("group_m", ctypes.c_int32)]
 
 
 class GemmEpilogError(RuntimeError):
@@ -251,8 +251,8 @@ class GemmEpilog:
         self.h = gemm_epilog_create(self.desc)
         self.epilog = None
 
-    def plan(self, epilog="bias", axis="row", path=0, unfused=0, tile=0, split_k=0):
-        gemm_epilog_plan(self.h, epilog, axis, ge_pref(path, unfused, tile, split_k))
+    def plan(self, epilog="bias", axis="row", path=0, unfused=0, tile=0, split_k=0, group_m=0):
+        gemm_epilog_plan(self.h, epilog, axis, ge_pref(path, unfused, tile, split_k, group_m))
         self.epilog = EPILOG_CODE[epilog] if isinstance(epilog, str) else epilog
         self.ws_bytes = gemm_epilog_workspace_size(self.h)
         self.aux_ld_bits = gemm_epilog_aux_ld(self.h)

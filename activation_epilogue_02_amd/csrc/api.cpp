@@ -62,7 +62,7 @@ struct ge_plan_s {
     int64_t part_bytes = 0;  // split-K partial bytes per product
     size_t ws_bgrad = 0;     // bias-gradient partial bytes
     int32_t bgrad_parts = 0; // bias-gradient partials per entry
-    ge_pref pref = {0, 0, 0, 0};   // the preferences the plan was made with
+    ge_pref pref = {0, 0, 0, 0, 0};   // the preferences the plan was made with
     int64_t ldaux = 0;       // mask row stride, 32-bit words
 };
 
@@ -120,6 +120,17 @@ const TileShape* find_tile(int id) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The register-staged tile kernel's tile for a problem (any dtype).
+int choose_tile_plain(int64_t m, int64_t n) {
+    const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
+    const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    if (t256 >= 512) return 3;
+    if (t128 >= 512) return 2;
+    if (t256 >= 256 && t128 < 256) return 3;
+    if (t128 >= 256) return 2;
+    return 1;
+}
+
 // Tile heuristic: the largest block tile that still gives every CU at least
 // two tiles (256 CUs); below that, the shape with the most tiles.  Large
 // tiles halve the L2 -> LDS traffic per flop; small problems need the
@@ -143,20 +154,40 @@ int choose_tile(int64_t m, int64_t n, int a_type) {
     }
     if (a_type == GE_F16 || a_type == GE_BF16) {
         // the pipelined direct-to-LDS kernel; at 256 x 256 the 8-wave
-        // layout (two waves per SIMD fill each other's barrier and copy
-        // gaps) with 128-byte K steps (full-line A requests, half the
-        // barriers) measures fastest
-        if (t256 >= 512) return 11;
+        // layout (two waves per SIMD fill each other's barrier gaps) with
+        // four 64-byte K stages, whose copies are spread among the MFMAs,
+        // measures fastest (65536 x 8192 x 16384: 1258 TFLOP/s against
+        // 1164 for two 128-byte stages with the copies in one burst)
+        if (t256 >= 512) return 6;
         if (t128 >= 512) return 8;
-        if (t256 >= 256 && t128 < 256) return 11;
+        if (t256 >= 256 && t128 < 256) return 6;
         if (t128 >= 256) return 8;
         return 13;   // small problems: 64 x 64 tiles, four deep stages
     }
-    if (t256 >= 512) return 3;
-    if (t128 >= 512) return 2;
-    if (t256 >= 256 && t128 < 256) return 3;
-    if (t128 >= 256) return 2;
-    return 1;
+    return choose_tile_plain(m, n);
+}
+
+// The pipelined kernels' direct copies address a tile's rows of A, and of B
+// (either layout), as 32-bit offsets from the tile's first row or column:
+// the span must stay below 4 GiB.  (A K step is at most 128 elements.)
+bool tile_span_ok(const TileShape* t, const ge_desc& d) {
+    if (t->kernel == 1 || t->kernel == 3) return true;   // per-lane 64-bit addresses
+    const int64_t es = elem_size(d.a_type), lim = (int64_t)1 << 32;
+    if ((int64_t)t->bm * d.lda * es > lim) return false;
+    if (d.op_b == GE_OP_T) return (int64_t)t->bn * d.ldb * es <= lim;
+    return ((int64_t)128 * d.ldb + t->bn) * es <= lim;
+}
+
+// Tile rows per group of the launch order (see tile_coords).  The 32 tiles
+// an XCD runs at once then cover g tile rows and 32 / g columns.  Fewer rows
+// than the 8 that minimise the panels in flight measure faster: with eight,
+// every B line is wanted by eight CUs at the same moment and A lines by
+// four, and the requests queue behind the one that misses (65536 x 8192 x
+// 16384 bf16, 256 x 256 tiles: 1207 / 1258 / 1236 TFLOP/s at 8 / 4 / 2 rows;
+// the block-scaled 128 x 128 tile: 1150 / 1198 / 1278).
+int32_t auto_group_m(const TileShape* t, int64_t tm, int a_type) {
+    const int64_t g = a_type == GE_MXF8_E4M3 ? 2 : (t->kernel == 1 ? 8 : 4);
+    return (int32_t)(tm < g ? (tm > 0 ? tm : 1) : g);
 }
 
 // The pipelined kernel takes 16-bit and fp8 inputs (its 64 x 64 tile only
@@ -228,9 +259,10 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     if (!h) return GE_ERR_NULL;
     if (epilog < GE_EPILOG_NONE || epilog > GE_EPILOG_TANH_BIAS) return GE_ERR_EPILOG;
     if (bias_axis != GE_BIAS_ROW && bias_axis != GE_BIAS_COL) return GE_ERR_EPILOG;
-    ge_pref pr = {0, 0, 0, 0};
+    ge_pref pr = {0, 0, 0, 0, 0};
     if (pref) pr = *pref;
-    if (pr.path < 0 || pr.path > PATH_SMALLM || pr.unfused < 0 || pr.unfused > 1 || pr.split_k < 0)
+    if (pr.path < 0 || pr.path > PATH_SMALLM || pr.unfused < 0 || pr.unfused > 1 || pr.split_k < 0 ||
+        pr.group_m < 0)
         return GE_ERR_SHAPE;
     if (pr.tile != 0 && !find_tile(pr.tile)) return GE_ERR_SHAPE;
     const ge_desc& d = h->d;
@@ -298,13 +330,19 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
             q.tile_id = 14;
         const TileShape* t = find_tile(q.tile_id);
         if (!tile_supports(t, d.a_type)) return GE_ERR_SHAPE;
+        if (!tile_span_ok(t, d)) {
+            if (pr.tile || d.a_type == GE_MXF8_E4M3) return GE_ERR_SHAPE;
+            q.tile_id = choose_tile_plain(d.m, d.n);
+            t = find_tile(q.tile_id);
+        }
         if (pr.split_k > 1 && t->kernel != 5) return GE_ERR_SHAPE;   // only the split-K tile splits K
         if (t->kernel == 5 && is_bgrad(epilog)) return GE_ERR_EPILOG;
         const int64_t tm = ceil_div(d.m, t->bm), tn = ceil_div(d.n, t->bn);
         if (tm * tn > INT32_MAX) return GE_ERR_SHAPE;
         q.tiles_m = (int32_t)tm;
         q.tiles_n = (int32_t)tn;
-        q.group_m = (int32_t)(tm < 8 ? (tm > 0 ? tm : 1) : 8);
+        q.group_m = pr.group_m > 0 ? (int32_t)(pr.group_m < tm ? pr.group_m : (tm > 0 ? tm : 1))
+                                   : auto_group_m(t, tm, d.a_type);
         q.grid = (unsigned)(tm * tn);
         q.k_per_split = (int32_t)d.k;
         if (t->kernel == 5) {

@@ -142,6 +142,17 @@ __device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// The same copy with its global address split into a wave-uniform 64-bit
+// base (SGPRs) and a 32-bit unsigned per-lane byte offset: advancing the
+// copy along K is then one scalar add per step instead of a 64-bit vector
+// add per copy in every lane.
+__device__ __forceinline__ void copy_to_lds16_sb(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
 // The same with 4 bytes per lane (global_load_lds_dword): lane l's word
 // lands at M0 + 4*l; the global address must be 4-byte aligned.
 __device__ __forceinline__ void copy_to_lds4(const void* g, uint32_t lds) {

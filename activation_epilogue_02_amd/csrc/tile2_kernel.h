@@ -110,6 +110,12 @@ struct Tile2Cfg {
     static constexpr int A_INS = A_BYTES / 1024 / NW;   // 1 KiB copies per wave per step
     static constexpr int B_INS = B_BYTES / 1024 / NW;
     static constexpr int VM_PER_STEP = A_INS + B_INS + SCA + SCB;
+    // Direct copies spread among the MFMAs: the copies of a step start
+    // while the stage they fill is two steps from being read, each sub-step
+    // region taking an equal share.  With three stages that leaves them
+    // about one step to land, less than the burst loop's two: measured
+    // slower (fp8 256 x 128), so it takes four or more.
+    static constexpr bool SPREAD = !REG && SE >= 4 && VM_PER_STEP % NKK == 0;
     static constexpr int KN_ROWB = BN * ESZ;          // bytes per [k][n] LDS row
     static constexpr int KN_CPR = KN_ROWB / 16;       // 16-byte chunks per [k][n] row
     static constexpr int KN_RPI = 1024 / KN_ROWB;     // [k][n] rows per 1 KiB copy
@@ -130,6 +136,7 @@ struct Tile2Cfg {
     static_assert(!MX || (ESZ == 1 && !REG && (BM / WM) % 64 == 0 && (BN / WN) % 64 == 0),
                   "MX scales: fp8 elements, direct copies, wave tiles of whole 64-row groups");
     static_assert((SE - 1) * VM_PER_STEP < 64, "vmcnt range");
+    static_assert(!SPREAD || (SE - 3) * VM_PER_STEP + (NKK - 1) * (VM_PER_STEP / NKK) < 64, "vmcnt range");
 };
 
 // swizzle of the chunks of a ROWB-byte row (A, or B given n x k)
@@ -175,7 +182,12 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
 
     // ---- per-lane sources of this wave's 1 KiB copies, at K step 0 ----
     // A: copy i covers LDS rows R = (wave*A_INS + i)*RPC + lane/CPR, slot lane%CPR
+    // srcA/srcB: per-lane addresses (register-staged copies); voA/voB: the
+    // same as 32-bit offsets from the tile's wave-uniform bases baseA/baseB
+    // (direct copies).  The planner keeps a tile's span of A rows (and of B
+    // given n x k) below 4 GiB.
     const uint8_t* srcA[C::A_INS];
+    uint32_t voA[C::A_INS], voB[C::B_INS];
     int rowA_cp[C::A_INS], chA_cp[C::A_INS];
 #pragma unroll
     for (int i = 0; i < C::A_INS; ++i) {
@@ -185,6 +197,7 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
         rowA_cp[i] = m0 + R;
         chA_cp[i] = c;
         srcA[i] = gA + ((int64_t)gm * p.lda + c * EPC) * ESZ;
+        voA[i] = (uint32_t)(((int64_t)(gm - m0) * p.lda + c * EPC) * ESZ);
     }
     const uint8_t* srcB[C::B_INS];
     int rowB_cp[C::B_INS], chB_cp[C::B_INS];
@@ -198,6 +211,7 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             rowB_cp[i] = n0 + R;
             chB_cp[i] = c;
             srcB[i] = gB + ((int64_t)gn * p.ldb + c * EPC) * ESZ;
+            voB[i] = (uint32_t)(((int64_t)(gn - n0) * p.ldb + c * EPC) * ESZ);
         } else {
             const int kr = (wave * C::B_INS + i) * C::KN_RPI + lane / C::KN_CPR;
             const int c = (lane % C::KN_CPR) ^ (ESZ == 1 ? swz_kn8(kr, C::KN_CPR) : swz_kn(kr, C::KN_CPR));
@@ -205,9 +219,12 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             rowB_cp[i] = kr;
             chB_cp[i] = n0 + c * EPC;
             srcB[i] = gB + ((int64_t)kr * p.ldb + gn) * ESZ;
+            voB[i] = (uint32_t)(((int64_t)kr * p.ldb + (gn - n0)) * ESZ);
         }
     }
     const int64_t stepA = (int64_t)BK * ESZ;
+    const uint8_t* baseA = gA + (int64_t)m0 * p.lda * ESZ;
+    const uint8_t* baseB = OPB == GE_OP_T ? gB + (int64_t)n0 * p.ldb * ESZ : gB + (int64_t)n0 * ESZ;
     const int64_t stepB = (OPB == GE_OP_T) ? (int64_t)BK * ESZ : (int64_t)BK * p.ldb * ESZ;
 
     // MX block scales: lane l of scale copy c fetches, at step t, the 4 bytes
@@ -237,10 +254,10 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
         uint8_t* sa = smem + (t % SE) * C::A_BYTES;                      // A stages first,
         uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;    // then B stages
         if (c < C::A_INS)
-            copy_to_lds16(srcA[c] + (int64_t)t * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
+            copy_to_lds16_sb(voA[c], baseA + (int64_t)t * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
         else if (c < C::A_INS + C::B_INS)
-            copy_to_lds16(srcB[c - C::A_INS] + (int64_t)t * stepB,
-                          lds_addr(sb + (wave * C::B_INS + c - C::A_INS) * 1024));
+            copy_to_lds16_sb(voB[c - C::A_INS], baseB + (int64_t)t * stepB,
+                             lds_addr(sb + (wave * C::B_INS + c - C::A_INS) * 1024));
         else if constexpr (MX) {
             const int sc = c - C::A_INS - C::B_INS;   // scale copy: A rows first, then B columns
             const uint8_t* src = sc < C::SCA ? srcSA[sc] : srcSB[sc - C::SCA];
@@ -557,6 +574,118 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             mfmas(a1, b1, sa1, sb1);
         }
     } else {
+    if constexpr (C::SPREAD) {
+    // ---- main loop, copies spread among the MFMAs ----
+    // Step kt reads stage kt % SE.  Its sub-step regions also issue the
+    // copies of step kt + SE - 1 into stage (kt - 1) % SE, which every wave
+    // finished reading before the barrier of step kt - 1.  Each region puts
+    // its share of the copies between its fragment reads, so that the
+    // address unit takes them while the matrix cores run: issued in one
+    // burst, they hold back every wave's next MFMA behind the copy queue.
+    // The prologue starts SE - 1 steps; the last steps fall back to one
+    // burst per step with the counted waits of the burst loop.
+    constexpr int VM = C::VM_PER_STEP;
+    constexpr int CPR = VM / C::NKK;   // copies per sub-step region
+#pragma unroll
+    for (int t = 0; t < SE - 1; ++t)
+        if (t < KT) issue(t);
+    Frag a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    uint32_t sa0[C::FM], sb0[C::FN], sa1[C::FM], sb1[C::FN];   // MX scale words of each set
+    if (KT > 0) {
+        wait_step(min(SE - 2, KT - 1));
+        load_frags(0, 0, a0, b0, sa0, sb0);
+    }
+    auto reads_first = [&]() {
+        if constexpr (C::FM * C::FN < 4) __builtin_amdgcn_sched_barrier(0);
+    };
+    // one region: the fragment reads of sub-step rkk of stage rst into
+    // (ra, rb), with NC copies of step ct (numbers c0 ..) placed evenly
+    // between them, then the MFMAs of (ma, mb)
+    auto region = [&](auto nc_c, int rst, int rkk, Frag (&ra)[C::FM], Frag (&rb)[C::FN], uint32_t (&rsa)[C::FM],
+                      uint32_t (&rsb)[C::FN], const Frag (&ma)[C::FM], const Frag (&mb)[C::FN],
+                      const uint32_t (&msa)[C::FM], const uint32_t (&msb)[C::FN], int ct, int c0)
+        __attribute__((always_inline)) {
+        constexpr int NC = decltype(nc_c)::value;
+        constexpr int R = C::FN + C::FM;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r < C::FN) load_fragB(rst, rkk, r, rb);
+            else load_fragA(rst, rkk, r - C::FN, ra);
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const int pos = min(max((j + 1) * R / (NC + 1) - 1, 0), R - 1);
+                if (pos == r) copy_one(ct, c0 + j);
+            }
+        }
+        if constexpr (MX) {
+#pragma unroll
+            for (int f = 0; f < C::FM; ++f) rsa[f] = load_scale(rst, rkk, f * 32 + r32);
+#pragma unroll
+            for (int f = 0; f < C::FN; ++f) rsb[f] = load_scale(rst, rkk, C::SCA * 64 + f * 32 + r32);
+        }
+        reads_first();
+        mfmas(ma, mb, msa, msb);
+        interleave();
+    };
+    auto step_spread = [&](int kt, int stage) __attribute__((always_inline)) {
+        const int ct = kt + SE - 1;
+#pragma unroll
+        for (int kk = 0; kk < C::NKK - 1; ++kk) {
+            if (kk % 2 == 0)
+                region(std::integral_constant<int, CPR>{}, stage, kk + 1, a1, b1, sa1, sb1, a0, b0, sa0, sb0, ct,
+                       kk * CPR);
+            else
+                region(std::integral_constant<int, CPR>{}, stage, kk + 1, a0, b0, sa0, sb0, a1, b1, sa1, sb1, ct,
+                       kk * CPR);
+        }
+        // step kt + 1 has landed once only the copies issued after it are
+        // outstanding: steps kt + 2 .. kt + SE - 2 and this step's regions'
+        // share of step kt + SE - 1
+        wait_vm<(SE - 3) * VM + (C::NKK - 1) * CPR>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads done
+        asm volatile("s_barrier" ::: "memory");
+        region(std::integral_constant<int, VM - (C::NKK - 1) * CPR>{}, (stage + 1) % SE, 0, a0, b0, sa0, sb0, a1,
+               b1, sa1, sb1, ct, (C::NKK - 1) * CPR);
+    };
+    auto inner = [&](int stage) {
+#pragma unroll
+        for (int kk = 0; kk < C::NKK - 1; ++kk) {
+            if (kk % 2 == 0) {
+                load_frags(stage, kk + 1, a1, b1, sa1, sb1);
+                reads_first();
+                mfmas(a0, b0, sa0, sb0);
+            } else {
+                load_frags(stage, kk + 1, a0, b0, sa0, sb0);
+                reads_first();
+                mfmas(a1, b1, sa1, sb1);
+            }
+            interleave();
+        }
+    };
+    auto step_last = [&](int kt, int stage) {
+        if (kt + SE - 1 < KT) issue(kt + SE - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        inner(stage);
+        wait_step(min(SE - 2, KT - 2 - kt));
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags((stage + 1) % SE, 0, a0, b0, sa0, sb0);
+        reads_first();
+        mfmas(a1, b1, sa1, sb1);   // the last sub-step (NKK - 1 is odd)
+        interleave();
+    };
+    int kt = 0;
+    // SE steps per iteration (constant stage offsets), each issuing the
+    // copies of a full step
+    for (; kt + 2 * SE - 2 < KF; kt += SE) {
+#pragma unroll
+        for (int u = 0; u < SE; ++u) step_spread(kt + u, u);
+    }
+    for (; kt < KT - 1; ++kt) step_last(kt, kt % SE);
+    if (KT > 0) {
+        inner((KT - 1) % SE);
+        mfmas(a1, b1, sa1, sb1);
+    }
+    } else {
     // ---- main loop ----
     // All SE stages start filling at once; afterwards the copy of step
     // kt + SE goes into the stage step kt used, as soon as every wave has
@@ -625,6 +754,7 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
         inner((KT - 1) % SE);
         mfmas(a1, b1, sa1, sb1);
     }
+    }   // spread or burst copies
     }   // copy mode
 
     if constexpr (SPLIT) {

@@ -46,6 +46,8 @@ def parse():
                    help="copies of the operands cycled through (defeats the 256 MiB MALL "
                         "for HBM-bound workloads); default 16 for the batch-16 Linear, else 1")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--group-m", type=int, default=0,
+                   help="tile rows per group of the launch order (0 = the planner's choice)")
     p.add_argument("--tile", type=int, default=0,
                    help="force a tile id of the planner (0 = its own choice)")
     p.add_argument("--autotune", action="store_true",
@@ -360,7 +362,7 @@ def run_workload(w, args, dev, with_unfused=True, tile=0, split_k=0, autotune=Fa
 
     t0 = time.perf_counter()
     g = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-    g.plan(w.epilog, w.axis, tile=tile, split_k=split_k)
+    g.plan(w.epilog, w.axis, tile=tile, split_k=split_k, group_m=getattr(args, 'group_m', 0))
     plan_us = (time.perf_counter() - t0) * 1e6
     outs = [g.alloc_outputs(dev) for _ in range(rot)]
     if autotune:
@@ -434,12 +436,12 @@ def run_workload(w, args, dev, with_unfused=True, tile=0, split_k=0, autotune=Fa
     unfused = None
     if with_unfused and w.epilog != "none":
         gu = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-        gu.plan(w.epilog, w.axis, unfused=1, tile=tile, split_k=split_k)
+        gu.plan(w.epilog, w.axis, unfused=1, tile=tile, split_k=split_k, group_m=getattr(args, 'group_m', 0))
         outs_u = [gu.alloc_outputs(dev) for _ in range(rot)]
         wall_u, durs_u = timed(lambda i: step(i, gu, outs_u))
         # the pair's first kernel alone: the product with no epilogue
         gp = B.GemmEpilog(w.m, w.n, w.k, w.in_dtype, w.out_dtype, w.op_b)
-        gp.plan("none", w.axis, tile=tile, split_k=split_k)
+        gp.plan("none", w.axis, tile=tile, split_k=split_k, group_m=getattr(args, 'group_m', 0))
         outs_p = [gp.alloc_outputs(dev) for _ in range(rot)]
         _, durs_p = timed(lambda i: step(i, gp, outs_p, with_aux_in=False))
         # the fused kernel once more after the pair, so that the comparison

@@ -191,12 +191,17 @@ typedef struct {
  *          input dtype does not support gives GE_ERR_SHAPE.  The automatic
  *          choice takes 14 for fp16/bf16 problems of at most 64 such tiles
  *          with k >= 4096.  15: the pipelined kernel at 256x128 with 8 waves.
- * split_k: 0 auto, else the number of K slices (small-m path, or tile 14) */
+ * split_k: 0 auto, else the number of K slices (small-m path, or tile 14)
+ * group_m: 0 auto, else the tile rows per group of the tile kernels' launch
+ *          order (tiles are taken a group of rows at a time, column by
+ *          column; a group of g rows keeps g row panels of A and the column
+ *          panels of B in flight per die's L2); ignored by the small-m path */
 typedef struct {
     int32_t path;
     int32_t unfused;
     int32_t tile;
     int32_t split_k;
+    int32_t group_m;
 } ge_pref;
 
 typedef struct ge_plan_s* ge_handle;
@@ -218,7 +223,10 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc);
  * TANH_BIAS); the automatic path takes the tile kernel for the others.
  * Errors: GE_ERR_NULL (h), GE_ERR_EPILOG (unknown epilogue or axis, or the
  * small-m path forced with a training-side epilogue), GE_ERR_SHAPE (an
- * unknown tile id or split in p), GE_ERR_ALIGN (batch > 1 with a COL bias
+ * unknown tile id, split or group in p; or a forced pipelined tile whose
+ * rows of A, or rows of B given n x k, span 4 GiB or more: its copies
+ * address them as 32-bit offsets from the tile's first row, so the
+ * automatic choice takes the register-staged kernel then), GE_ERR_ALIGN (batch > 1 with a COL bias
  * read by the epilogue and n * element size not a multiple of 16 bytes:
  * product b's bias, b*n values in, would not be 16-byte aligned). */
 int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pref* p);

@@ -294,8 +294,8 @@ def test_forced_launch_failure_hook(monkeypatch):
     (16, 4096, 4096, 0, "f16", "path=tile"),       # B given k x n: tile path
     (17, 4096, 4096, 1, "f16", "path=tile"),
     (16, 4096, 4096, 1, "f32", "path=tile"),
-    (8192, 8192, 8192, 0, "bf16", "tile=256x256 waves=2x4 tile_id=11 kernel=4 stages=2"),
-    (65536, 8192, 16384, 0, "bf16", "tile_id=11 kernel=4"),
+    (8192, 8192, 8192, 0, "bf16", "tile=256x256 waves=2x4 tile_id=6 kernel=2 stages=4"),
+    (65536, 8192, 16384, 0, "bf16", "tile_id=6 kernel=2 stages=4 grid=8192 group_m=4 "),
     (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=4x2 tile_id=15 kernel=2 stages=3"),
     (4096, 1024, 4096, 1, "f16", "tile_id=8 kernel=2"),
     (1024, 512, 2048, 0, "f16", "tile=64x64 waves=2x2 tile_id=13 kernel=4 stages=4"),
@@ -308,6 +308,61 @@ def test_planner_choices(m, n, k, op_b, a, expect):
     try:
         B.gemm_epilog_plan(h, "bias", "row")
         assert expect in B.gemm_epilog_describe(h)
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_group_order_preference():
+    """group_m: 0 = the planner's choice, n > 0 = n tile rows per group
+    (clamped to the tile rows there are), negative = GE_ERR_SHAPE."""
+    h = B.gemm_epilog_create(B.make_desc(4096, 4096, 1024, "bf16", "bf16", 0))
+    try:
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(0, 0, 0, 0, -1)) == B.GE_ERR_SHAPE
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(0, 0, 6, 0, 3))
+        assert " group_m=3 " in B.gemm_epilog_describe(h)
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(0, 0, 6, 0, 1000))
+        assert " group_m=16 " in B.gemm_epilog_describe(h)   # 4096 / 256 tile rows
+        B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(0, 0, 2, 0, 0))
+        assert " group_m=8 " in B.gemm_epilog_describe(h)    # register-staged tile
+    finally:
+        B.gemm_epilog_free(h)
+
+
+@pytest.mark.parametrize("a,op_b", [("bf16", 0), ("bf16", 1), ("e4m3", 1)])
+def test_pipelined_tiles_need_rows_within_4_gib(a, op_b):
+    """The pipelined tiles address a tile's rows as 32-bit offsets from its
+    first row: with rows of 128 MiB the automatic
+    plan takes the register-staged kernel and a forced pipelined tile is
+    refused; a span of exactly 4 GiB keeps the pipelined tile (the 4096 x
+    4096 plan takes 128-row tiles for bf16, 256-row ones for fp8)."""
+    big = 1 << 26 if a == "bf16" else 1 << 27   # 128 MiB per row
+    h = B.gemm_epilog_create(B.make_desc(4096, 4096, 64, a, "bf16", 0, lda=big))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert "kernel=1 " in B.gemm_epilog_describe(h)
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(0, 0, 5, 0)) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+    if op_b == 1:   # B given n x k: its rows count too
+        h = B.gemm_epilog_create(B.make_desc(4096, 4096, 64, a, "bf16", 1, ldb=big))
+        try:
+            B.gemm_epilog_plan(h, "bias", "row")
+            assert "kernel=1 " in B.gemm_epilog_describe(h)
+        finally:
+            B.gemm_epilog_free(h)
+    ok = 1 << 24   # 128 rows of 32 MiB (bf16) or 256 rows of 16 MiB (fp8): 4 GiB
+    h = B.gemm_epilog_create(B.make_desc(4096, 4096, 64, a, "bf16", op_b, lda=ok))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert "kernel=1 " not in B.gemm_epilog_describe(h)
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_block_scaled_plan_refuses_rows_beyond_4_gib():
+    h = B.gemm_epilog_create(B.make_desc(4096, 4096, 64, "mxf8", "bf16", 1, lda=1 << 26))
+    try:
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, None) == B.GE_ERR_SHAPE
     finally:
         B.gemm_epilog_free(h)
 
