@@ -60,6 +60,13 @@ class ge_pref(ctypes.Structure):
                 ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32), ("group_m", ctypes.c_int32)]
 
 
+class ge_batch_strides(ctypes.Structure):
+    """Per-product strides of a batched handle, in elements of each buffer's
+    type (aux: 32-bit words for the mask)."""
+    _fields_ = [("a", ctypes.c_int64), ("b", ctypes.c_int64), ("bias", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("aux", ctypes.c_int64)]
+
+
 class GemmEpilogError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -92,6 +99,8 @@ def lib():
         L.gemm_epilog_execute_c.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gemm_epilog_execute_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gemm_epilog_execute_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gemm_epilog_execute_m.argtypes = [vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gemm_epilog_set_batch_strides.argtypes = [vp, ctypes.POINTER(ge_batch_strides)]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
                   "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c",
@@ -165,6 +174,28 @@ def gemm_epilog_execute(h: int, A, B, bias, D, aux=None, scale_a=None, scale_b=N
                                      _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
                                      workspace_bytes, stream or None),
            "gemm_epilog_execute")
+
+
+def gemm_epilog_execute_m(h: int, m: int, A, B, bias, D, aux=None, scale_a=None, scale_b=None,
+                          workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """execute with m rows (0 <= m <= the handle's m), the plan unchanged."""
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if isinstance(workspace, torch.Tensor) else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    _check(lib().gemm_epilog_execute_m(h, m, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux),
+                                       _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
+                                       workspace_bytes, stream or None),
+           "gemm_epilog_execute_m")
+
+
+def gemm_epilog_set_batch_strides(h: int, strides: Optional[ge_batch_strides]) -> None:
+    """Per-product strides (elements) of a batched handle; None = packed."""
+    _check(lib().gemm_epilog_set_batch_strides(h, ctypes.byref(strides) if strides is not None else None),
+           "gemm_epilog_set_batch_strides")
 
 
 def gemm_epilog_execute_mx(h: int, A, B, a_scales, b_scales, bias, D, aux=None, scale_a=None, scale_b=None,

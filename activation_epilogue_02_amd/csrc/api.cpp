@@ -64,6 +64,8 @@ struct ge_plan_s {
     int32_t bgrad_parts = 0; // bias-gradient partials per entry
     ge_pref pref = {0, 0, 0, 0, 0};   // the preferences the plan was made with
     int64_t ldaux = 0;       // mask row stride, 32-bit words
+    bool bstr_set = false;   // per-product strides given (else packed)
+    ge_batch_strides bstr = {0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -413,23 +415,63 @@ int gemm_epilog_aux_ld(ge_handle h, int64_t* ld_bits) {
 // execute and execute_c: cin (NULL = no added term) is C in D's dtype with
 // row stride ldc, scaled by the device scalar *beta.  static_ws: the
 // workspace is the library's own array (execute_static), not the caller's.
+// Per-product byte strides of a launch (the packed layout unless the caller
+// set strides), validated: GE_OK or an error status.
+struct ProductStrides {
+    int64_t a, b, bias, d, aux, c, sa, sb;
+};
+
+static int product_strides(const ge_plan_s& h, int64_t ldc, ProductStrides* out) {
+    const ge_desc& d = h.d;
+    const int64_t ea = elem_size(d.a_type), ed = elem_size(d.d_type);
+    const bool aux_matrix = aux_is_matrix(h.epilog);
+    const int64_t aux_es = aux_matrix ? ed : 4;
+    const int64_t len = h.axis == GE_BIAS_ROW ? d.m : d.n;
+    const int64_t mx_ld = GE_MX_SCALE_LD(d.k);
+    ge_batch_strides s = {d.m * d.lda, (d.op_b == GE_OP_N ? d.k : d.n) * d.ldb, len, d.m * d.ldd,
+                          d.m * h.ldaux};
+    if (h.bstr_set && d.batch > 1) {
+        s = h.bstr;
+        // inputs: any stride (0 shares one operand); rows stay 16-byte aligned
+        if ((s.a * ea) % 16 || (s.b * ea) % 16 || (s.d * ed) % 16 || (s.aux * aux_es) % 16) return GE_ERR_ALIGN;
+        if (h.axis == GE_BIAS_COL && has_bias(h.epilog) && (s.bias * ed) % 16) return GE_ERR_ALIGN;
+        // outputs: no two products may write the same element
+        if (s.d < (d.m - 1) * d.ldd + d.n) return GE_ERR_SHAPE;
+        const bool aux_out = h.epilog == GE_EPILOG_RELU_AUX_BIAS || h.epilog == GE_EPILOG_GELU_AUX_BIAS;
+        if (aux_out && s.aux < d.m * h.ldaux) return GE_ERR_SHAPE;
+        if (is_bgrad(h.epilog) && s.bias < len) return GE_ERR_SHAPE;
+    }
+    out->a = s.a * ea;
+    out->b = s.b * ea;
+    out->bias = s.bias * ed;
+    out->d = s.d * ed;
+    out->aux = s.aux * aux_es;
+    out->c = d.m * ldc * ed;
+    out->sa = d.m * mx_ld;
+    out->sb = d.n * mx_ld;
+    return GE_OK;
+}
+
+// m_run < 0: the planned m; else the rows of this call (0 .. planned m).
 static int execute_impl(ge_handle h, const void* A, const void* B, const void* cin, int64_t ldc, const float* beta,
                         const void* bias, void* D, void* aux, const float* scale_a, const float* scale_b,
                         void* workspace, size_t workspace_bytes, void* stream, bool static_ws = false,
-                        const void* mx_a = nullptr, const void* mx_b = nullptr) {
+                        const void* mx_a = nullptr, const void* mx_b = nullptr, int64_t m_run = -1) {
     if (!h) return GE_ERR_NULL;
     if (!h->planned) return GE_ERR_STATE;
     const ge_desc& d = h->d;
+    if (m_run > d.m) return GE_ERR_SHAPE;
+    const int64_t M = m_run >= 0 ? m_run : d.m;   // rows of this call
     // block-scaled fp8: the scales come with execute_mx, and only with it
     const bool mx = d.a_type == GE_MXF8_E4M3;
     if (!mx && (mx_a || mx_b)) return GE_ERR_DTYPE;
-    if (mx && ((!mx_a && d.m * d.k > 0) || (!mx_b && d.n * d.k > 0))) return GE_ERR_NULL;
+    if (mx && ((!mx_a && M * d.k > 0) || (!mx_b && d.n * d.k > 0))) return GE_ERR_NULL;
     if (!aligned(mx_a, 16) || !aligned(mx_b, 16)) return GE_ERR_ALIGN;
     // a pointer may be NULL only when its buffer holds no elements
-    if ((!A && d.m * d.k > 0) || (!B && d.k * d.n > 0) || (!D && d.m * d.n > 0)) return GE_ERR_NULL;
-    const int64_t bias_len = h->axis == GE_BIAS_ROW ? d.m : d.n;
+    if ((!A && M * d.k > 0) || (!B && d.k * d.n > 0) || (!D && M * d.n > 0)) return GE_ERR_NULL;
+    const int64_t bias_len = h->axis == GE_BIAS_ROW ? M : d.n;
     if ((has_bias(h->epilog) || is_bgrad(h->epilog)) && !bias && bias_len > 0) return GE_ERR_NULL;
-    const bool want_aux = has_aux(h->epilog) && d.m > 0 && d.n > 0;   // else aux holds nothing
+    const bool want_aux = has_aux(h->epilog) && M > 0 && d.n > 0;   // else aux holds nothing
     if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
     if (cin) {
@@ -439,6 +481,11 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(bias, 16) || !aligned(aux, 16) ||
         !aligned(workspace, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
         return GE_ERR_ALIGN;
+    ProductStrides ps;
+    {
+        const int st = product_strides(*h, cin ? ldc : 0, &ps);
+        if (st != GE_OK) return st;
+    }
     const size_t need = h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad;
     if (static_ws) {
         if (need > (size_t)GE_STATIC_WORKSPACE_BYTES) return GE_ERR_STATIC_LIMIT;
@@ -452,16 +499,17 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         if (st != GE_OK) return st;
         workspace_bytes = (size_t)GE_STATIC_WORKSPACE_BYTES;
     }
-    if (d.m == 0 || d.n == 0) {
+    if (M == 0 || d.n == 0) {
         // empty output; a bias gradient over no rows (or columns) is zero
         if (is_bgrad(h->epilog) && bias_len > 0) {
             KernelArgs z;
             memset(&z, 0, sizeof(z));
             z.bias = bias;
-            z.m = (int32_t)d.m;
+            z.m = (int32_t)M;
             z.n = (int32_t)d.n;
             z.axis = h->axis;
             z.batch = d.batch > 1 ? d.batch : 1;
+            z.bs_bias = ps.bias;
             if (launch_bgrad_reduce(d.d_type, z, 0, stream) != 0) return GE_ERR_HIP;
         }
         return GE_OK;
@@ -476,7 +524,7 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     a.aux = (uint32_t*)aux;
     a.scale_a = scale_a;
     a.scale_b = scale_b;
-    a.m = (int32_t)d.m;
+    a.m = (int32_t)M;
     a.n = (int32_t)d.n;
     a.k = (int32_t)d.k;
     a.epilog = h->epilog;
@@ -490,11 +538,28 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     a.group_m = h->group_m;
     a.split_k = h->split_k;
     a.k_per_split = h->k_per_split;
-    // batched: the packed per-product strides, in bytes (counters: elements)
+    unsigned grid = h->grid;
+    int32_t bgrad_parts = h->bgrad_parts;
+    if (h->path != PATH_SMALLM && M != d.m) {
+        // fewer rows than planned: the same kernel over the tile rows there are
+        const TileShape* t = find_tile(h->tile_id);
+        a.tiles_m = (int32_t)ceil_div(M, t->bm);
+        grid = (unsigned)(a.tiles_m * (int64_t)a.tiles_n);
+        if (is_bgrad(h->epilog) && h->axis == GE_BIAS_COL)
+            bgrad_parts = (int32_t)(h->unfused ? ceil_div(M, 256) : a.tiles_m);
+    }
+    // batched: per-product strides in bytes (counters: elements); the
+    // workspace parts keep their planned (largest) size
     const int64_t len = h->axis == GE_BIAS_COL ? d.n : d.m;
     a.batch = d.batch > 1 ? d.batch : 1;
     a.bs_part = h->split_k > 1 ? h->part_bytes : (int64_t)h->bgrad_parts * len * (int64_t)sizeof(float);
     a.bs_cnt = h->n_counters;
+    a.bs_a = ps.a;
+    a.bs_b = ps.b;
+    a.bs_bias = ps.bias;
+    a.bs_d = ps.d;
+    a.bs_aux = ps.aux;
+    a.bs_c = ps.c;
     a.cin = cin;
     a.beta = beta;
     a.ldc = ldc;
@@ -516,16 +581,17 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         k1.aux = nullptr;
         k1.ldaux = 0;
         k1.D = ws;
+        k1.bs_d = M * d.ldd * elem_size(d.d_type);   // packed, as the second kernel reads it
     }
     int err;
     if (h->path == PATH_SMALLM) {
-        err = launch_smallm(d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
+        err = launch_smallm(d.a_type, d.d_type, d.op_b, k1, grid, stream);
     } else if (mx) {
         const MxArgs mxa = {(const uint8_t*)mx_a, (const uint8_t*)mx_b, (int32_t)GE_MX_SCALE_LD(d.k),
-                            (int32_t)ceil_div(d.k, 32)};
-        err = launch_tile_mx(h->tile_id, d.d_type, d.op_b, k1, mxa, h->grid, stream);
+                            (int32_t)ceil_div(d.k, 32), ps.sa, ps.sb};
+        err = launch_tile_mx(h->tile_id, d.d_type, d.op_b, k1, mxa, grid, stream);
     } else {
-        err = launch_tile(h->tile_id, d.a_type, d.d_type, d.op_b, k1, h->grid, stream);
+        err = launch_tile(h->tile_id, d.a_type, d.d_type, d.op_b, k1, grid, stream);
     }
     if (err != 0) return GE_ERR_HIP;
     if (h->unfused) {
@@ -533,10 +599,10 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         err = launch_elementwise(d.d_type, a, ws, stream);
         if (err != 0) return GE_ERR_HIP;
         // the bias gradient of the stored D
-        if (is_bgrad(h->epilog) && launch_bgrad_sum(d.d_type, a, h->bgrad_parts, stream) != 0)
+        if (is_bgrad(h->epilog) && launch_bgrad_sum(d.d_type, a, bgrad_parts, stream) != 0)
             return GE_ERR_HIP;
     }
-    if (is_bgrad(h->epilog) && launch_bgrad_reduce(d.d_type, a, h->bgrad_parts, stream) != 0) return GE_ERR_HIP;
+    if (is_bgrad(h->epilog) && launch_bgrad_reduce(d.d_type, a, bgrad_parts, stream) != 0) return GE_ERR_HIP;
     return GE_OK;
 }
 
@@ -562,6 +628,28 @@ int gemm_epilog_execute_mx(ge_handle h, const void* A, const void* B, const void
     if (h->d.a_type != GE_MXF8_E4M3) return GE_ERR_DTYPE;
     return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
                         stream, false, a_scales, b_scales);
+}
+
+int gemm_epilog_execute_m(ge_handle h, int64_t m, const void* A, const void* B, const void* bias, void* D,
+                          void* aux, const float* scale_a, const float* scale_b, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!h) return GE_ERR_NULL;
+    if (m < 0 || m > h->d.m) return GE_ERR_SHAPE;
+    if (h->d.a_type == GE_MXF8_E4M3) return GE_ERR_DTYPE;   // block scales come with execute_mx
+    return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
+                        stream, false, nullptr, nullptr, m);
+}
+
+int gemm_epilog_set_batch_strides(ge_handle h, const ge_batch_strides* s) {
+    if (!h) return GE_ERR_NULL;
+    if (!s) {
+        h->bstr_set = false;
+        return GE_OK;
+    }
+    if (s->a < 0 || s->b < 0 || s->bias < 0 || s->d < 0 || s->aux < 0) return GE_ERR_SHAPE;
+    h->bstr = *s;
+    h->bstr_set = true;
+    return GE_OK;
 }
 
 int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias, void* D, void* aux,

@@ -30,7 +30,7 @@ __host__ __device__ inline int64_t ew_chunks_per_row(const KernelArgs& p) {
 template <int DT>
 __global__ void __launch_bounds__(kEwThreads) ge_ew_kernel(KernelArgs p_all, const void* c_all) {
     // this product of a batch; its intermediate C sits at D's per-product offset
-    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.y, 0);
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);
     const void* c = (const uint8_t*)c_all + (int64_t)blockIdx.y * p_all.m * p_all.ldd * Elem<DT>::size;
     const int64_t cpr = ew_chunks_per_row(p);
     const int ep = p.epilog;
@@ -141,7 +141,7 @@ int launch_elementwise(int d_type, const KernelArgs& args, const void* c, void* 
 // of 256 rows (COL: partial[rb * n + j]) or 256 columns (ROW: partial[cb * m + i]).
 template <int DT>
 __global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.z, 0);   // this product
+    const KernelArgs p = batch_slice(p_all, blockIdx.z);   // this product
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int blk = blockIdx.y;
     if (p.axis == GE_BIAS_COL) {
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(256) ge_sum_kernel(KernelArgs p_all) {
 // gradient's output).  parts = 0 writes zeros (an empty sum).
 template <int DT>
 __global__ void __launch_bounds__(256) ge_bgrad_reduce(KernelArgs p_all, int parts) {
-    const KernelArgs p = batch_slice<Elem<DT>::size, Elem<DT>::size>(p_all, blockIdx.y, 0);   // this product
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product
     const int len = p.axis == GE_BIAS_COL ? p.n : p.m;
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= len) return;

@@ -29,42 +29,33 @@ struct KernelArgs {
     int32_t group_m;       // tile-rows per group in the launch order
     int32_t split_k;       // K slices (small-m path)
     int32_t k_per_split;   // K elements per slice, multiple of the k step
-    // batched launches: the product's index comes from the launch grid and
-    // its operands follow the packed strides (see batch_slice); only the
-    // workspace parts' strides are stored: bytes of partials, counters
+    // batched launches: the product's index z comes from the launch grid;
+    // product z's buffers start z * bs_* bytes after product 0's (a stride
+    // of 0 shares one input between all products); counters: elements
     int32_t batch;
     int64_t bs_part, bs_cnt;
+    int64_t bs_a, bs_b, bs_bias, bs_d, bs_aux, bs_c;
     // the added input term beta*C (gemm_epilog_execute_c): C in D's dtype
     // with row stride ldc elements, beta a device scalar; cin NULL = none
     const void* cin;
     const float* beta;
     int64_t ldc;
 };
-// (The block is passed by value and copied by batch_slice; kept small on
-// purpose: a larger copy made the compiler place the tile kernel's
-// accumulators in scratch memory, 10% slower.)
-
-// The arguments of product z of a batched launch, whose buffers are packed
-// back to back: A z*m*lda, B z*rows_b*ldb (rows_b = k for B given k x n, n
-// for n x k), bias z*len (len = m for ROW, n for COL), D z*m*ldd, C z*m*ldc
-// elements; aux z*m*ldaux words (mask) or elements of D (pre-activation);
-// the workspace parts by their stored strides.  EA, ED: element bytes of the
-// inputs and of D.
-template <int EA, int ED>
-__host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z, int64_t rows_b) {
+// The arguments of product z of a batched launch: each buffer advanced by
+// its per-product stride (bytes; counters in elements).  (The block is
+// passed by value; the copy batch_slice makes is taken apart by the
+// compiler, since only z == 0 skips the offsets.)
+__host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z) {
     KernelArgs q = p;
     if (z == 0) return q;
-    const int64_t m = p.m, len = p.axis == GE_BIAS_COL ? p.n : p.m;
-    const bool aux_matrix = p.epilog == GE_EPILOG_GELU_AUX_BIAS || p.epilog == GE_EPILOG_DGELU ||
-                            p.epilog == GE_EPILOG_DGELU_BGRAD;
-    q.A = p.A ? (const void*)((const uint8_t*)p.A + z * m * p.lda * EA) : nullptr;
-    q.B = p.B ? (const void*)((const uint8_t*)p.B + z * rows_b * p.ldb * EA) : nullptr;
-    q.bias = p.bias ? (const void*)((const uint8_t*)p.bias + z * len * ED) : nullptr;
-    q.D = p.D ? (void*)((uint8_t*)p.D + z * m * p.ldd * ED) : nullptr;
-    q.aux = p.aux ? (uint32_t*)((uint8_t*)p.aux + z * m * p.ldaux * (aux_matrix ? ED : 4)) : nullptr;
+    q.A = p.A ? (const void*)((const uint8_t*)p.A + z * p.bs_a) : nullptr;
+    q.B = p.B ? (const void*)((const uint8_t*)p.B + z * p.bs_b) : nullptr;
+    q.bias = p.bias ? (const void*)((const uint8_t*)p.bias + z * p.bs_bias) : nullptr;
+    q.D = p.D ? (void*)((uint8_t*)p.D + z * p.bs_d) : nullptr;
+    q.aux = p.aux ? (uint32_t*)((uint8_t*)p.aux + z * p.bs_aux) : nullptr;
     q.partial = p.partial ? (float*)((uint8_t*)p.partial + z * p.bs_part) : nullptr;
     q.counters = p.counters ? p.counters + z * p.bs_cnt : nullptr;
-    q.cin = p.cin ? (const void*)((const uint8_t*)p.cin + z * m * p.ldc * ED) : nullptr;
+    q.cin = p.cin ? (const void*)((const uint8_t*)p.cin + z * p.bs_c) : nullptr;
     return q;
 }
 
@@ -73,12 +64,13 @@ __host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z
 // consecutive K values, for each row of A (sa: m rows) and each column of B
 // (sb: n rows, whichever layout B has), rows of `ld` bytes (a multiple of
 // 16); kb = ceil(k / 32) blocks are valid in a row.  Product z of a batch
-// reads sa + z*m*ld and sb + z*n*ld.
+// reads sa + z*bs_sa and sb + z*bs_sb (bytes).
 struct MxArgs {
     const uint8_t* sa;
     const uint8_t* sb;
     int32_t ld;
     int32_t kb;
+    int64_t bs_sa, bs_sb;
 };
 
 // Kernel families.

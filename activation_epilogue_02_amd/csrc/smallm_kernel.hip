@@ -73,7 +73,7 @@ __device__ __forceinline__ u32x4 sm_load_masked(const uint16_t* row, int col, in
 
 template <int DIN, int DOUT>
 __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice<2, Elem<DOUT>::size>(p_all, blockIdx.y, p_all.n);   // this product
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product
     __shared__ f32x4 red[kSmWaves][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, q = lane >> 4;

@@ -153,8 +153,7 @@ __device__ __forceinline__ int swz_row(int row) {
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, bool REG, int RB, bool SPLIT = false,
           bool MX = false>
 __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all, MxArgs mx_all) {
-    const KernelArgs p = batch_slice<Elem<DIN>::size, Elem<DOUT>::size>(   // this product of a batch
-        p_all, blockIdx.y, OPB == GE_OP_N ? p_all.k : p_all.n);
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
     using C = Tile2Cfg<DIN, DOUT, OPB, BM, BN, WM, WN, S, REG, RB, MX>;
     constexpr int BK = C::BK, SE = C::SE, ESZ = C::ESZ, EPC = C::EPC;
     using Frag = typename std::conditional<ESZ == 1, i32x8, u32x4>::type;
@@ -234,8 +233,8 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     const uint8_t* srcSA[C::SCA > 0 ? C::SCA : 1];
     const uint8_t* srcSB[C::SCB > 0 ? C::SCB : 1];
     if constexpr (MX) {
-        const uint8_t* sa = mx_all.sa + (int64_t)blockIdx.y * p.m * mx_all.ld;
-        const uint8_t* sb = mx_all.sb + (int64_t)blockIdx.y * p.n * mx_all.ld;
+        const uint8_t* sa = mx_all.sa + (int64_t)blockIdx.y * mx_all.bs_sa;
+        const uint8_t* sb = mx_all.sb + (int64_t)blockIdx.y * mx_all.bs_sb;
 #pragma unroll
         for (int c = 0; c < C::SCA; ++c)
             srcSA[c] = sa + (int64_t)min(m0 + wm * C::TM + 64 * c + lane, max(M - 1, 0)) * mx_all.ld;

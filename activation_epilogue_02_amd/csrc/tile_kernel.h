@@ -116,8 +116,7 @@ __device__ __forceinline__ void tile_coords(const KernelArgs& p, int& tm, int& t
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM* WN * 64)
 ge_tile_kernel(KernelArgs p_all) {
-    const KernelArgs p = batch_slice<Elem<DIN>::size, Elem<DOUT>::size>(   // this product of a batch
-        p_all, blockIdx.y, OPB == GE_OP_N ? p_all.k : p_all.n);
+    const KernelArgs p = batch_slice(p_all, blockIdx.y);   // this product of a batch
     using C = TileCfg<DIN, DOUT, OPB, BM, BN, WM, WN>;
     constexpr int ESZ = C::ESZ, BK = C::BK, E = C::E, NT = C::NT;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];

@@ -156,11 +156,12 @@ typedef enum { GE_BIAS_ROW = 0, GE_BIAS_COL = 1 } ge_bias_axis;
  * bias_type must equal d_type (for every epilogue): there is no implicit
  * conversion (nvmath page, paragraph on dtype agreement).
  * batch: 0 or 1 for one product; B > 1 (at most 65535) for B independent
- * products of the same shape and epilogue in one launch, their buffers
- * packed back to back: product b reads A + b*m*lda, B + b*k*ldb (N) or
- * b*n*ldb (T), the bias (or writes the bias gradient) at b*len (len = m for
- * ROW, n for COL), writes D + b*m*ldd and aux + b*m*(aux_ld_bits/8) bytes
- * (all offsets in elements of the buffer's dtype unless stated).  The fp8
+ * products of the same shape and epilogue in one launch.  By default their
+ * buffers are packed back to back: product b reads A + b*m*lda, B + b*k*ldb
+ * (N) or b*n*ldb (T), the bias (or writes the bias gradient) at b*len (len =
+ * m for ROW, n for COL), writes D + b*m*ldd and aux + b*m*(aux_ld_bits/8)
+ * bytes (all offsets in elements of the buffer's dtype unless stated);
+ * gemm_epilog_set_batch_strides sets other strides per operand.  The fp8
  * scales are shared.  The workspace scales with B. */
 typedef struct {
     int64_t m, n, k;
@@ -320,6 +321,42 @@ int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const 
                                void* D, void* aux, const float* scale_a, const float* scale_b,
                                void* stream);
 
+/* Per-product strides of a batched handle (batch > 1), in elements of each
+ * buffer's type (aux: 32-bit words for the mask, D's dtype for the
+ * pre-activation matrix): product z uses A + z*a, B + z*b, bias + z*bias,
+ * D + z*d, aux + z*aux.  This is the strided-batch layout of the pages'
+ * batched matmul (nvmath page, batched and strided operands; cuBLASLt page,
+ * batch count and strides).  An input's stride may be anything >= 0; 0
+ * shares one operand (a weight, a bias) between all products.  Outputs must
+ * not overlap: d >= (m-1)*ldd + n, aux >= m * aux_ld_bits/32 words (the
+ * mask's or pre-activation's rows as the plan lays them out), and a bias
+ * gradient's stride >= its length.  Every stride times the element size
+ * must keep 16-byte alignment (the operands' rows are read 16 bytes at a
+ * time), except a ROW bias's, which is read one element at a time.  The
+ * C input of execute_c stays packed (m*ldc elements per product).
+ * s = NULL returns to the packed layout.  Strides are checked when execute
+ * runs (they depend on the plan's epilogue).
+ * Errors: GE_ERR_NULL (h), GE_ERR_SHAPE (a negative stride); at execute:
+ * GE_ERR_ALIGN (a misaligned stride), GE_ERR_SHAPE (overlapping outputs). */
+typedef struct {
+    int64_t a, b, bias, d, aux;
+} ge_batch_strides;
+int gemm_epilog_set_batch_strides(ge_handle h, const ge_batch_strides* s);
+
+/* execute with m rows, 0 <= m <= the m the handle was created with (the
+ * dynamic-shape case of the NVGEMM page's upgrade checklist: one plan
+ * serves every batch of rows up to its maximum, with no re-planning).  The
+ * planned kernel, tile and launch order are kept; only the grid follows m.
+ * A, D, the ROW bias and the aux rows hold m rows; with batch > 1 the
+ * products stay where the planned m puts them (product z at z*m_max*lda,
+ * ...), or at the strides set.  The workspace size of the plan suffices.
+ * Errors: those of execute; GE_ERR_SHAPE (m < 0 or above the planned m);
+ * GE_ERR_DTYPE for block-scaled handles (their scales come with
+ * execute_mx). */
+int gemm_epilog_execute_m(ge_handle h, int64_t m, const void* A, const void* B, const void* bias,
+                          void* D, void* aux, const float* scale_a, const float* scale_b,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* execute for GE_MXF8_E4M3 handles (block-scaled fp8).  Arguments as for
  * execute, plus the block scales:
  *   a_scales  device, m rows of GE_MX_SCALE_LD(k) bytes: byte b of row i is
@@ -337,6 +374,8 @@ int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const 
  * execute_static and autotune on an MXF8_E4M3 handle return GE_ERR_NULL
  * (the scales are missing). */
 #define GE_MX_SCALE_LD(k) ((((k) + 31) / 32 + 15) / 16 * 16)
+/* (batched MX: the scale arrays stay packed, z*m*ld and z*n*ld bytes, with
+ * or without gemm_epilog_set_batch_strides) */
 int gemm_epilog_execute_mx(ge_handle h, const void* A, const void* B, const void* a_scales,
                            const void* b_scales, const void* bias, void* D, void* aux,
                            const float* scale_a, const float* scale_b, void* workspace,

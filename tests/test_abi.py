@@ -540,3 +540,71 @@ def test_mx_dtype_validation_and_planner():
         B.gemm_epilog_free(h)
     assert B.mx_scale_ld(1) == 16 and B.mx_scale_ld(512) == 16 and B.mx_scale_ld(513) == 32
     assert B.mx_scale_ld(16384) == 512
+
+
+def test_batch_strides_validation(monkeypatch):
+    """set_batch_strides checks signs; execute checks overlap and alignment
+    before any launch (the hook stops a call that passed validation)."""
+    monkeypatch.setenv("GE_TEST_FAIL_LAUNCH", "1")
+    m, n, k, nb = 64, 48, 32, 3
+    S = B.ge_batch_strides
+    assert B.lib().gemm_epilog_set_batch_strides(None, None) == B.GE_ERR_NULL
+    h = B.gemm_epilog_create(B.make_desc(m, n, k, "bf16", "bf16", 0, batch=nb))
+    try:
+        B.gemm_epilog_plan(h, "relu_aux_bias", "col")
+        ldw = B.gemm_epilog_aux_ld(h) // 32
+        ex = lambda: status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE, FAKE)
+        assert status_of(B.gemm_epilog_set_batch_strides, h, S(-1, 0, 0, m * n, m * ldw)) == B.GE_ERR_SHAPE
+        # shared weight and bias, gaps between products: valid
+        B.gemm_epilog_set_batch_strides(h, S(m * k + 8, 0, 0, m * n + n, m * ldw + 4))
+        assert ex() == B.GE_ERR_HIP
+        # D of two products would overlap
+        B.gemm_epilog_set_batch_strides(h, S(m * k, 0, 0, m * n - 8, m * ldw))
+        assert ex() == B.GE_ERR_SHAPE
+        # the mask rows of two products would overlap
+        B.gemm_epilog_set_batch_strides(h, S(m * k, 0, 0, m * n, m * ldw - 4))
+        assert ex() == B.GE_ERR_SHAPE
+        # a product's A, D or mask rows would not start 16-byte aligned
+        for s in (S(m * k + 1, 0, 0, m * n, m * ldw), S(m * k, 0, 0, m * n + 4, m * ldw),
+                  S(m * k, 0, 0, m * n, m * ldw + 1), S(m * k, 4, 0, m * n, m * ldw)):
+            B.gemm_epilog_set_batch_strides(h, s)
+            assert ex() == B.GE_ERR_ALIGN, (s.a, s.b, s.d, s.aux)
+        # a COL bias is read 16 bytes at a time
+        B.gemm_epilog_set_batch_strides(h, S(m * k, 0, n + 1, m * n, m * ldw))
+        assert ex() == B.GE_ERR_ALIGN
+        # a ROW bias one element at a time: any stride
+        B.gemm_epilog_plan(h, "relu_aux_bias", "row")
+        B.gemm_epilog_set_batch_strides(h, S(m * k, 0, m + 1, m * n, m * ldw))
+        assert ex() == B.GE_ERR_HIP
+        # a bias gradient (an output) needs its own n entries per product
+        B.gemm_epilog_plan(h, "drelu_bgrad", "col")
+        B.gemm_epilog_set_batch_strides(h, S(m * k, 0, n - 8, m * n, m * ldw))
+        assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE, FAKE, workspace=FAKE,
+                         workspace_bytes=1 << 30) == B.GE_ERR_SHAPE
+        # back to the packed layout
+        B.gemm_epilog_set_batch_strides(h, None)
+        B.gemm_epilog_plan(h, "relu_aux_bias", "col")
+        assert ex() == B.GE_ERR_HIP
+    finally:
+        B.gemm_epilog_free(h)
+
+
+def test_execute_m_validation(monkeypatch):
+    monkeypatch.setenv("GE_TEST_FAIL_LAUNCH", "1")
+    h = B.gemm_epilog_create(B.make_desc(100, 64, 32, "bf16", "bf16", 0))
+    try:
+        ex = lambda m: status_of(B.gemm_epilog_execute_m, h, m, FAKE, FAKE, FAKE, FAKE)
+        assert ex(10) == B.GE_ERR_STATE   # not planned
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert ex(101) == B.GE_ERR_SHAPE
+        assert ex(-1) == B.GE_ERR_SHAPE
+        assert ex(100) == B.GE_ERR_HIP and ex(37) == B.GE_ERR_HIP and ex(0) == B.GE_ERR_HIP
+        assert status_of(B.gemm_epilog_execute_m, h, 37, FAKE, FAKE, None, FAKE) == B.GE_ERR_NULL   # bias
+    finally:
+        B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(100, 64, 32, "mxf8", "bf16", 1))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert status_of(B.gemm_epilog_execute_m, h, 50, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_DTYPE
+    finally:
+        B.gemm_epilog_free(h)
