@@ -5,10 +5,12 @@ and compare.
 Two gates, both applied to every compared output element:
 
 * the relative Frobenius error of D against the unrounded float64 oracle
-  result: fp32 output 1e-5; fp16/bf16 output 5e-3.  fp8-e4m3 inputs are held
-  to the same output-dtype tolerance here, because the oracle is the exact
-  product of the quantised codes (the contract's looser 5e-2 bounds the error
-  against the unquantised draw, which is reported, not gated);
+  result: fp32 output 1e-5; fp16/bf16 output 5e-3; fp8 and block-scaled fp8
+  inputs 5e-3 on every output dtype.  The oracle is the exact product of the
+  quantised codes (the contract's looser 5e-2 bounds the error against the
+  unquantised draw, which is reported, not gated), but the fp8 matrix-core
+  instruction sums each 64-product block more coarsely than fp32 (see
+  FP8_BLOCK_U), so fp32 output of fp8 inputs cannot be held to 1e-5;
 * a bound on each element: the standard forward error bound of a dot product
   in fp32 (Higham, "Accuracy and Stability of Numerical Algorithms", section
   3.1: |fl(a.b) - a.b| <= gamma_n |a|.|b|, gamma_n = n u / (1 - n u)) with
