@@ -316,7 +316,7 @@ def assert_mask_exact_with_ties(w, r):
 
 
 @pytest.mark.parametrize("tile,a", [(1, "bf16"), (11, "bf16"), (13, "bf16"), (15, "bf16"),
-                                    (15, "e4m3"), (11, "e4m3"), (14, "bf16")])
+                                    (15, "e4m3"), (11, "e4m3"), (14, "bf16"), (6, "bf16"), (6, "e4m3")])
 @pytest.mark.parametrize("op_b", [0, 1])
 def test_relu_aux_tie_rule_tiles(tile, a, op_b):
     w = wl(300, 520, 200 if a == "bf16" else 456, a, "bf16", "relu_aux_bias", "row", op_b, seed=tile)
