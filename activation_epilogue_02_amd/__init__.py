@@ -13,6 +13,7 @@ from .binding import (GE_BIAS_COL, GE_BIAS_ROW, GE_EPILOG_BIAS, GE_EPILOG_DGELU,
                       gemm_epilog_describe, gemm_epilog_execute, gemm_epilog_execute_c,
                       gemm_epilog_execute_static, gemm_epilog_execute_mx, mx_scale_ld,
                       gemm_epilog_execute_m, gemm_epilog_set_batch_strides, ge_batch_strides,
+                      gemm_epilog_set_fp8_output,
                       gemm_epilog_free, gemm_epilog_plan,
                       gemm_epilog_status_string, gemm_epilog_workspace_size, ge_desc, ge_pref,
                       make_desc)

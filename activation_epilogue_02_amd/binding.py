@@ -101,6 +101,7 @@ def lib():
         L.gemm_epilog_execute_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gemm_epilog_execute_m.argtypes = [vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gemm_epilog_set_batch_strides.argtypes = [vp, ctypes.POINTER(ge_batch_strides)]
+        L.gemm_epilog_set_fp8_output.argtypes = [vp, vp, vp]
         for f in ("gemm_epilog_create", "gemm_epilog_plan", "gemm_epilog_workspace_size",
                   "gemm_epilog_aux_ld", "gemm_epilog_execute", "gemm_epilog_free",
                   "gemm_epilog_describe", "gemm_epilog_autotune", "gemm_epilog_execute_c",
@@ -128,7 +129,8 @@ def make_desc(m, n, k, a_type, d_type, op_b=GE_OP_N, lda=None, ldb=None, ldd=Non
     a = DTYPE_CODE[a_type] if not isinstance(a_type, int) else a_type
     d = DTYPE_CODE[d_type] if not isinstance(d_type, int) else d_type
     b = a if b_type is None else (DTYPE_CODE[b_type] if not isinstance(b_type, int) else b_type)
-    bt = d if bias_type is None else (DTYPE_CODE[bias_type] if not isinstance(bias_type, int) else bias_type)
+    bt = ((DTYPE_CODE["bf16"] if d == DTYPE_CODE["e4m3"] else d) if bias_type is None
+          else (DTYPE_CODE[bias_type] if not isinstance(bias_type, int) else bias_type))
     return ge_desc(m, n, k, a, b, d, bt, op_b, batch,
                    k if lda is None else lda,
                    (n if op_b == GE_OP_N else k) if ldb is None else ldb,
@@ -190,6 +192,12 @@ def gemm_epilog_execute_m(h: int, m: int, A, B, bias, D, aux=None, scale_a=None,
                                        _ptr(scale_a), _ptr(scale_b), _ptr(workspace),
                                        workspace_bytes, stream or None),
            "gemm_epilog_execute_m")
+
+
+def gemm_epilog_set_fp8_output(h: int, scale_d=None, amax_d=None) -> None:
+    """fp8 (E4M3) output: D's scale (device fp32, None = 1) and the amax
+    output (device fp32 per product, or None)."""
+    _check(lib().gemm_epilog_set_fp8_output(h, _ptr(scale_d), _ptr(amax_d)), "gemm_epilog_set_fp8_output")
 
 
 def gemm_epilog_set_batch_strides(h: int, strides: Optional[ge_batch_strides]) -> None:

@@ -23,6 +23,7 @@ SOURCES = ["api.cpp", "tile_launch.hip", "tile_f32.hip", "tile_f16.hip", "tile_b
            "tile2_f16_f16.hip", "tile2_f16_f32.hip", "tile2_bf16_bf16.hip", "tile2_bf16_f32.hip",
            "tile2_f8_bf16.hip", "tile2_f8_f16.hip", "tile2_f8_f32.hip",
            "tile2_mx_bf16.hip", "tile2_mx_f16.hip", "tile2_mx_f32.hip",
+           "tile2_bf16_f8.hip", "tile2_f16_f8.hip", "tile2_f8_f8.hip", "tile2_mx_f8.hip",
            "smallm_kernel.hip", "ew_kernel.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -66,6 +66,8 @@ struct ge_plan_s {
     int64_t ldaux = 0;       // mask row stride, 32-bit words
     bool bstr_set = false;   // per-product strides given (else packed)
     ge_batch_strides bstr = {0, 0, 0, 0, 0};
+    const float* scale_d = nullptr;   // fp8 output: D's scale (NULL = 1)
+    float* amax_d = nullptr;          // fp8 output: largest |y| per product, or NULL
 };
 
 namespace {
@@ -85,10 +87,10 @@ bool dtype_combo_ok(int a, int b, int d) {
     if (a != b) return false;
     switch (a) {
     case GE_F32: return d == GE_F32;
-    case GE_F16: return d == GE_F16 || d == GE_F32;
-    case GE_BF16: return d == GE_BF16 || d == GE_F32;
+    case GE_F16: return d == GE_F16 || d == GE_F32 || d == GE_F8_E4M3;
+    case GE_BF16: return d == GE_BF16 || d == GE_F32 || d == GE_F8_E4M3;
     case GE_F8_E4M3:
-    case GE_MXF8_E4M3: return d == GE_BF16 || d == GE_F16 || d == GE_F32;
+    case GE_MXF8_E4M3: return d == GE_BF16 || d == GE_F16 || d == GE_F32 || d == GE_F8_E4M3;
     }
     return false;
 }
@@ -137,9 +139,16 @@ int choose_tile_plain(int64_t m, int64_t n) {
 // two tiles (256 CUs); below that, the shape with the most tiles.  Large
 // tiles halve the L2 -> LDS traffic per flop; small problems need the
 // parallelism more than the reuse.
-int choose_tile(int64_t m, int64_t n, int a_type) {
+int choose_tile(int64_t m, int64_t n, int a_type, int d_type) {
     const int64_t t256 = ceil_div(m, 256) * ceil_div(n, 256);
     const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128);
+    // fp8 output: the tiles instantiated for it (the large one when it
+    // gives every CU a tile, else 128 x 128)
+    if (d_type == GE_F8_E4M3) {
+        if (a_type == GE_MXF8_E4M3) return 8;
+        if (a_type == GE_F8_E4M3) return ceil_div(m, 256) * ceil_div(n, 128) >= 512 ? 15 : 8;
+        return t256 >= 256 ? 6 : 8;
+    }
     // block-scaled fp8: the one tile the block-scaled MFMA compiles into
     // without register spills
     if (a_type == GE_MXF8_E4M3) return 8;
@@ -194,7 +203,12 @@ int32_t auto_group_m(const TileShape* t, int64_t tm, int a_type) {
 
 // The pipelined kernel takes 16-bit and fp8 inputs (its 64 x 64 tile only
 // 16-bit ones); block-scaled fp8 runs on its 128 x 128 tile only.
-bool tile_supports(const TileShape* t, int a_type) {
+bool tile_supports(const TileShape* t, int a_type, int d_type) {
+    if (d_type == GE_F8_E4M3) {   // fp8 output: the instantiated tiles only
+        if (a_type == GE_MXF8_E4M3) return t->id == 8;
+        if (a_type == GE_F8_E4M3) return t->id == 15 || t->id == 8;
+        return t->id == 6 || t->id == 8;
+    }
     if (a_type == GE_MXF8_E4M3) return t->id == 8;
     if (t->kernel == 1) return true;
     if (t->id == 13 || t->id == 14) return a_type == GE_F16 || a_type == GE_BF16;
@@ -244,7 +258,8 @@ int gemm_epilog_create(ge_handle* h, const ge_desc* desc) {
     if (d.m > INT32_MAX || d.n > INT32_MAX || d.k > INT32_MAX) return GE_ERR_SHAPE;
     if (d.batch < 0 || d.batch > 65535 || (d.op_b != GE_OP_N && d.op_b != GE_OP_T)) return GE_ERR_SHAPE;
     if (!dtype_combo_ok(d.a_type, d.b_type, d.d_type)) return GE_ERR_DTYPE;
-    if (d.bias_type != d.d_type) return GE_ERR_DTYPE;
+    // the bias follows D's dtype; for fp8 D it is bf16
+    if (d.bias_type != (d.d_type == GE_F8_E4M3 ? GE_BF16 : d.d_type)) return GE_ERR_DTYPE;
     if (d.lda < d.k || d.ldd < d.n) return GE_ERR_SHAPE;
     if (d.ldb < (d.op_b == GE_OP_N ? d.n : d.k)) return GE_ERR_SHAPE;
     if ((d.lda * elem_size(d.a_type)) % 16 || (d.ldb * elem_size(d.b_type)) % 16 ||
@@ -274,6 +289,12 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     q.epilog = epilog;
     q.axis = bias_axis;
     q.unfused = (pr.unfused && epilog != GE_EPILOG_NONE) ? 1 : 0;
+    // fp8 output serves the inference epilogues in the fused kernel (no aux
+    // matrix in D's dtype, no backward epilogue, no fp8 intermediate)
+    if (d.d_type == GE_F8_E4M3) {
+        const bool inference = epilog <= GE_EPILOG_GELU_BIAS || epilog == GE_EPILOG_TANH_BIAS;
+        if (!inference || q.unfused) return GE_ERR_DTYPE;
+    }
     // aux row stride: round_up(n, 128) bits (mask, in 32-bit words) or
     // elements (pre-activation matrix)
     q.ldaux = !has_aux(epilog) ? 0
@@ -284,7 +305,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     // a batch takes product z's bias at z * len values: with a column bias
     // whose n values are not a whole number of 16-byte chunks, every other
     // product's bias would start misaligned for the kernels' 16-byte loads
-    if (d.batch > 1 && bias_axis == GE_BIAS_COL && has_bias(epilog) && (d.n * elem_size(d.d_type)) % 16 != 0)
+    if (d.batch > 1 && bias_axis == GE_BIAS_COL && has_bias(epilog) && (d.n * elem_size(d.bias_type)) % 16 != 0)
         return GE_ERR_ALIGN;
 
     // the small-m kernel serves the inference epilogues only
@@ -320,7 +341,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
             q.ws_counters = round_up(nbs * (size_t)q.n_counters * sizeof(uint32_t), 256);
         }
     } else {
-        q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n, d.a_type);
+        q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n, d.a_type, d.d_type);
         // the automatic split-K 64 x 64 tile serves problems with so few tiles
         // (at most a quarter of the CUs) and so long a K that the slices'
         // parallelism outweighs their partial exchange, which costs about as
@@ -331,9 +352,9 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
             ceil_div(d.m, 64) * ceil_div(d.n, 64) <= 64)
             q.tile_id = 14;
         const TileShape* t = find_tile(q.tile_id);
-        if (!tile_supports(t, d.a_type)) return GE_ERR_SHAPE;
+        if (!tile_supports(t, d.a_type, d.d_type)) return GE_ERR_SHAPE;
         if (!tile_span_ok(t, d)) {
-            if (pr.tile || d.a_type == GE_MXF8_E4M3) return GE_ERR_SHAPE;
+            if (pr.tile || d.a_type == GE_MXF8_E4M3 || d.d_type == GE_F8_E4M3) return GE_ERR_SHAPE;
             q.tile_id = choose_tile_plain(d.m, d.n);
             t = find_tile(q.tile_id);
         }
@@ -423,7 +444,7 @@ struct ProductStrides {
 
 static int product_strides(const ge_plan_s& h, int64_t ldc, ProductStrides* out) {
     const ge_desc& d = h.d;
-    const int64_t ea = elem_size(d.a_type), ed = elem_size(d.d_type);
+    const int64_t ea = elem_size(d.a_type), ed = elem_size(d.d_type), eb = elem_size(d.bias_type);
     const bool aux_matrix = aux_is_matrix(h.epilog);
     const int64_t aux_es = aux_matrix ? ed : 4;
     const int64_t len = h.axis == GE_BIAS_ROW ? d.m : d.n;
@@ -434,7 +455,7 @@ static int product_strides(const ge_plan_s& h, int64_t ldc, ProductStrides* out)
         s = h.bstr;
         // inputs: any stride (0 shares one operand); rows stay 16-byte aligned
         if ((s.a * ea) % 16 || (s.b * ea) % 16 || (s.d * ed) % 16 || (s.aux * aux_es) % 16) return GE_ERR_ALIGN;
-        if (h.axis == GE_BIAS_COL && has_bias(h.epilog) && (s.bias * ed) % 16) return GE_ERR_ALIGN;
+        if (h.axis == GE_BIAS_COL && has_bias(h.epilog) && (s.bias * eb) % 16) return GE_ERR_ALIGN;
         // outputs: no two products may write the same element
         if (s.d < (d.m - 1) * d.ldd + d.n) return GE_ERR_SHAPE;
         const bool aux_out = h.epilog == GE_EPILOG_RELU_AUX_BIAS || h.epilog == GE_EPILOG_GELU_AUX_BIAS;
@@ -443,7 +464,7 @@ static int product_strides(const ge_plan_s& h, int64_t ldc, ProductStrides* out)
     }
     out->a = s.a * ea;
     out->b = s.b * ea;
-    out->bias = s.bias * ed;
+    out->bias = s.bias * eb;
     out->d = s.d * ed;
     out->aux = s.aux * aux_es;
     out->c = d.m * ldc * ed;
@@ -475,6 +496,7 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     if (aux && !has_aux(h->epilog)) return GE_ERR_EPILOG;
     if (want_aux && !aux) return GE_ERR_EPILOG;
     if (cin) {
+        if (h->d.d_type == GE_F8_E4M3) return GE_ERR_DTYPE;
         if (ldc < h->d.n) return GE_ERR_SHAPE;
         if ((ldc * elem_size(h->d.d_type)) % 16 || !aligned(cin, 16) || !aligned(beta, 4)) return GE_ERR_ALIGN;
     }
@@ -499,6 +521,10 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
         if (st != GE_OK) return st;
         workspace_bytes = (size_t)GE_STATIC_WORKSPACE_BYTES;
     }
+    // fp8 output: amax starts from 0 at every call (a kernel, so that the
+    // call can be captured in a HIP graph)
+    if (h->amax_d && launch_clear_counters((uint32_t*)h->amax_d, d.batch > 1 ? d.batch : 1, stream) != 0)
+        return GE_ERR_HIP;
     if (M == 0 || d.n == 0) {
         // empty output; a bias gradient over no rows (or columns) is zero
         if (is_bgrad(h->epilog) && bias_len > 0) {
@@ -563,6 +589,8 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     a.cin = cin;
     a.beta = beta;
     a.ldc = ldc;
+    a.scale_d = h->scale_d;
+    a.amax = h->amax_d;
     uint8_t* ws = (uint8_t*)workspace;
     if (h->split_k > 1) {
         a.partial = (float*)(ws + h->ws_c);
@@ -638,6 +666,15 @@ int gemm_epilog_execute_m(ge_handle h, int64_t m, const void* A, const void* B, 
     if (h->d.a_type == GE_MXF8_E4M3) return GE_ERR_DTYPE;   // block scales come with execute_mx
     return execute_impl(h, A, B, nullptr, 0, nullptr, bias, D, aux, scale_a, scale_b, workspace, workspace_bytes,
                         stream, false, nullptr, nullptr, m);
+}
+
+int gemm_epilog_set_fp8_output(ge_handle h, const float* scale_d, float* amax_d) {
+    if (!h) return GE_ERR_NULL;
+    if (h->d.d_type != GE_F8_E4M3) return GE_ERR_DTYPE;
+    if (!aligned(scale_d, 4) || !aligned(amax_d, 4)) return GE_ERR_ALIGN;
+    h->scale_d = scale_d;
+    h->amax_d = amax_d;
+    return GE_OK;
 }
 
 int gemm_epilog_set_batch_strides(ge_handle h, const ge_batch_strides* s) {

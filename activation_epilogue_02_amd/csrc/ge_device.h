@@ -58,6 +58,27 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
     return r;
 }
 
+// fp32 -> OCP E4M3 (E4 M3, bias 7, no infinities, 0x7F = NaN), round to
+// nearest even, saturating: magnitudes that round above the largest finite
+// value 448 (and infinities) give +-448, NaN gives 0x7F with the sign.
+// Written from the format definition: the quantum is 2^(e-3) for a value in
+// [2^e, 2^(e+1)), e >= -6, and the subnormal quantum 2^-9 below 2^-6.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = __builtin_fabsf(x);
+    if (!(a == a)) return sign | 0x7fu;
+    if (a >= 448.0f) return sign | 0x7eu;   // ties at 464 round to 448 too
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    if (e < -6) e = -6;
+    int n = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - e));   // exact scaling, RNE
+    if (n >= 16) {   // carried into the next binade
+        n >>= 1;
+        e += 1;
+    }
+    const uint32_t code = n < 8 ? (uint32_t)n : ((uint32_t)(e + 7) << 3) | (uint32_t)(n - 8);
+    return sign | code;
+}
+
 // Pack 8 fp32 values into 16 bytes of 16-bit outputs.
 template <int DT>
 __device__ __forceinline__ u32x4 pack8_16bit(const float* v) {
@@ -80,7 +101,8 @@ __device__ __forceinline__ u32x4 pack8_16bit(const float* v) {
 // Store one converted element.
 template <int DT>
 __device__ __forceinline__ void store_one(void* D, int64_t idx, float v) {
-    if constexpr (DT == GE_F32) ((float*)D)[idx] = v;
+    if constexpr (DT == GE_F8_E4M3) ((uint8_t*)D)[idx] = (uint8_t)f32_to_e4m3_sat(v);
+    else if constexpr (DT == GE_F32) ((float*)D)[idx] = v;
     else if constexpr (DT == GE_BF16) ((uint16_t*)D)[idx] = f32_to_bf16_bits(v);
     else ((uint16_t*)D)[idx] = f32_to_f16_bits(v);
 }
@@ -89,7 +111,16 @@ __device__ __forceinline__ void store_one(void* D, int64_t idx, float v) {
 // 32-byte span for fp32).
 template <int DT>
 __device__ __forceinline__ void store8(void* D, int64_t idx, const float* v) {
-    if constexpr (DT == GE_F32) {
+    if constexpr (DT == GE_F8_E4M3) {   // 8 bytes
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= f32_to_e4m3_sat(v[i]) << (8 * i);
+            hi |= f32_to_e4m3_sat(v[4 + i]) << (8 * i);
+        }
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        *(u32x2_t*)((uint8_t*)D + idx) = u32x2_t{lo, hi};
+    } else if constexpr (DT == GE_F32) {
         u32x4 a, b;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { a[i] = __float_as_uint(v[i]); b[i] = __float_as_uint(v[4 + i]); }

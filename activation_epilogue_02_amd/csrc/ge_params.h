@@ -40,6 +40,10 @@ struct KernelArgs {
     const void* cin;
     const float* beta;
     int64_t ldc;
+    // fp8 output (E4M3 D): D = E4M3(y * *scale_d) (NULL = 1); amax, if not
+    // NULL, receives the largest |y| of each product (one float per product)
+    const float* scale_d;
+    float* amax;
 };
 // The arguments of product z of a batched launch: each buffer advanced by
 // its per-product stride (bytes; counters in elements).  (The block is
@@ -56,6 +60,7 @@ __host__ __device__ inline KernelArgs batch_slice(const KernelArgs& p, int64_t z
     q.partial = p.partial ? (float*)((uint8_t*)p.partial + z * p.bs_part) : nullptr;
     q.counters = p.counters ? p.counters + z * p.bs_cnt : nullptr;
     q.cin = p.cin ? (const void*)((const uint8_t*)p.cin + z * p.bs_c) : nullptr;
+    q.amax = p.amax ? p.amax + z : nullptr;
     return q;
 }
 

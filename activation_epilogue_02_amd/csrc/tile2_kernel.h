@@ -822,13 +822,20 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     const bool bgrad_col = p.axis == GE_BIAS_COL;
     BgradAcc<C::FM, C::FN> bg;
     bg.clear();
+    // fp8 output: the bias is bf16; D = E4M3(y * scale_d), and the largest
+    // |y| of the product goes to *amax (inference epilogues only: the host
+    // refuses the C input, the aux matrix and the backward epilogues)
+    constexpr bool OUT8 = DOUT == GE_F8_E4M3;
+    constexpr int DB = OUT8 ? GE_BF16 : DOUT;
+    const float sd = (OUT8 && p.scale_d) ? *p.scale_d : 1.0f;
+    float amax_l = 0.0f;
 
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
         const int m = m0 + wm * C::TM + fm * 32 + r32;
         const bool mok = m < M;
         float brow = 0.0f;
-        if (has_bias && row_bias && mok) brow = load_scalar<DOUT>(p.bias, m);
+        if (has_bias && row_bias && mok) brow = load_scalar<DB>(p.bias, m);
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
             const int nb = n0 + wn * C::TN + fn * 32;
@@ -853,22 +860,21 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
 #pragma unroll
                 for (int j = 0; j < 8; ++j) bc[j] = brow;
                 if (has_bias && !row_bias) {
-                    if (full) load8<DOUT>(p.bias, nc, bc);
+                    if (full) load8<DB>(p.bias, nc, bc);
                     else {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DOUT>(p.bias, nc + j) : 0.0f;
+                        for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DB>(p.bias, nc + j) : 0.0f;
                     }
                 }
                 float gf[8], pre[8], cb[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) cb[j] = 0.0f;
-                if (with_c && mok) beta_c8<DOUT>(p, beta, m, nc, cb);
-                if (want_grad) {
-                    if (mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
-                    else {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) gf[j] = 0.0f;
-                    }
+                for (int j = 0; j < 8; ++j) {
+                    cb[j] = 0.0f;
+                    gf[j] = 0.0f;
+                }
+                if constexpr (!OUT8) {
+                    if (with_c && mok) beta_c8<DOUT>(p, beta, m, nc, cb);
+                    if (want_grad && mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -885,6 +891,14 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
                         else bg.row[fm] += val;
                     }
                 }
+                if constexpr (OUT8) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float av = __builtin_fabsf(v[g][j]);   // NaN compares false: not counted
+                        if (mok && nc + j < N && av > amax_l) amax_l = av;
+                        v[g][j] *= sd;
+                    }
+                }
                 if (mok) {
                     const int64_t idx = (int64_t)m * p.ldd + nc;
                     if (full) store8<DOUT>(p.D, idx, v[g]);
@@ -893,13 +907,29 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
                         for (int j = 0; j < 8; ++j)
                             if (nc + j < N) store_one<DOUT>(p.D, idx + j, v[g][j]);
                     }
-                    if (want_pre) store_pre8<DOUT>(p, m, nc, pre);
+                    if constexpr (!OUT8) {
+                        if (want_pre) store_pre8<DOUT>(p, m, nc, pre);
+                    }
                 }
             }
             if (want_aux) {
                 bits |= (uint32_t)__shfl_xor((int)bits, 32);
                 if (h == 0 && mok && (nb >> 5) < p.ldaux) p.aux[(int64_t)m * p.ldaux + (nb >> 5)] = bits;
             }
+        }
+    }
+    if constexpr (OUT8) {
+        if (p.amax) {
+            // the wave's largest |y|, then one order-free atomic max per wave
+            // (the bit patterns of non-negative floats order as the values)
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float o = __shfl_xor(amax_l, d);
+                amax_l = o > amax_l ? o : amax_l;
+            }
+            if (lane == 0 && amax_l > 0.0f)
+                __hip_atomic_fetch_max((uint32_t*)p.amax, __float_as_uint(amax_l), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (want_bgrad)
@@ -953,6 +983,24 @@ Tile2Fn pick_tile2(int tile_id) {
         else return nullptr;
     }
     return nullptr;
+}
+
+// fp8 output (E4M3 D): the 256 x 256 8-wave tile and the 128 x 128 tile for
+// 16-bit inputs; the 256 x 128 tile and the 128 x 128 tile for fp8 inputs
+template <int DIN, int OPB>
+Tile2Fn pick_tile2_out8(int tile_id) {
+    if constexpr (Elem<DIN>::size == 2) {
+        if (tile_id == 6) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 256, 256, 2, 4, 4, false, 64>;
+    } else {
+        if (tile_id == 15) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 256, 128, 4, 2, 4, false, 64>;
+    }
+    if (tile_id == 8) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 128, 128, 2, 2, 4, false, 64>;
+    return nullptr;
+}
+
+template <int DIN>
+Tile2Fn pick_op2_out8(int op_b, int tile_id) {
+    return op_b == GE_OP_T ? pick_tile2_out8<DIN, GE_OP_T>(tile_id) : pick_tile2_out8<DIN, GE_OP_N>(tile_id);
 }
 
 template <int DIN, int DOUT>

@@ -473,5 +473,9 @@ Tile2Fn pick_tile2_f8_f32(int op_b, int tile_id);
 Tile2Fn pick_tile2_mx_f8_bf16(int op_b, int tile_id);
 Tile2Fn pick_tile2_mx_f8_f16(int op_b, int tile_id);
 Tile2Fn pick_tile2_mx_f8_f32(int op_b, int tile_id);
+Tile2Fn pick_tile2_bf16_f8(int op_b, int tile_id);   // fp8 (E4M3) output
+Tile2Fn pick_tile2_f16_f8(int op_b, int tile_id);
+Tile2Fn pick_tile2_f8_f8(int op_b, int tile_id);
+Tile2Fn pick_tile2_mx_f8_f8(int op_b, int tile_id);
 
 }  // namespace ge

@@ -20,6 +20,9 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
         else if (a_type == GE_F8_E4M3 && d_type == GE_BF16) fn = pick_tile2_f8_bf16(op_b, tile_id);
         else if (a_type == GE_F8_E4M3 && d_type == GE_F16) fn = pick_tile2_f8_f16(op_b, tile_id);
         else if (a_type == GE_F8_E4M3 && d_type == GE_F32) fn = pick_tile2_f8_f32(op_b, tile_id);
+        else if (a_type == GE_BF16 && d_type == GE_F8_E4M3) fn = pick_tile2_bf16_f8(op_b, tile_id);
+        else if (a_type == GE_F16 && d_type == GE_F8_E4M3) fn = pick_tile2_f16_f8(op_b, tile_id);
+        else if (a_type == GE_F8_E4M3 && d_type == GE_F8_E4M3) fn = pick_tile2_f8_f8(op_b, tile_id);
         if (!fn) return (int)hipErrorInvalidDeviceFunction;
         const MxArgs none = {nullptr, nullptr, 0, 0, 0, 0};
         hipLaunchKernelGGL(fn, dim3(grid, args.batch, slices), dim3(threads), 0, (hipStream_t)stream, args, none);
@@ -47,6 +50,7 @@ int launch_tile_mx(int tile_id, int d_type, int op_b, const KernelArgs& args, co
     if (d_type == GE_BF16) fn = pick_tile2_mx_f8_bf16(op_b, tile_id);
     else if (d_type == GE_F16) fn = pick_tile2_mx_f8_f16(op_b, tile_id);
     else if (d_type == GE_F32) fn = pick_tile2_mx_f8_f32(op_b, tile_id);
+    else if (d_type == GE_F8_E4M3) fn = pick_tile2_mx_f8_f8(op_b, tile_id);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     hipLaunchKernelGGL(fn, dim3(grid, args.batch, 1), dim3(t->wm * t->wn * 64), 0, (hipStream_t)stream, args, mx);
     return (int)hipGetLastError();

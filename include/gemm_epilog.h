@@ -149,12 +149,18 @@ typedef enum { GE_BIAS_ROW = 0, GE_BIAS_COL = 1 } ge_bias_axis;
 
 /* Problem description.  Supported dtype combinations (a_type == b_type):
  *   F32  inputs -> d_type F32
- *   F16  inputs -> d_type F16 or F32
- *   BF16 inputs -> d_type BF16 or F32
- *   E4M3 inputs -> d_type BF16, F16 or F32
- *   MXF8_E4M3 inputs -> d_type BF16, F16 or F32 (the 128 x 128 tile)
+ *   F16  inputs -> d_type F16, F32 or E4M3
+ *   BF16 inputs -> d_type BF16, F32 or E4M3
+ *   E4M3 inputs -> d_type BF16, F16, F32 or E4M3
+ *   MXF8_E4M3 inputs -> d_type BF16, F16, F32 or E4M3 (the 128 x 128 tile)
  * bias_type must equal d_type (for every epilogue): there is no implicit
- * conversion (nvmath page, paragraph on dtype agreement).
+ * conversion (nvmath page, paragraph on dtype agreement); with an E4M3 D
+ * the bias is BF16.  E4M3 output: D = E4M3(y * scale_d), y the activated
+ * fp32 value, rounded to nearest even and saturated to +-448 (NaN stays
+ * NaN); see gemm_epilog_set_fp8_output for scale_d and the amax output.
+ * It serves the inference epilogues (NONE, BIAS, RELU_BIAS, RELU_AUX_BIAS,
+ * GELU_BIAS, TANH_BIAS) in the fused kernel: the plan refuses the others,
+ * the unfused pair and execute_c with GE_ERR_DTYPE.
  * batch: 0 or 1 for one product; B > 1 (at most 65535) for B independent
  * products of the same shape and epilogue in one launch.  By default their
  * buffers are packed back to back: product b reads A + b*m*lda, B + b*k*ldb
@@ -320,6 +326,23 @@ int gemm_epilog_execute_c(ge_handle h, const void* A, const void* B, const void*
 int gemm_epilog_execute_static(ge_handle h, const void* A, const void* B, const void* bias,
                                void* D, void* aux, const float* scale_a, const float* scale_b,
                                void* stream);
+
+/* fp8 (E4M3) output of a handle whose d_type is GE_F8_E4M3.  The nvmath page
+ * lists FP8 among the supported dtypes and, in its closing paragraph, names
+ * fp8 epilogues as where fusion is going; it gives no output-scaling rule,
+ * and this one is the common fp8 inference reading.  scale_d (device, one
+ * fp32, NULL = 1) multiplies y before the conversion; amax_d (device, one
+ * fp32 per product of the batch, or NULL) receives max |y| over the
+ * product's outputs (before the scale; NaN values do not count; 0 for a
+ * product with no outputs), for a caller that derives the next scale from
+ * it (delayed scaling).  The
+ * library clears amax_d with a small kernel on the stream before each
+ * execute, and the kernel combines the waves' maxima with atomic max on
+ * the float's bits, so the result does not depend on the order.  The
+ * pointers are kept in the handle and used by every later execute.
+ * Errors: GE_ERR_NULL (h), GE_ERR_DTYPE (d_type is not E4M3), GE_ERR_ALIGN
+ * (a pointer not 4-byte aligned). */
+int gemm_epilog_set_fp8_output(ge_handle h, const float* scale_d, float* amax_d);
 
 /* Per-product strides of a batched handle (batch > 1), in elements of each
  * buffer's type (aux: 32-bit words for the mask, D's dtype for the

@@ -60,7 +60,10 @@ def status_of(fn, *a, **kw):
     (dict(a_type="f32", d_type="bf16"), B.GE_ERR_DTYPE),
     (dict(a_type="bf16", d_type="f16"), B.GE_ERR_DTYPE),
     (dict(a_type="f16", d_type="bf16"), B.GE_ERR_DTYPE),
-    (dict(a_type="e4m3", d_type="e4m3"), B.GE_ERR_DTYPE),
+    (dict(a_type="e4m3", d_type="e4m3", k=64, bias_type="e4m3"), B.GE_ERR_DTYPE),   # fp8 D takes a bf16 bias
+    (dict(a_type="f16", d_type="e4m3", bias_type="f16"), B.GE_ERR_DTYPE),
+    (dict(a_type="f32", d_type="e4m3"), B.GE_ERR_DTYPE),
+    (dict(d_type="e4m3", ldd=56), B.GE_ERR_ALIGN),   # 56-byte fp8 rows
     (dict(b_type="f16"), B.GE_ERR_DTYPE),
     (dict(bias_type="f32"), B.GE_ERR_DTYPE),
     (dict(a_type="e4m3", d_type="bf16", k=40), B.GE_ERR_ALIGN),   # 40-byte rows
@@ -510,10 +513,12 @@ def test_batched_column_bias_alignment():
 
 
 def test_mx_dtype_validation_and_planner():
-    """Block-scaled fp8: bf16/f16/f32 outputs, the 128 x 128 tile only; the
-    scales come with execute_mx, and only with it."""
+    """Block-scaled fp8: bf16/f16/f32/e4m3 outputs, the 128 x 128 tile only;
+    the scales come with execute_mx, and only with it."""
     assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "f16")) == B.GE_OK
-    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "e4m3")) == B.GE_ERR_DTYPE
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "e4m3", ldd=64)) == B.GE_OK
+    assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "e4m3", bias_type="e4m3")) == \
+        B.GE_ERR_DTYPE
     assert status_of(B.gemm_epilog_create, B.make_desc(64, 48, 64, "mxf8", "bf16", b_type="e4m3")) == B.GE_ERR_DTYPE
     h = B.gemm_epilog_create(B.make_desc(4096, 4096, 4096, "mxf8", "bf16"))
     try:
@@ -608,3 +613,39 @@ def test_execute_m_validation(monkeypatch):
         assert status_of(B.gemm_epilog_execute_m, h, 50, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_DTYPE
     finally:
         B.gemm_epilog_free(h)
+
+
+def test_fp8_output_validation(monkeypatch):
+    """E4M3 output: bf16 bias only, inference epilogues in the fused kernel,
+    the instantiated tiles, no C input; set_fp8_output on other handles."""
+    monkeypatch.setenv("GE_TEST_FAIL_LAUNCH", "1")
+    assert B.lib().gemm_epilog_create(ctypes.byref(ctypes.c_void_p()),
+                                      ctypes.byref(B.make_desc(64, 64, 64, "bf16", "e4m3", 0,
+                                                               bias_type="e4m3"))) == B.GE_ERR_DTYPE
+    for a in ("bf16", "f16", "e4m3", "mxf8"):
+        h = B.gemm_epilog_create(B.make_desc(256, 256, 64, a, "e4m3", 0))
+        try:
+            for ep in ("gelu_aux_bias", "drelu", "dgelu", "drelu_bgrad", "dgelu_bgrad"):
+                assert status_of(B.gemm_epilog_plan, h, ep, "row") == B.GE_ERR_DTYPE, (a, ep)
+            assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(0, 1, 0, 0)) == B.GE_ERR_DTYPE
+            assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(1, 0, 11, 0)) == B.GE_ERR_SHAPE
+            assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(1, 0, 2, 0)) == B.GE_ERR_SHAPE
+            B.gemm_epilog_plan(h, "relu_aux_bias", "row")
+            assert status_of(B.gemm_epilog_set_fp8_output, h, FAKE + 2, None) == B.GE_ERR_ALIGN
+            B.gemm_epilog_set_fp8_output(h, FAKE, FAKE + 4)
+            if a != "mxf8":
+                assert status_of(B.gemm_epilog_execute, h, FAKE, FAKE, FAKE, FAKE, FAKE) == B.GE_ERR_HIP
+                assert L_execute_c(h) == B.GE_ERR_DTYPE
+        finally:
+            B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(64, 64, 64, "bf16", "bf16", 0))
+    try:
+        assert status_of(B.gemm_epilog_set_fp8_output, h, None, None) == B.GE_ERR_DTYPE
+    finally:
+        B.gemm_epilog_free(h)
+    assert B.lib().gemm_epilog_set_fp8_output(None, None, None) == B.GE_ERR_NULL
+
+
+def L_execute_c(h):
+    return B.lib().gemm_epilog_execute_c(h, FAKE, FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, None, None, None, 0,
+                                         None)
