@@ -321,7 +321,18 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     if (path == PATH_SMALLM) {
         q.tile_id = 0;
         q.tiles_m = 1;
-        q.tiles_n = (int32_t)ceil_div(d.n, 16);
+        // column blocks of 16 * rg rows of W (rg row groups per wave, which
+        // share each x fragment).  Every workgroup reads all of x, as many
+        // load instructions per CU as its W slab needs, so two groups cut a
+        // CU's loads by a quarter; they pay when the 32-column blocks alone
+        // still fill the chip (measured at k = 4096: n = 8192 19.0 against
+        // 21.0 us, 16384 33.2 against 39.8 us; four groups no better).  A K
+        // split to make up the blocks does not: its partial exchange costs
+        // about 6 us (n = 4096: 14.5 us with two groups in two slices,
+        // 11.1 us with one group unsplit).
+        if (pr.group_m != 0 && pr.group_m != 1 && pr.group_m != 2 && pr.group_m != 4) return GE_ERR_SHAPE;
+        const int rg = pr.group_m > 0 ? pr.group_m : (ceil_div(d.n, 32) >= 256 ? 2 : 1);
+        q.tiles_n = (int32_t)ceil_div(d.n, 16 * rg);
         // K slices of whole 64-element spans (the kernel's load unit)
         const int64_t spans = ceil_div(d.k, 64);
         int split = pr.split_k > 0 ? pr.split_k : smallm_auto_split(q.tiles_n, spans);
@@ -329,14 +340,14 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.k_per_split = (int32_t)(ceil_div(spans, split) * 64);
         split = q.k_per_split > 0 ? (int)ceil_div(d.k, q.k_per_split) : 1;
         q.split_k = split;
-        q.group_m = 1;
+        q.group_m = rg;
         const int64_t grid = (int64_t)q.tiles_n * split;
         if (grid > INT32_MAX) return GE_ERR_SHAPE;
         q.grid = (unsigned)grid;
         if (split > 1) {
             const size_t nbs = d.batch > 1 ? (size_t)d.batch : 1;
             q.n_counters = q.tiles_n;
-            q.part_bytes = (int64_t)split * q.tiles_n * 256 * (int64_t)sizeof(float);
+            q.part_bytes = (int64_t)split * q.tiles_n * 256 * rg * (int64_t)sizeof(float);
             q.ws_partial = round_up(nbs * (size_t)q.part_bytes, 256);
             q.ws_counters = round_up(nbs * (size_t)q.n_counters * sizeof(uint32_t), 256);
         }
@@ -613,7 +624,7 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     }
     int err;
     if (h->path == PATH_SMALLM) {
-        err = launch_smallm(d.a_type, d.d_type, d.op_b, k1, grid, stream);
+        err = launch_smallm(d.a_type, d.d_type, d.op_b, h->group_m, k1, grid, stream);
     } else if (mx) {
         const MxArgs mxa = {(const uint8_t*)mx_a, (const uint8_t*)mx_b, (int32_t)GE_MX_SCALE_LD(d.k),
                             (int32_t)ceil_div(d.k, 32), ps.sa, ps.sb};
@@ -725,12 +736,14 @@ int gemm_epilog_autotune(ge_handle h, const void* A, const void* B, const void* 
     if (!h->planned) return GE_ERR_STATE;
     if (iters < 1) return GE_ERR_SHAPE;
     const ge_plan_s orig = *h;
-    // candidates: tile ids (tile path) or K splits (small-m path)
-    int cand[kNumTiles + 8];
+    // candidates: tile ids (tile path) or row groups x K splits (small-m
+    // path, encoded as 256 * row groups + split)
+    int cand[kNumTiles + 24];
     int nc = 0;
     if (orig.path == PATH_SMALLM) {
         const int64_t spans = ceil_div(orig.d.k, 64);
-        for (int s = 1; s <= 64 && s <= (spans > 0 ? spans : 1); s *= 2) cand[nc++] = s;
+        for (int rg = 1; rg <= 4; rg *= 2)
+            for (int s = 1; s <= 64 && s <= (spans > 0 ? spans : 1); s *= 2) cand[nc++] = 256 * rg + s;
     } else {
         for (int i = 0; i < kNumTiles; ++i) cand[nc++] = kTiles[i].id;
     }
@@ -747,7 +760,8 @@ int gemm_epilog_autotune(ge_handle h, const void* A, const void* B, const void* 
         ge_pref pr = orig.pref;
         if (orig.path == PATH_SMALLM) {
             pr.path = PATH_SMALLM;
-            pr.split_k = cand[c];
+            pr.group_m = cand[c] / 256;
+            pr.split_k = cand[c] % 256;
         } else {
             pr.path = PATH_TILE;
             pr.tile = cand[c];
@@ -805,7 +819,7 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
              "tile_id=%d kernel=%d stages=%d grid=%u group_m=%d split_k=%d unfused=%d workspace=%zu "
              "ldaux_words=%lld",
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
-             h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16, t ? t->wm : 1,
+             h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16 * h->group_m, t ? t->wm : 1,
              t ? t->wn : 8, h->tile_id, t ? t->kernel : 0,
              t ? (t->kernel >= 2 && t->kernel != 3 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
              h->split_k,

@@ -129,8 +129,9 @@ int launch_tile(int tile_id, int a_type, int d_type, int op_b, const KernelArgs&
 int launch_tile_mx(int tile_id, int d_type, int op_b, const KernelArgs& args, const MxArgs& mx,
                    unsigned grid, void* stream);
 
-// Launch the small-m streaming kernel.
-int launch_smallm(int a_type, int d_type, int op_b, const KernelArgs& args, unsigned grid,
+// Launch the small-m streaming kernel with rg (1, 2 or 4) groups of 16 W
+// rows per wave; args.tiles_n counts column blocks of 16 * rg rows.
+int launch_smallm(int a_type, int d_type, int op_b, int rg, const KernelArgs& args, unsigned grid,
                   void* stream);
 
 // Zero n split-K arrival counters on `stream` (a kernel, graph-capturable).

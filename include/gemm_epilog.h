@@ -202,7 +202,10 @@ typedef struct {
  * group_m: 0 auto, else the tile rows per group of the tile kernels' launch
  *          order (tiles are taken a group of rows at a time, column by
  *          column; a group of g rows keeps g row panels of A and the column
- *          panels of B in flight per die's L2); ignored by the small-m path */
+ *          panels of B in flight per die's L2).  Small-m path: 1, 2 or 4
+ *          groups of 16 rows of W per wave, which share each fragment of x
+ *          (a workgroup then covers 16, 32 or 64 output columns); any other
+ *          value gives GE_ERR_SHAPE */
 typedef struct {
     int32_t path;
     int32_t unfused;
@@ -418,8 +421,8 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap);
  * paragraph on limitations and the nvmath page's paragraph on timing both
  * suggest letting the library try its kernels when the default choice is not
  * fast enough).  Every candidate the plan's path and input dtype allow -- the
- * tile ids of the tile path, or the K splits 1, 2, 4, ... of the small-m
- * path -- is re-planned with the same epilogue, bias axis and unfused
+ * tile ids of the tile path, or the row groups 1, 2, 4 times the K splits
+ * 1, 2, 4, ... of the small-m path -- is re-planned with the same epilogue, bias axis and unfused
  * choice, run once, then `iters` times between two HIP events on `stream`;
  * the fastest replaces the plan (the shape heuristic's own choice is among
  * the candidates, so the result is never slower than it as measured).

@@ -208,7 +208,7 @@ def make_aux_input(w: synth.Workload, device="cuda", seed=None) -> torch.Tensor:
 def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int = 0,
                 unfused: int = 0, tile: int = 0, split_k: int = 0, poison=True,
                 device="cuda", lda=None, ldb=None, ldd=None, aux_in=None, cin=None, beta=None,
-                in_place=False):
+                in_place=False, group_m: int = 0):
     """Execute the planned op through the C ABI; returns (D_full, aux, h-desc, buffers)."""
     a_dt, d_dt = w.in_dtype, w.out_dtype
     ea, ed = ESZ[a_dt], ESZ[d_dt]
@@ -225,7 +225,7 @@ def run_library(w: synth.Workload, inp: synth.Inputs, *, pad: int = 0, path: int
     mxb = inp.mx_b.to(device).contiguous() if getattr(inp, "mx_b", None) is not None else None
     g = B.GemmEpilog(w.m, w.n, k_b, a_dt, d_dt, w.op_b, lda, ldb, ldd)
     try:
-        g.plan(w.epilog, w.axis, path=path, unfused=unfused, tile=tile, split_k=split_k)
+        g.plan(w.epilog, w.axis, path=path, unfused=unfused, tile=tile, split_k=split_k, group_m=group_m)
         desc = g.describe()
         D = torch.empty((w.m, ldd), dtype=synth.TORCH_DTYPE[d_dt], device=device)
         D.fill_(float("nan"))

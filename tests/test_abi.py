@@ -419,6 +419,24 @@ def test_split_k_tile_plan():
         B.gemm_epilog_free(h)
 
 
+def test_smallm_row_groups_plan():
+    """group_m on the small-m path: 1, 2 or 4 row groups per wave (blocks of
+    16 * g columns, partials of 256 * g floats per slice and block); other
+    values are refused."""
+    h = B.gemm_epilog_create(B.make_desc(16, 1000, 4096, "f16", "f16", 1))
+    try:
+        for g in (1, 2, 4):
+            B.gemm_epilog_plan(h, "gelu_bias", "col", B.ge_pref(2, 0, 0, 4, g))
+            s = B.gemm_epilog_describe(h)
+            tiles = (1000 + 16 * g - 1) // (16 * g)
+            assert f"tile=16x{16 * g} " in s and f"grid={tiles * 4} " in s and f"group_m={g} " in s, s
+            assert B.gemm_epilog_workspace_size(h) == 4 * tiles * 256 * g * 4 + ((tiles * 4 + 255) // 256) * 256
+        for g in (3, 8, -1):
+            assert status_of(B.gemm_epilog_plan, h, "gelu_bias", "col", B.ge_pref(2, 0, 0, 0, g)) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_smallm_split_workspace():
     h = B.gemm_epilog_create(B.make_desc(16, 4096, 4096, "f16", "f16", 1))
     try:
@@ -438,19 +456,24 @@ def test_smallm_split_workspace():
     (16, 128, 65536, 32),
     (4, 1024, 1024, 1),      # 32 K steps: 4 per wave leaves no room to split
     (1, 1024, 2048, 2),
+    (16, 8192, 4096, 1),     # two 16-row groups per wave: 256 blocks of 32 columns
+    (16, 8160, 4096, 1),     # 255 such blocks: one group
+    (16, 28672, 4096, 1),
 ])
 def test_smallm_auto_split(m, n, k, split):
     """Without a preference the small-m path splits K while the grid stays
-    within one workgroup per CU and each wave keeps >= 2 spans of 64 K values."""
+    within one workgroup per CU and each wave keeps >= 2 spans of 64 K values;
+    two row groups per wave once 32-column blocks fill the 256 CUs."""
     h = B.gemm_epilog_create(B.make_desc(m, n, k, "bf16", "bf16", 1))
     try:
         B.gemm_epilog_plan(h, "bias", "col")
         s = B.gemm_epilog_describe(h)
-        assert "path=smallm" in s and f"split_k={split} " in s, s
-        tiles_n = (n + 15) // 16
+        rg = 2 if (n + 31) // 32 >= 256 else 1
+        assert "path=smallm" in s and f"split_k={split} " in s and f"group_m={rg} " in s, s
+        tiles_n = (n + 16 * rg - 1) // (16 * rg)
         assert f"grid={tiles_n * split} " in s, s
         ws = B.gemm_epilog_workspace_size(h)
-        assert ws == (0 if split == 1 else split * tiles_n * 1024 + ((tiles_n * 4 + 255) // 256) * 256)
+        assert ws == (0 if split == 1 else split * tiles_n * rg * 1024 + ((tiles_n * 4 + 255) // 256) * 256)
         # an explicit preference still wins
         B.gemm_epilog_plan(h, "bias", "col", B.ge_pref(2, 0, 0, 1))
         assert "split_k=1 " in B.gemm_epilog_describe(h)

@@ -154,6 +154,47 @@ def test_smallm_path(m, n, k, a, d, split):
             check_full(w, r)
 
 
+@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("n,k", [(48, 1000), (1000, 4096), (272, 8200)])
+@pytest.mark.parametrize("rg", [2, 4])
+@pytest.mark.parametrize("split", [0, 3])
+def test_smallm_row_groups(m, n, k, rg, split):
+    """Two or four 16-row groups of W per wave sharing each x fragment: a
+    workgroup covers 32 or 64 columns, groups past n are clamped (their
+    outputs and mask bits never stored), with and without a K split."""
+    for ep, axis in (("gelu_bias", "col"), ("relu_aux_bias", "row"), ("bias", "col")):
+        w = wl(m, n, k, "bf16", "bf16", ep, axis, op_b=1, seed=m + n + rg)
+        r = run_library(w, synth.make_inputs(w), pad=1, path=2, split_k=split, group_m=rg)
+        assert "path=smallm" in r.desc and f"group_m={rg} " in r.desc, r.desc
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("m,n", [(5, 8200), (16, 8192)])
+def test_smallm_auto_row_groups(m, n):
+    """The planner's own choice of two row groups per wave once 32-column
+    blocks fill the chip (n >= 8161), ragged and whole."""
+    for ep, axis in (("gelu_bias", "col"), ("relu_aux_bias", "row")):
+        w = wl(m, n, 512, "f16", "f16", ep, axis, op_b=1, seed=n)
+        r = run_library(w, synth.make_inputs(w), pad=1)
+        assert "path=smallm" in r.desc and "group_m=2 " in r.desc, r.desc
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("rg,split", [(2, 2), (4, 4), (4, 1)])
+def test_smallm_row_groups_integer_bit_exact(rg, split):
+    """Integer inputs: every partial and slice sum is exact, so each row
+    group's outputs must equal the oracle's RNE encoding bit for bit."""
+    m, n, k = 16, 520, 8200
+    w = wl(m, n, k, "f16", "f16", "relu_aux_bias", "col", 1)
+    inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    r = run_library(w, inp, path=2, split_k=split, group_m=rg)
+    assert f"split_k={split} " in r.desc and f"group_m={rg} " in r.desc, r.desc
+    from parity import oracle_full
+    Y, P, _ = oracle_full(w, r)
+    assert np.array_equal(codes(r.D)[:, :n], oracle.encode(Y, "f16").reshape(Y.shape))
+    check_full(w, r)
+
+
 @pytest.mark.parametrize("m,n,k,split", [(16, 130, 8200, 8), (4, 128, 65560, 32), (1, 1000, 4096, 4)])
 def test_smallm_auto_split_ragged(m, n, k, split):
     """The planner's own K split (few column blocks, long K, a ragged last
