@@ -96,10 +96,11 @@ def autotuned_desc(w, inp, ws_bytes=None, **plan):
 
 
 def tuned_pref(desc):
-    """The tuned plan as preferences (tile id or K split) for a fresh plan."""
+    """The tuned plan as preferences (tile id, or row groups and K split) for
+    a fresh plan."""
     kv = dict(x.split("=", 1) for x in desc.split() if "=" in x)
     if kv["path"] == "smallm":
-        return dict(path=2, split_k=int(kv["split_k"]))
+        return dict(path=2, split_k=int(kv["split_k"]), group_m=int(kv["group_m"]))
     return dict(path=1, tile=int(kv["tile_id"]))
 
 
