@@ -139,11 +139,15 @@ struct Tile2Cfg {
     static_assert(!SPREAD || (SE - 3) * VM_PER_STEP + (NKK - 1) * (VM_PER_STEP / NKK) < 64, "vmcnt range");
 };
 
-// swizzle of the chunks of a ROWB-byte row (A, or B given n x k)
+// swizzle of the chunks of a ROWB-byte row (A, or B given n x k).  Both
+// depend on row bits 0-4 only: a fragment read covers 32 consecutive rows,
+// and rows 32 apart then share the swizzle, so the fragments of a wave tile
+// lie at constant offsets from each other (immediate offsets of the reads
+// rather than one address register per fragment)
 template <int ROWB>
 __device__ __forceinline__ int swz_row(int row) {
     if constexpr (ROWB == 64) return swz64(row);
-    else return lds_swz(row);   // 128-byte rows: as in tile_kernel.h
+    else return lds_swz(row & 31);   // 128-byte rows: eight rows cover the 8 chunk slots
 }
 
 // One kernel template for the plain and the block-scaled (MX) instantiations.
@@ -330,16 +334,17 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     // every lane by the E8M0 value of the row's lane half 0 and bytes 16-31 by
     // that of lane half 1 (measured), so each 32-value K block of the
     // instruction must be the two lane halves' 16-byte pieces.
-    int offA[C::FM][C::NKK][C::NRA];
-#pragma unroll
-    for (int f = 0; f < C::FM; ++f) {
-        const int row = wm * C::TM + f * 32 + r32;
+    // (fragment f of A sits 32 rows below fragment f - 1: offset
+    // offA[kk][e] + f * 32 * ROWB, the swizzle repeating every 32 rows)
+    int offA[C::NKK][C::NRA];
+    {
+        const int row = wm * C::TM + r32;
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
             for (int e = 0; e < C::NRA; ++e) {
                 const int chunk = ESZ == 1 ? 4 * kk + h + 2 * e : 2 * kk + h;
-                offA[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
+                offA[kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
             }
     }
     // B given n x k: as A.  B given k x n, transposing reads:
@@ -348,26 +353,33 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     //  fp8, read e of 4:    group G, lane i: k = 64kk + 16(G/2) + 32(e/2) +
     //          8(e%2) + i/2, n = wave col + 32f + 16(G%2) + 8(i%2)
     //          (the lane halves' K pieces as for A).
-    int offB[C::FN][C::NKK][C::NRB];
+    // (n x k: fragment f at offB[0][kk][e] + f * 32 * ROWB, as for A.
+    // k x n: the swizzles depend on k mod 4 (16-bit) or mod 8 (fp8) only, so
+    // the sub-steps and reads of a fragment lie at constant k-row offsets
+    // from its first read (kn_koff); one base per fragment, offB[f][0][0])
+    constexpr int NBF = OPB == GE_OP_T ? 1 : C::FN;
+    constexpr int NBK = OPB == GE_OP_T ? C::NKK : 1;
+    constexpr int NBE = OPB == GE_OP_T ? C::NRB : 1;
+    int offB[NBF][NBK][NBE];
 #pragma unroll
-    for (int f = 0; f < C::FN; ++f) {
+    for (int f = 0; f < NBF; ++f) {
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
+        for (int kk = 0; kk < NBK; ++kk) {
 #pragma unroll
-            for (int e = 0; e < C::NRB; ++e) {
+            for (int e = 0; e < NBE; ++e) {
                 if constexpr (OPB == GE_OP_T) {
-                    const int row = wn * C::TN + f * 32 + r32;
+                    const int row = wn * C::TN + r32;
                     const int chunk = ESZ == 1 ? 4 * kk + h + 2 * e : 2 * kk + h;
                     offB[f][kk][e] = row * C::ROWB + ((chunk ^ swz_row<C::ROWB>(row)) << 4);
                 } else if constexpr (ESZ == 2) {
                     const int G = lane >> 4, i = lane & 15;
-                    const int k = 16 * kk + 8 * (G >> 1) + 4 * e + (i >> 2);
+                    const int k = 8 * (G >> 1) + (i >> 2);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 4 * (i & 3);
                     offB[f][kk][e] =
                         k * C::KN_ROWB + (((n >> 3) ^ swz_kn(k, C::KN_CPR)) << 4) + ((n & 4) << 1);
                 } else {
                     const int G = lane >> 4, i = lane & 15;
-                    const int k = 64 * kk + 16 * (G >> 1) + 32 * (e >> 1) + 8 * (e & 1) + (i >> 1);
+                    const int k = 16 * (G >> 1) + (i >> 1);
                     const int n = wn * C::TN + f * 32 + 16 * (G & 1) + 8 * (i & 1);
                     offB[f][kk][e] = k * C::KN_ROWB +
                                      (((n >> 4) ^ swz_kn8(k, C::KN_CPR)) << 4) + (n & 8);
@@ -375,22 +387,32 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             }
         }
     }
+    // k-row offset of read e of sub-step kk of a k x n fragment:
+    //  16-bit: k = 16kk + 8(G/2) + 4e + i/4;  fp8: k = 64kk + 16(G/2) +
+    //  32(e/2) + 8(e%2) + i/2 (the lane halves' K pieces as for A)
+    auto kn_koff = [](int kk, int e) {
+        return ESZ == 2 ? 16 * kk + 4 * e : 64 * kk + 32 * (e >> 1) + 8 * (e & 1);
+    };
+    auto offB_at = [&](int f, int kk, int e) __attribute__((always_inline)) {
+        if constexpr (OPB == GE_OP_T) return offB[0][kk][e] + f * 32 * C::ROWB;
+        else return offB[f][0][0] + kn_koff(kk, e) * C::KN_ROWB;
+    };
 
     auto read16 = [&](const uint8_t* a) { return *(const u32x4*)a; };
     // fragment f of B (or of A) for k sub-step kk of the step held in `stage`
     auto load_fragB = [&](int stage, int kk, int f, Frag (&bfr)[C::FN]) {
         const uint8_t* st = smem + SE * C::A_BYTES + stage * C::B_BYTES;   // B stage
         if constexpr (OPB == GE_OP_T && ESZ == 2) {
-            bfr[f] = read16(st + offB[f][kk][0]);
+            bfr[f] = read16(st + offB_at(f, kk, 0));
         } else if constexpr (OPB == GE_OP_T) {
-            const u32x4 lo = read16(st + offB[f][kk][0]), hi = read16(st + offB[f][kk][1]);
+            const u32x4 lo = read16(st + offB_at(f, kk, 0)), hi = read16(st + offB_at(f, kk, 1));
             bfr[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         } else if constexpr (ESZ == 2) {
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][0])));
+                (lds_s16x4_t*)((lds_void_t*)(st + offB_at(f, kk, 0))));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t*)((lds_void_t*)(st + offB[f][kk][1])));
+                (lds_s16x4_t*)((lds_void_t*)(st + offB_at(f, kk, 1))));
             bfr[f] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
                            (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                            (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
@@ -400,16 +422,17 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 v[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (lds_i32x2_t*)((lds_void_t*)(st + offB[f][kk][e])));
+                    (lds_i32x2_t*)((lds_void_t*)(st + offB_at(f, kk, e))));
             bfr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
         }
     };
     auto load_fragA = [&](int stage, int kk, int f, Frag (&af)[C::FM]) {
         const uint8_t* st = smem + stage * C::A_BYTES;   // A stage
         if constexpr (ESZ == 2) {
-            af[f] = read16(st + offA[f][kk][0]);
+            af[f] = read16(st + offA[kk][0] + f * 32 * C::ROWB);
         } else {
-            const u32x4 lo = read16(st + offA[f][kk][0]), hi = read16(st + offA[f][kk][1]);
+            const u32x4 lo = read16(st + offA[kk][0] + f * 32 * C::ROWB),
+                        hi = read16(st + offA[kk][1] + f * 32 * C::ROWB);
             af[f] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }

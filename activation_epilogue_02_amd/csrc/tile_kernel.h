@@ -67,35 +67,29 @@ struct TileCfg {
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
 };
 
-// Load `nvalid` (< 16/ESZ) leading elements of a 16-byte chunk, zero the rest.
-template <int ESZ>
-__device__ __forceinline__ u32x4 load_partial(const uint8_t* p, int nvalid) {
-    uint8_t buf[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) buf[i] = 0;
-#pragma unroll
-    for (int e = 0; e < 16 / ESZ; ++e) {
-        if (e < nvalid) {
-#pragma unroll
-            for (int b = 0; b < ESZ; ++b) buf[e * ESZ + b] = p[e * ESZ + b];
-        }
-    }
-    u32x4 r;
-    __builtin_memcpy(&r, buf, 16);
-    return r;
-}
-
 // 16-byte chunk at element (row, col) of a row-major matrix with `ld`
-// elements per row, of which `ncols` are valid; zero when the row is out of
-// range or the chunk lies beyond `ncols`.
+// elements per row, of which `ncols` are valid (col a multiple of 16/ESZ,
+// nrows and ncols >= 1); elements of rows >= nrows or columns >= ncols read
+// as zero.  No per-lane branch: the load always reads a chunk that holds a
+// valid element (the row clamped to the last, the chunk to the last one
+// with valid columns), so its 16-byte-aligned bytes lie on a mapped page
+// even where the matrix ends mid-row, and the invalid elements are masked
+// off afterwards.  (Divergent branches here made the register allocator
+// spill and reload values for the active lanes only.)
 template <int ESZ>
 __device__ __forceinline__ u32x4 load_chunk(const uint8_t* base, int64_t ld, int row, int nrows,
                                             int col, int ncols) {
     constexpr int E = 16 / ESZ;
-    if (row >= nrows || col >= ncols) return u32x4{0, 0, 0, 0};
-    const uint8_t* p = base + ((int64_t)row * ld + col) * ESZ;
-    if (col + E <= ncols) return *(const u32x4*)p;
-    return load_partial<ESZ>(p, ncols - col);
+    const int rr = max(min(row, nrows - 1), 0);
+    const int cc = min(col, max((ncols - 1) / E * E, 0));
+    u32x4 v = *(const u32x4*)(base + ((int64_t)rr * ld + cc) * ESZ);
+    const int nb = (row < nrows ? min(max(ncols - col, 0), E) : 0) * ESZ;   // valid bytes
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int b = min(max(nb - 4 * d, 0), 4);
+        v[d] &= b >= 4 ? 0xffffffffu : ((1u << (8 * b)) - 1u);
+    }
+    return v;
 }
 
 template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN>
