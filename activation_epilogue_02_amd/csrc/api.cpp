@@ -153,12 +153,15 @@ int choose_tile(int64_t m, int64_t n, int a_type, int d_type) {
     // without register spills
     if (a_type == GE_MXF8_E4M3) return 8;
     if (a_type == GE_F8_E4M3) {
-        // fp8 rows are 128 bytes per step: a 256 x 256 stage is 64 KiB, so
-        // only two stages fit and the registers spill; 256 x 128 keeps three
-        // stages, and with 8 waves (64 x 64 each, two per SIMD, which hide
-        // each other's barrier and copy waits) it measures 10% faster than
-        // with 4 (65536 x 8192 x 16384: 1943 against 1765 TFLOP/s)
+        // A CU takes about 0.2 128-byte lines per cycle into LDS, so tiles
+        // with fewer bytes per flop keep the matrix cores busier: 256 x 256
+        // with 8 waves and 64-byte K steps (four 32 KiB stages, spread
+        // copies; tile 16) measures 8% faster than 256 x 128 (tile 15) on
+        // 65536 x 8192 x 16384 (2379 against 2200 TFLOP/s).  With 128-byte
+        // steps a 256 x 256 stage is 64 KiB and only two fit.  256 x 128 with
+        // 8 waves (two per SIMD) beats 4 waves by 10% (1943 against 1765).
         const int64_t t2x1 = ceil_div(m, 256) * ceil_div(n, 128);
+        if (t256 >= 512) return 16;
         if (t2x1 >= 512) return 15;
         if (t128 >= 256) return 8;
         return 1;
@@ -212,6 +215,7 @@ bool tile_supports(const TileShape* t, int a_type, int d_type) {
     if (a_type == GE_MXF8_E4M3) return t->id == 8;
     if (t->kernel == 1) return true;
     if (t->id == 13 || t->id == 14) return a_type == GE_F16 || a_type == GE_BF16;
+    if (t->kernel == 6) return a_type == GE_F8_E4M3;
     return a_type == GE_F16 || a_type == GE_BF16 || a_type == GE_F8_E4M3;
 }
 

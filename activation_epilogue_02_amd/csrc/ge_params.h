@@ -91,10 +91,12 @@ enum Path : int32_t { PATH_TILE = 1, PATH_SMALLM = 2 };
 // per step, four MFMA sub-steps, two 64 KiB stages at 256 x 256).
 // Kernel 5: kernel 4 with split-K: K slices in the launch grid's z, fp32
 // partials and an arrival counter per tile in the workspace.
+// Kernel 6: kernel 2 for fp8 inputs with 64-byte K steps (one MFMA sub-step
+// per step, 32 KiB stages at 256 x 256).
 struct TileShape {
     int32_t id, bm, bn, wm, wn, kernel, stages;
 };
-constexpr int kNumTiles = 15;
+constexpr int kNumTiles = 16;
 constexpr TileShape kTiles[kNumTiles] = {
     {1, 64, 64, 2, 2, 1, 2},     // 4 waves, 32 x 32 per wave
     {2, 128, 128, 2, 2, 1, 2},   // 4 waves, 64 x 64 per wave
@@ -111,12 +113,13 @@ constexpr TileShape kTiles[kNumTiles] = {
     {13, 64, 64, 2, 2, 4, 4},    // 128-byte K steps, 16-bit inputs only: 4 waves, 32 x 32 per wave
     {14, 64, 64, 2, 2, 5, 4},    // tile 13 with split-K (kernel 5): small problems with long K
     {15, 256, 128, 4, 2, 2, 4},  // 8 waves, 64 x 64 per wave (two waves per SIMD; fp8's fastest)
+    {16, 256, 256, 2, 4, 6, 4},  // fp8 only: 8 waves, 128 x 64 per wave, 64-byte K steps
 };
 
 // LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64
 // bytes (16-bit inputs) or 128 bytes (fp8); at most 160 KiB in total.
 constexpr int tile2_stages(const TileShape& t, int elem_size) {
-    const int stage = (t.bm + t.bn) * (elem_size == 1 || t.kernel >= 4 ? 128 : 64);
+    const int stage = (t.bm + t.bn) * (t.kernel == 6 ? 64 : elem_size == 1 || t.kernel >= 4 ? 128 : 64);
     return t.stages * stage <= 160 * 1024 ? t.stages : (160 * 1024) / stage;
 }
 

@@ -88,9 +88,13 @@ template <int DIN, int DOUT, int OPB, int BM, int BN, int WM, int WN, int S, boo
 struct Tile2Cfg {
     static constexpr int NW = WM * WN, NT = NW * 64;
     static constexpr int ESZ = Elem<DIN>::size;
-    static constexpr int ROWB = ESZ == 1 ? 128 : RB;  // bytes of an A (or n x k B) row per K step
-    static constexpr int BK = ROWB / ESZ;             // K elements per step: 32/64 (16-bit) or 128 (fp8)
-    static constexpr int NKK = ESZ == 1 ? 2 : ROWB / 32;   // MFMA k sub-steps per step (even)
+    // bytes of an A (or n x k B) row per K step: RB (64 or 128) for 16-bit
+    // inputs; fp8 rows are 128 bytes, or 64 with RB = 32
+    static constexpr int ROWB = ESZ == 1 ? (RB == 32 ? 64 : 128) : RB;
+    static constexpr int BK = ROWB / ESZ;             // K elements per step: 32/64 (16-bit) or 64/128 (fp8)
+    // MFMA k sub-steps per step: even, or one (fp8 64-byte rows), when the
+    // two fragment register sets alternate from step to step
+    static constexpr int NKK = ESZ == 1 ? ROWB / 64 : ROWB / 32;
     static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row: 4 or 8
     static constexpr int RPC = 1024 / ROWB;           // rows per 1 KiB copy
     static constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
@@ -132,7 +136,9 @@ struct Tile2Cfg {
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(SE >= 2, "LDS budget");
     static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte rows");
-    static_assert(NKK % 2 == 0, "fragment sets alternate over an even number of sub-steps");
+    static_assert(NKK % 2 == 0 || (NKK == 1 && SPREAD && SE % 2 == 0 && !MX),
+                  "fragment sets alternate over an even number of sub-steps, or from step to step over an "
+                  "even number of stages with spread copies");
     static_assert(!MX || (ESZ == 1 && !REG && (BM / WM) % 64 == 0 && (BN / WN) % 64 == 0),
                   "MX scales: fp8 elements, direct copies, wave tiles of whole 64-row groups");
     static_assert((SE - 1) * VM_PER_STEP < 64, "vmcnt range");
@@ -651,6 +657,22 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     };
     auto step_spread = [&](int kt, int stage) __attribute__((always_inline)) {
         const int ct = kt + SE - 1;
+        if constexpr (C::NKK == 1) {
+            // one sub-step per step: step kt's fragments are in set kt & 1
+            // (stage has kt's parity: SE is even); after the barrier the
+            // region reads step kt + 1's into the other set, issues every
+            // copy of step kt + SE - 1 and runs step kt's MFMAs
+            wait_vm<(SE - 3) * VM>();
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): own LDS reads done
+            asm volatile("s_barrier" ::: "memory");
+            if ((stage & 1) == 0)
+                region(std::integral_constant<int, VM>{}, (stage + 1) % SE, 0, a1, b1, sa1, sb1, a0, b0, sa0, sb0,
+                       ct, 0);
+            else
+                region(std::integral_constant<int, VM>{}, (stage + 1) % SE, 0, a0, b0, sa0, sb0, a1, b1, sa1, sb1,
+                       ct, 0);
+            return;
+        }
 #pragma unroll
         for (int kk = 0; kk < C::NKK - 1; ++kk) {
             if (kk % 2 == 0)
@@ -684,15 +706,23 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             interleave();
         }
     };
-    auto step_last = [&](int kt, int stage) {
+    // (odd_c: with one sub-step per step, whether kt is odd, i.e. which set
+    // holds step kt's fragments)
+    auto step_last = [&](int kt, int stage, auto odd_c) __attribute__((always_inline)) {
         if (kt + SE - 1 < KT) issue(kt + SE - 1);
         __builtin_amdgcn_sched_barrier(0);
         inner(stage);
         wait_step(min(SE - 2, KT - 2 - kt));
         __builtin_amdgcn_sched_barrier(0);
-        load_frags((stage + 1) % SE, 0, a0, b0, sa0, sb0);
-        reads_first();
-        mfmas(a1, b1, sa1, sb1);   // the last sub-step (NKK - 1 is odd)
+        if constexpr (C::NKK == 1 && !decltype(odd_c)::value) {
+            load_frags((stage + 1) % SE, 0, a1, b1, sa1, sb1);
+            reads_first();
+            mfmas(a0, b0, sa0, sb0);
+        } else {
+            load_frags((stage + 1) % SE, 0, a0, b0, sa0, sb0);
+            reads_first();
+            mfmas(a1, b1, sa1, sb1);   // the last sub-step (NKK - 1 is odd), or step kt of odd kt
+        }
         interleave();
     };
     int kt = 0;
@@ -702,12 +732,29 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
 #pragma unroll
         for (int u = 0; u < SE; ++u) step_spread(kt + u, u);
     }
-    for (; kt < KT - 1; ++kt) step_last(kt, kt % SE);
-    if (KT > 0) {
-        inner((KT - 1) % SE);
-        mfmas(a1, b1, sa1, sb1);
+    if constexpr (C::NKK == 1) {
+        // kt is even here (a multiple of SE): steps in pairs, so that each
+        // call knows its set; the last step's MFMAs use the set the final
+        // reads went to
+        for (; kt + 2 <= KT - 1; kt += 2) {
+            step_last(kt, kt % SE, std::false_type{});
+            step_last(kt + 1, (kt + 1) % SE, std::true_type{});
+        }
+        if (kt < KT - 1) {
+            step_last(kt, kt % SE, std::false_type{});
+            mfmas(a1, b1, sa1, sb1);
+        } else if (KT > 0) {
+            mfmas(a0, b0, sa0, sb0);
+        }
+    } else {
+        for (; kt < KT - 1; ++kt) step_last(kt, kt % SE, std::false_type{});
+        if (KT > 0) {
+            inner((KT - 1) % SE);
+            mfmas(a1, b1, sa1, sb1);
+        }
     }
     } else {
+    static_assert(C::NKK % 2 == 0, "the burst loop alternates the sets within a step");
     // ---- main loop ----
     // All SE stages start filling at once; afterwards the copy of step
     // kt + SE goes into the stage step kt used, as soon as every wave has
@@ -1000,6 +1047,9 @@ Tile2Fn pick_tile2(int tile_id) {
         if constexpr (Elem<DIN>::size == 2) return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128>;
         else return nullptr;
     case 15: return ge_tile2_kernel<DIN, DOUT, OPB, 256, 128, 4, 2, 4, false, 64>;
+    case 16:   // fp8 only: 256 x 256, 8 waves, 64-byte K steps (one sub-step each) in four stages
+        if constexpr (Elem<DIN>::size == 1) return ge_tile2_kernel<DIN, DOUT, OPB, 256, 256, 2, 4, 4, false, 32>;
+        else return nullptr;
     case 14:   // tile 13 with split-K
         if constexpr (Elem<DIN>::size == 2)
             return ge_tile2_kernel<DIN, DOUT, OPB, 64, 64, 2, 2, 4, false, 128, true>;

@@ -299,7 +299,8 @@ def test_forced_launch_failure_hook(monkeypatch):
     (16, 4096, 4096, 1, "f32", "path=tile"),
     (8192, 8192, 8192, 0, "bf16", "tile=256x256 waves=2x4 tile_id=6 kernel=2 stages=4"),
     (65536, 8192, 16384, 0, "bf16", "tile_id=6 kernel=2 stages=4 grid=8192 group_m=4 "),
-    (65536, 8192, 16384, 0, "e4m3", "tile=256x128 waves=4x2 tile_id=15 kernel=2 stages=3"),
+    (65536, 8192, 16384, 0, "e4m3", "tile=256x256 waves=2x4 tile_id=16 kernel=6 stages=4 grid=8192 group_m=4 "),
+    (4096, 4096, 1024, 0, "e4m3", "tile=256x128 waves=4x2 tile_id=15 kernel=2 stages=3"),
     (4096, 1024, 4096, 1, "f16", "tile_id=8 kernel=2"),
     (1024, 512, 2048, 0, "f16", "tile=64x64 waves=2x2 tile_id=13 kernel=4 stages=4"),
     (256, 256, 65536, 0, "bf16", "tile=64x64 waves=2x2 tile_id=14 kernel=5 stages=4 grid=16 group_m=4 split_k=8 "),
@@ -370,11 +371,31 @@ def test_block_scaled_plan_refuses_rows_beyond_4_gib():
         B.gemm_epilog_free(h)
 
 
-@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15])
+@pytest.mark.parametrize("tile", [5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16])
 def test_pipelined_tiles_reject_fp32_inputs(tile):
     h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "f32", "f32", 0))
     try:
         assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, tile, 0)) == B.GE_ERR_SHAPE
+    finally:
+        B.gemm_epilog_free(h)
+
+
+@pytest.mark.parametrize("tile", [16])
+def test_fp8_deep_tiles_take_fp8_only(tile):
+    """Tile 16 (256 x 256, 8 waves, 64-byte fp8 K steps, four stages) serves
+    fp8 inputs only; id 17 does not exist."""
+    for a, d, ok in (("e4m3", "bf16", True), ("bf16", "bf16", False), ("f16", "f16", False)):
+        h = B.gemm_epilog_create(B.make_desc(512, 512, 512, a, d, 0))
+        try:
+            st = status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, tile, 0))
+            assert st == (B.GE_OK if ok else B.GE_ERR_SHAPE), a
+            if ok:
+                assert f"tile_id={tile} kernel=6 stages=4 " in B.gemm_epilog_describe(h)
+        finally:
+            B.gemm_epilog_free(h)
+    h = B.gemm_epilog_create(B.make_desc(512, 512, 512, "e4m3", "bf16", 0))
+    try:
+        assert status_of(B.gemm_epilog_plan, h, 1, 0, B.ge_pref(1, 0, 17, 0)) == B.GE_ERR_SHAPE
     finally:
         B.gemm_epilog_free(h)
 

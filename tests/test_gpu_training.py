@@ -37,7 +37,7 @@ def test_training_epilogues_ragged(a, d, ep, axis, op_b):
     check_full(w, r)
 
 
-TILES = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15]
+TILES = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -48,6 +48,8 @@ def test_training_epilogues_every_tile(tile, a, d, op_b):
         pytest.skip("the pipelined tiles take 16-bit and fp8 inputs only")
     if a == "e4m3" and tile in (13, 14):
         pytest.skip("the pipelined 64x64 tile takes 16-bit inputs only")
+    if a != "e4m3" and tile == 16:
+        pytest.skip("tile 16 (64-byte fp8 K steps) takes fp8 inputs only")
     k = 456 if a == "e4m3" else 200
     cases = [(ep, "col") for ep in TRAIN] + [("drelu_bgrad", "row"), ("dgelu_bgrad", "row")]
     if tile == 14:   # the split-K tile does not take the bias-gradient epilogues
