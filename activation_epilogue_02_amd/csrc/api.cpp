@@ -146,7 +146,7 @@ int choose_tile(int64_t m, int64_t n, int a_type, int d_type) {
     // gives every CU a tile, else 128 x 128)
     if (d_type == GE_F8_E4M3) {
         if (a_type == GE_MXF8_E4M3) return 8;
-        if (a_type == GE_F8_E4M3) return ceil_div(m, 256) * ceil_div(n, 128) >= 512 ? 15 : 8;
+        if (a_type == GE_F8_E4M3) return t256 >= 512 ? 16 : ceil_div(m, 256) * ceil_div(n, 128) >= 512 ? 15 : 8;
         return t256 >= 256 ? 6 : 8;
     }
     // block-scaled fp8: the one tile the block-scaled MFMA compiles into
@@ -209,7 +209,7 @@ int32_t auto_group_m(const TileShape* t, int64_t tm, int a_type) {
 bool tile_supports(const TileShape* t, int a_type, int d_type) {
     if (d_type == GE_F8_E4M3) {   // fp8 output: the instantiated tiles only
         if (a_type == GE_MXF8_E4M3) return t->id == 8;
-        if (a_type == GE_F8_E4M3) return t->id == 15 || t->id == 8;
+        if (a_type == GE_F8_E4M3) return t->id == 16 || t->id == 15 || t->id == 8;
         return t->id == 6 || t->id == 8;
     }
     if (a_type == GE_MXF8_E4M3) return t->id == 8;

@@ -117,7 +117,8 @@ constexpr TileShape kTiles[kNumTiles] = {
 };
 
 // LDS stages the pipelined kernel uses: a stage holds BM + BN rows of 64
-// bytes (16-bit inputs) or 128 bytes (fp8); at most 160 KiB in total.
+// bytes (16-bit inputs in kernel 2; fp8 in kernel 6) or 128 bytes (fp8 in
+// kernel 2, 16-bit inputs in kernels 4 and 5); at most 160 KiB in total.
 constexpr int tile2_stages(const TileShape& t, int elem_size) {
     const int stage = (t.bm + t.bn) * (t.kernel == 6 ? 64 : elem_size == 1 || t.kernel >= 4 ? 128 : 64);
     return t.stages * stage <= 160 * 1024 ? t.stages : (160 * 1024) / stage;

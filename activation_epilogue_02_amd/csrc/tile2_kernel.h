@@ -1059,13 +1059,15 @@ Tile2Fn pick_tile2(int tile_id) {
 }
 
 // fp8 output (E4M3 D): the 256 x 256 8-wave tile and the 128 x 128 tile for
-// 16-bit inputs; the 256 x 128 tile and the 128 x 128 tile for fp8 inputs
+// 16-bit inputs; the 256 x 256 tile with 64-byte steps, the 256 x 128 tile
+// and the 128 x 128 tile for fp8 inputs
 template <int DIN, int OPB>
 Tile2Fn pick_tile2_out8(int tile_id) {
     if constexpr (Elem<DIN>::size == 2) {
         if (tile_id == 6) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 256, 256, 2, 4, 4, false, 64>;
     } else {
         if (tile_id == 15) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 256, 128, 4, 2, 4, false, 64>;
+        if (tile_id == 16) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 256, 256, 2, 4, 4, false, 32>;
     }
     if (tile_id == 8) return ge_tile2_kernel<DIN, GE_F8_E4M3, OPB, 128, 128, 2, 2, 4, false, 64>;
     return nullptr;

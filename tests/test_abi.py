@@ -674,6 +674,8 @@ def test_fp8_output_validation(monkeypatch):
             assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(0, 1, 0, 0)) == B.GE_ERR_DTYPE
             assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(1, 0, 11, 0)) == B.GE_ERR_SHAPE
             assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(1, 0, 2, 0)) == B.GE_ERR_SHAPE
+            assert status_of(B.gemm_epilog_plan, h, "relu_bias", "row", B.ge_pref(1, 0, 16, 0)) == \
+                (B.GE_OK if a == "e4m3" else B.GE_ERR_SHAPE), a
             B.gemm_epilog_plan(h, "relu_aux_bias", "row")
             assert status_of(B.gemm_epilog_set_fp8_output, h, FAKE + 2, None) == B.GE_ERR_ALIGN
             B.gemm_epilog_set_fp8_output(h, FAKE, FAKE + 4)

@@ -74,7 +74,7 @@ def oracle_product(a, A, Bm, SA, SB, sa, sb, op_b):
             oracle.gemm_abs(codes(A), a, codes(Bm), a, op_b, fa, fb))
 
 
-def run_out8(a, m, n, k, ep, axis, op_b, scale_d, seed, batch=0):
+def run_out8(a, m, n, k, ep, axis, op_b, scale_d, seed, batch=0, tile=0):
     g = torch.Generator().manual_seed(seed)
     A, Bm, SA, SB, sa, sb = make_operands(a, m, n, k, op_b, g)
     Bm, ldb = padded_b(Bm, op_b)
@@ -85,7 +85,7 @@ def run_out8(a, m, n, k, ep, axis, op_b, scale_d, seed, batch=0):
     amax = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
     h = B.GemmEpilog(m, n, k, a, "e4m3", op_b, ldb=ldb, ldd=ldd)
     try:
-        h.plan(ep, axis)
+        h.plan(ep, axis, tile=tile)
         desc = h.describe()
         B.gemm_epilog_set_fp8_output(h.h, sd, amax)
         aux = None
@@ -159,6 +159,18 @@ def test_fp8_output_ragged(a, op_b, ep, axis):
         assert not (diff[:, :P.shape[1]] & (np.abs(P) > y_bound(dict(r, ep="bias")))).any()
 
 
+@pytest.mark.parametrize("op_b", [0, 1])
+@pytest.mark.parametrize("ep,axis", [("relu_aux_bias", "row"), ("gelu_bias", "col")])
+@pytest.mark.parametrize("k", [464, 48, 1024])
+def test_fp8_output_deep_fp8_tile(op_b, ep, axis, k):
+    """fp8 inputs and output on the 256 x 256 tile with 64-byte K steps (the
+    planner's choice for large problems), forced here at ragged shapes: a
+    single ragged step, a ragged tail after full steps, whole steps only."""
+    r = run_out8("e4m3", 300, 520, k, ep, axis, op_b, 2.0, seed=k + op_b, tile=16)
+    assert "tile_id=16 " in r["desc"], r["desc"]
+    check_out8(r, 2.0)
+
+
 @pytest.mark.parametrize("a", ["bf16", "e4m3"])
 def test_fp8_output_integer_codes_exact_with_saturation(a):
     """Integer inputs: y is exact, so every code must equal the oracle's
@@ -224,9 +236,11 @@ def test_fp8_output_amax_per_product_and_per_call():
 
 def test_fp8_output_planner_tiles():
     """The large bf16 problem takes the 256 x 256 tile, small ones 128 x 128;
-    fp8 inputs the 256 x 128 tile; block-scaled the 128 x 128 tile."""
+    fp8 inputs the 256 x 256 tile with 64-byte steps when there are >= 512
+    such tiles, else 256 x 128; block-scaled the 128 x 128 tile."""
     for a, m, n, k, tile in (("bf16", 4096, 4096, 512, "tile_id=6 "), ("bf16", 512, 512, 512, "tile_id=8 "),
-                             ("e4m3", 8192, 4096, 512, "tile_id=15 "), ("mxf8", 4096, 4096, 512, "tile_id=8 ")):
+                             ("e4m3", 8192, 4096, 512, "tile_id=16 "), ("e4m3", 4096, 4096, 512, "tile_id=15 "),
+                             ("mxf8", 4096, 4096, 512, "tile_id=8 ")):
         h = B.GemmEpilog(m, n, k, a, "e4m3", 0)
         try:
             h.plan("relu_bias", "row")
