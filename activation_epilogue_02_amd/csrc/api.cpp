@@ -54,6 +54,7 @@ struct ge_plan_s {
     int32_t path = 0, tile_id = 0, unfused = 0;
     int32_t split_k = 1, k_per_split = 0;
     int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
+    int32_t k_stagger = 0;
     unsigned grid = 0;
     size_t ws_c = 0;         // unfused intermediate bytes
     size_t ws_partial = 0;   // split-K partial bytes
@@ -204,6 +205,26 @@ int32_t auto_group_m(const TileShape* t, int64_t tm, int a_type) {
     return (int32_t)(tm < g ? (tm > 0 ? tm : 1) : g);
 }
 
+// Full K steps of rotation per tile row and column of a group (the
+// pipelined kernel's K order).  The tiles that share a panel of A or B run in
+// lock-step, so their requests for the same lines arrive together and queue
+// behind the one that misses; rotating each tile's K order spreads them, at
+// the cost of a longer stretch of each panel held in L2.  Measured on 65536 x
+// 8192 x 16384 (TFLOP/s at 0 / 1 / 2 / 4 / 8 steps): the block-scaled 128 x
+// 128 tile, 16 tiles on each A panel at once, 1290 / 1335 / 1356 / 1347 /
+// 1290; the fp8 256 x 256 tile 2332-2367 unrotated against 2358-2392 at one
+// step; the bf16 256 x 256 tile 1273-1276 / 1273 / 1262 / 1247 (none there).
+// GE_K_STAGGER=<steps> in the environment overrides the choice.
+int32_t auto_k_stagger(const TileShape* t, int a_type) {
+    if (const char* e = getenv("GE_K_STAGGER")) {
+        const int v = atoi(e);
+        return v > 0 ? v : 0;
+    }
+    if (a_type == GE_MXF8_E4M3 && t->id == 8) return 2;
+    if (a_type == GE_F8_E4M3 && t->id == 16) return 1;
+    return 0;
+}
+
 // The pipelined kernel takes 16-bit and fp8 inputs (its 64 x 64 tile only
 // 16-bit ones); block-scaled fp8 runs on its 128 x 128 tile only.
 bool tile_supports(const TileShape* t, int a_type, int d_type) {
@@ -290,6 +311,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
 
     ge_plan_s q = *h;
     q.planned = false;
+    q.k_stagger = 0;
     q.epilog = epilog;
     q.axis = bias_axis;
     q.unfused = (pr.unfused && epilog != GE_EPILOG_NONE) ? 1 : 0;
@@ -383,6 +405,7 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
                                    : auto_group_m(t, tm, d.a_type);
         q.grid = (unsigned)(tm * tn);
         q.k_per_split = (int32_t)d.k;
+        q.k_stagger = auto_k_stagger(t, d.a_type);
         if (t->kernel == 5) {
             // K slices of whole 64-element steps: the largest power of two
             // that keeps the grid within 128 workgroups and every slice at
@@ -579,6 +602,7 @@ static int execute_impl(ge_handle h, const void* A, const void* B, const void* c
     a.group_m = h->group_m;
     a.split_k = h->split_k;
     a.k_per_split = h->k_per_split;
+    a.k_stagger = h->k_stagger;
     unsigned grid = h->grid;
     int32_t bgrad_parts = h->bgrad_parts;
     if (h->path != PATH_SMALLM && M != d.m) {
@@ -821,14 +845,15 @@ int gemm_epilog_describe(ge_handle h, char* buf, size_t cap) {
     snprintf(buf, cap,
              "m=%lld n=%lld k=%lld a=%d d=%d op_b=%d epilog=%d axis=%d path=%s tile=%dx%d waves=%dx%d "
              "tile_id=%d kernel=%d stages=%d grid=%u group_m=%d split_k=%d unfused=%d workspace=%zu "
-             "ldaux_words=%lld",
+             "ldaux_words=%lld k_stagger=%d",
              (long long)d.m, (long long)d.n, (long long)d.k, d.a_type, d.d_type, d.op_b, h->epilog, h->axis,
              h->path == PATH_SMALLM ? "smallm" : "tile", t ? t->bm : 16, t ? t->bn : 16 * h->group_m, t ? t->wm : 1,
              t ? t->wn : 8, h->tile_id, t ? t->kernel : 0,
              t ? (t->kernel >= 2 && t->kernel != 3 ? tile2_stages(*t, elem_size(d.a_type)) : t->stages) : 0, h->grid, h->group_m,
              h->split_k,
              h->unfused,
-             h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad, (long long)h->ldaux);
+             h->ws_c + h->ws_partial + h->ws_counters + h->ws_bgrad, (long long)h->ldaux,
+             h->k_stagger);
     return GE_OK;
 }
 

@@ -29,6 +29,8 @@ struct KernelArgs {
     int32_t group_m;       // tile-rows per group in the launch order
     int32_t split_k;       // K slices (small-m path)
     int32_t k_per_split;   // K elements per slice, multiple of the k step
+    int32_t k_stagger;     // pipelined tiles: full K steps of rotation per
+                           // position in the tile group (0 = none)
     // batched launches: the product's index z comes from the launch grid;
     // product z's buffers start z * bs_* bytes after product 0's (a stride
     // of 0 shares one input between all products); counters: elements

@@ -188,6 +188,18 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     const uint8_t* gB = (const uint8_t*)p.B + (OPB == GE_OP_T ? (int64_t)ks * ESZ : (int64_t)ks * p.ldb * ESZ);
     const int KT = (K + BK - 1) / BK;       // K steps
     const int KF = K / BK;                  // full K steps (direct copies)
+    // The full steps are taken in a rotated order, step t reading K position
+    // kpos(t) = (t + koff) mod KF (the ragged step, if any, stays last), with
+    // koff growing by k_stagger per tile row and column of the group, so that
+    // the tiles sharing a panel of A or B do not request its lines at the
+    // same moment.
+    const int koff = (p.k_stagger > 0 && KF > 1)
+                         ? (int)(((int64_t)(tm % max(p.group_m, 1) + tn) * p.k_stagger) % KF)
+                         : 0;
+    auto kpos = [&](int t) __attribute__((always_inline)) {
+        const int q = t + koff;
+        return q >= KF ? q - KF : q;
+    };
 
     // ---- per-lane sources of this wave's 1 KiB copies, at K step 0 ----
     // A: copy i covers LDS rows R = (wave*A_INS + i)*RPC + lane/CPR, slot lane%CPR
@@ -263,14 +275,14 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
         uint8_t* sa = smem + (t % SE) * C::A_BYTES;                      // A stages first,
         uint8_t* sb = smem + SE * C::A_BYTES + (t % SE) * C::B_BYTES;    // then B stages
         if (c < C::A_INS)
-            copy_to_lds16_sb(voA[c], baseA + (int64_t)t * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
+            copy_to_lds16_sb(voA[c], baseA + (int64_t)kpos(t) * stepA, lds_addr(sa + (wave * C::A_INS + c) * 1024));
         else if (c < C::A_INS + C::B_INS)
-            copy_to_lds16_sb(voB[c - C::A_INS], baseB + (int64_t)t * stepB,
+            copy_to_lds16_sb(voB[c - C::A_INS], baseB + (int64_t)kpos(t) * stepB,
                              lds_addr(sb + (wave * C::B_INS + c - C::A_INS) * 1024));
         else if constexpr (MX) {
             const int sc = c - C::A_INS - C::B_INS;   // scale copy: A rows first, then B columns
             const uint8_t* src = sc < C::SCA ? srcSA[sc] : srcSB[sc - C::SCA];
-            copy_to_lds4(src + 4 * t, lds_addr(sc_base(t % SE) + sc * 256));
+            copy_to_lds4(src + 4 * kpos(t), lds_addr(sc_base(t % SE) + sc * 256));
         }
     };
     // issue the direct copies of full K step t into stage t % SE
@@ -532,9 +544,9 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             if (t >= KT) return;
             if (t < KF) {
 #pragma unroll
-                for (int i = 0; i < C::A_INS; ++i) ra[i] = *(const u32x4*)(srcA[i] + (int64_t)t * stepA);
+                for (int i = 0; i < C::A_INS; ++i) ra[i] = *(const u32x4*)(srcA[i] + (int64_t)kpos(t) * stepA);
 #pragma unroll
-                for (int i = 0; i < C::B_INS; ++i) rb[i] = *(const u32x4*)(srcB[i] + (int64_t)t * stepB);
+                for (int i = 0; i < C::B_INS; ++i) rb[i] = *(const u32x4*)(srcB[i] + (int64_t)kpos(t) * stepB);
             } else {
                 const int k0 = t * BK;
 #pragma unroll

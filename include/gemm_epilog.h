@@ -43,6 +43,17 @@
  *   - A planned handle is immutable: concurrent executes on different
  *     streams are safe.  free() touches only host memory and is safe while
  *     kernels launched from the handle are still running.
+ *
+ * Environment, read by gemm_epilog_plan:
+ *   GE_LOG=1           print each successful plan's description to stderr
+ *   GE_K_STAGGER=<n>   the tile path takes its full K steps in a rotated
+ *                      order, each tile starting n steps further in per tile
+ *                      row and column of its launch group, so that tiles
+ *                      sharing a panel of A or B do not fetch the same lines
+ *                      at once; overrides the planner's choice (0 = off).
+ *                      The K summation order, and so the rounding of float
+ *                      results, depends on it; results stay bitwise
+ *                      reproducible for a given plan.
  */
 #ifndef GEMM_EPILOG_H
 #define GEMM_EPILOG_H

@@ -316,6 +316,36 @@ def test_planner_choices(m, n, k, op_b, a, expect):
         B.gemm_epilog_free(h)
 
 
+@pytest.mark.parametrize("a,tile,rot", [("bf16", 6, 0), ("e4m3", 16, 1), ("mxf8", 8, 2)])
+def test_k_rotation_choice(a, tile, rot, monkeypatch):
+    """The planner rotates the K order of the pipelined tiles where it was
+    measured to help (the block-scaled 128 x 128 tile by 2 steps, the fp8
+    64-byte-step tile by 1); GE_K_STAGGER overrides it, 0 turning it off."""
+    monkeypatch.delenv("GE_K_STAGGER", raising=False)
+    h = B.gemm_epilog_create(B.make_desc(65536, 8192, 16384, a, "bf16", 0))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        s = B.gemm_epilog_describe(h)
+        assert f"tile_id={tile} " in s and s.endswith(f" k_stagger={rot}"), s
+        monkeypatch.setenv("GE_K_STAGGER", "3")
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert B.gemm_epilog_describe(h).endswith(" k_stagger=3")
+        monkeypatch.setenv("GE_K_STAGGER", "0")
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert B.gemm_epilog_describe(h).endswith(" k_stagger=0")
+    finally:
+        B.gemm_epilog_free(h)
+    # the small-m path has no K order to rotate
+    monkeypatch.setenv("GE_K_STAGGER", "3")
+    h = B.gemm_epilog_create(B.make_desc(16, 4096, 4096, "bf16", "bf16", 1))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        assert "path=smallm" in B.gemm_epilog_describe(h)
+        assert B.gemm_epilog_describe(h).endswith(" k_stagger=0")
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_group_order_preference():
     """group_m: 0 = the planner's choice, n > 0 = n tile rows per group
     (clamped to the tile rows there are), negative = GE_ERR_SHAPE."""

@@ -51,6 +51,19 @@ def test_mx_short_and_ragged_k(k, op_b):
     check_full(w, run_library(w, inp, pad=1))
 
 
+@pytest.mark.parametrize("rot", [0, 1, 2, 5])
+@pytest.mark.parametrize("op_b", [0, 1])
+def test_mx_k_rotation(rot, op_b, monkeypatch):
+    """The block-scaled tile with its K steps in a rotated order: each step's
+    scale words must follow its data (k = 1000: seven 128-deep steps and a
+    tail of 104 values, 4 x 5 tiles of 128)."""
+    monkeypatch.setenv("GE_K_STAGGER", str(rot))
+    w = wl(500, 520, 1000, "bf16", "gelu_bias", "col", op_b, seed=40 + rot)
+    r = run_library(w, synth.make_inputs(w), pad=1)
+    assert r.desc.endswith(f" k_stagger={rot}"), r.desc
+    check_full(w, r)
+
+
 def test_mx_unit_scales_match_the_per_tensor_path():
     """All block scales 2^0: the block-scaled kernel must compute what the
     per-tensor fp8 kernel computes on the same codes (same tile)."""

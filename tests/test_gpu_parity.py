@@ -84,6 +84,49 @@ def test_pipelined_tiles_ragged(tile, a, d, op_b):
         check_full(w, r)
 
 
+@pytest.mark.parametrize("rot", [1, 3, 7])
+@pytest.mark.parametrize("tile", [5, 6, 8, 9, 11, 13, 15, 16])
+@pytest.mark.parametrize("a", ["bf16", "e4m3"])
+def test_pipelined_k_rotation(tile, a, rot, monkeypatch):
+    """The full K steps taken in a rotated order (GE_K_STAGGER overrides the
+    planner's rotation): each tile starts rot * (its row in the group + its
+    column) steps in and wraps round, the ragged step last.  Ragged m, n and
+    k: 16-bit k = 488 (fifteen 32-deep steps and a tail of 8; 64-deep tiles
+    seven and a tail of 40), fp8 k = 1000 (seven 128-deep steps and a tail of
+    104; tile 16 fifteen 64-deep ones and 40), 3 x 4 to 10 x 13 tiles."""
+    skip_unsupported(tile, a)
+    monkeypatch.setenv("GE_K_STAGGER", str(rot))
+    k = 1000 if a == "e4m3" else 488
+    for op_b in (0, 1):
+        w = wl(600, 776, k, a, "bf16", "relu_aux_bias", "row", op_b, seed=rot * 100 + tile)
+        r = run_library(w, synth.make_inputs(w), pad=1, path=1, tile=tile)
+        assert f"tile_id={tile} " in r.desc and r.desc.endswith(f" k_stagger={rot}"), r.desc
+        check_full(w, r)
+
+
+@pytest.mark.parametrize("tile", [6, 8, 15, 16])
+@pytest.mark.parametrize("a", ["bf16", "e4m3"])
+def test_pipelined_k_rotation_integer_bit_exact(tile, a, monkeypatch):
+    """Integer inputs under a rotated K order: each K step must be taken
+    exactly once (a step skipped or taken twice changes the exact sum)."""
+    skip_unsupported(tile, a)
+    monkeypatch.setenv("GE_K_STAGGER", "5")
+    m, n, k = 520, 392, 1104
+    w = wl(m, n, k, a, "bf16", "relu_bias", "col", 1)
+    inp = synth.make_inputs(w, a_dist=("int", -4, 4), b_dist=("int", -4, 4), bias_dist=("int", -64, 64))
+    if a == "e4m3":
+        g = torch.Generator().manual_seed(9)
+        inp.A = torch.randint(-4, 5, (m, k), generator=g).float().to(torch.float8_e4m3fn)
+        inp.B = torch.randint(-4, 5, (n, k), generator=g).float().to(torch.float8_e4m3fn)
+        inp.scale_a = torch.ones(1)
+        inp.scale_b = torch.ones(1)
+    r = run_library(w, inp, path=1, tile=tile)
+    assert r.desc.endswith(" k_stagger=5"), r.desc
+    from parity import oracle_full
+    Y, P, _ = oracle_full(w, r)
+    assert np.array_equal(codes(r.D)[:, :n], oracle.encode(Y, "bf16").reshape(Y.shape))
+
+
 @pytest.mark.parametrize("k", [1, 8, 31, 32, 33, 64, 95, 96, 97, 128, 129, 256, 385, 512])
 @pytest.mark.parametrize("tile", [5, 6, 8, 9, 11, 13, 14, 15, 16])
 @pytest.mark.parametrize("a", ["bf16", "e4m3"])
