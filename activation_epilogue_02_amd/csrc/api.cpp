@@ -380,13 +380,15 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
     } else {
         q.tile_id = pr.tile ? pr.tile : choose_tile(d.m, d.n, d.a_type, d.d_type);
         // the automatic split-K 64 x 64 tile serves problems with so few tiles
-        // (at most a quarter of the CUs) and so long a K that the slices'
-        // parallelism outweighs their partial exchange, which costs about as
-        // much as 30 K steps of the unsplit tile (measured: 1024 x 512 x 2048
-        // takes 13 us unsplit and 29 / 45 us in 2 / 4 slices); the
-        // bias-gradient partials would share its partial buffer
-        if (!pr.tile && q.tile_id == 13 && !is_bgrad(epilog) && d.k >= 4096 &&
-            ceil_div(d.m, 64) * ceil_div(d.n, 64) <= 64)
+        // and so long a K that the slices' parallelism outweighs their
+        // partial exchange: at most 64 tiles with k >= 4096, or at most 128
+        // with k >= 8192 (measured: 1024 x 512 x 8192 takes 29.2 us unsplit
+        // and 22.6 us in 2 slices; 1024 x 512 x 2048 10.8 us unsplit and
+        // 12.9 / 13.9 us in 2 / 4); the bias-gradient partials would share
+        // its partial buffer
+        const int64_t t64 = ceil_div(d.m, 64) * ceil_div(d.n, 64);
+        if (!pr.tile && q.tile_id == 13 && !is_bgrad(epilog) &&
+            ((t64 <= 64 && d.k >= 4096) || (t64 <= 128 && d.k >= 8192)))
             q.tile_id = 14;
         const TileShape* t = find_tile(q.tile_id);
         if (!tile_supports(t, d.a_type, d.d_type)) return GE_ERR_SHAPE;
@@ -408,16 +410,24 @@ int gemm_epilog_plan(ge_handle h, int32_t epilog, int32_t bias_axis, const ge_pr
         q.k_stagger = auto_k_stagger(t, d.a_type);
         if (t->kernel == 5) {
             // K slices of whole 64-element steps: the largest power of two
-            // that keeps the grid within 128 workgroups and every slice at
-            // four or more steps, unless forced.  The last slice of a tile
-            // reads every partial, so more slices cost more than they gain
-            // (measured at 256 x 256 x 65536: 245 us unsplit, 61 us in 8
-            // slices, 118 us in 32)
+            // that keeps the grid within 256 workgroups, every slice at 16 or
+            // more steps (32 beyond 128 workgroups) and the split at most 8
+            // (16 for at most 4 tiles), unless forced.  The last slice of a tile reads every partial, so
+            // beyond that more slices cost more than they gain.  Measured
+            // (bf16, the best split and its time): 128 x 128 x 65536 16,
+            // 25.9 us (30.0 at 32); 256 x 256 x 4096 4, 12.4; 256 x 256 x
+            // 8192 4-8, 14.6; 256 x 256 x 65536 8, 38.4 (41.4 at 16, 180 us
+            // unsplit); 256 x 512 x 32768 8, 33.7; 512 x 512 x 8192 4, 17.5;
+            // 512 x 512 x 16384 4, 23.5; 1024 x 512 x 16384 2, 37.8;
+            // 1024 x 512 x 2048 1, 10.8 (12.9 in 2 slices of 16 steps)
             const int64_t steps = ceil_div(d.k, 64);
             int split = pr.split_k;
             if (split <= 0) {
+                const int cap = tm * tn <= 4 ? 16 : 8;
                 split = 1;
-                while (tm * tn * split * 2 <= 128 && steps >= split * 2 * 4) split *= 2;
+                while (split * 2 <= cap && tm * tn * split * 2 <= 256 &&
+                       steps >= split * 2 * (tm * tn * split * 2 > 128 ? 32 : 16))
+                    split *= 2;
             }
             if (split > steps) split = steps > 0 ? (int)steps : 1;
             if (split > 65535) return GE_ERR_SHAPE;

@@ -264,12 +264,14 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_a
         // themselves.  A device-scope fence would do instead, but on this
         // chip it writes back and invalidates the whole L2 of the XCD, and
         // every other workgroup there then re-fetches x from memory.
-        float* part = p.partial + ((int64_t)slice * p.tiles_n + nblk) * 256 * RG + lane * 4;
+        // (element i of lane l at i * 64 + l: each store covers 256
+        // contiguous bytes)
+        float* part = p.partial + ((int64_t)slice * p.tiles_n + nblk) * 256 * RG + lane;
 #pragma unroll
         for (int g = 0; g < RG; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __hip_atomic_store(part + g * 256 + i, sum[g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part + g * 256 + i * 64, sum[g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // every lane's stores complete (performed at device scope) before
         // the arrival is counted; the clobber keeps the compiler from
         // moving either across the wait
@@ -287,12 +289,13 @@ __global__ void __launch_bounds__(kSmWaves * 64) ge_smallm_kernel(KernelArgs p_a
 #pragma unroll
         for (int g = 0; g < RG; ++g) sum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int sl = 0; sl < p.split_k; ++sl) {
-            float* ps = p.partial + ((int64_t)sl * p.tiles_n + nblk) * 256 * RG + lane * 4;
+            float* ps = p.partial + ((int64_t)sl * p.tiles_n + nblk) * 256 * RG + lane;
 #pragma unroll
             for (int g = 0; g < RG; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sum[g][i] += __hip_atomic_load(ps + g * 256 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sum[g][i] += __hip_atomic_load(ps + g * 256 + i * 64, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         if (lane == 0) p.counters[nblk] = 0u;   // re-arm for the next launch
     }

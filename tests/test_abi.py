@@ -438,6 +438,26 @@ def test_small_pipelined_tile_rejects_fp8():
         B.gemm_epilog_free(h)
 
 
+@pytest.mark.parametrize("m,n,k,tile,split", [
+    (128, 128, 65536, 14, 16), (256, 256, 4096, 14, 4), (256, 256, 8192, 14, 8), (256, 256, 65536, 14, 8),
+    (256, 512, 32768, 14, 8), (512, 512, 4096, 14, 2), (512, 512, 8192, 14, 4), (512, 512, 16384, 14, 4),
+    (1024, 512, 8192, 14, 2), (1024, 512, 16384, 14, 2), (1024, 512, 2048, 13, 1), (1024, 1024, 8192, 13, 1),
+    (256, 256, 2048, 13, 1),
+])
+def test_split_k_planner_choice(m, n, k, tile, split):
+    """The planner's split-K choice on the shapes it was measured on: the
+    split tile for at most 64 tiles with k >= 4096 or at most 128 with
+    k >= 8192; slices of 16 or more K steps (32 beyond 128 workgroups), at
+    most 256 workgroups, at most 8 slices (16 for at most 4 tiles)."""
+    h = B.gemm_epilog_create(B.make_desc(m, n, k, "bf16", "bf16", 0))
+    try:
+        B.gemm_epilog_plan(h, "bias", "row")
+        s = B.gemm_epilog_describe(h)
+        assert f"tile_id={tile} " in s and f" split_k={split} " in s, s
+    finally:
+        B.gemm_epilog_free(h)
+
+
 def test_split_k_tile_plan():
     """Tile 14 (the 64x64 tile with split-K): 16-bit inputs only, no
     bias-gradient epilogues, partials (tiles x split x 64 x 64 fp32) and one
@@ -446,7 +466,9 @@ def test_split_k_tile_plan():
     try:
         B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 0))
         assert "tile_id=14" in B.gemm_epilog_describe(h) and "split_k=1 " in B.gemm_epilog_describe(h)
-        assert B.gemm_epilog_workspace_size(h) == 0     # 128 tiles already fill the 128-workgroup budget
+        # 32 K steps over 128 tiles: two slices would pass 128 workgroups
+        # with fewer than 32 steps each, so the tile stays unsplit
+        assert B.gemm_epilog_workspace_size(h) == 0
         B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 4))
         assert B.gemm_epilog_workspace_size(h) == 128 * 4 * 64 * 64 * 4 + 512
         B.gemm_epilog_plan(h, "bias", "row", B.ge_pref(1, 0, 14, 3))

@@ -373,6 +373,18 @@ def test_split_k_tile_unfused_and_repeated_calls():
     check_full(w, r)
 
 
+@pytest.mark.parametrize("m,n,k,split", [(128, 128, 65536, 16), (1000, 500, 8200, 2), (500, 500, 8192, 4),
+                                         (250, 260, 4100, 4)])
+def test_split_k_tile_planner_choice(m, n, k, split):
+    """The planner's own split-K plans, ragged where the shape allows: up to
+    256 workgroups, 16 slices on 4 tiles, the last slice shorter than the
+    others (k = 8200 in 2, 4100 in 4)."""
+    w = wl(m, n, k, "bf16", "bf16", "relu_aux_bias", "row", 0, seed=m + k)
+    r = run_library(w, synth.make_inputs(w), pad=1)
+    assert "tile_id=14 " in r.desc and f" split_k={split} " in r.desc, r.desc
+    check_full(w, r)
+
+
 # ---- the mask's tie rule: P == 0 gives bit 0 ---------------------------------------
 def int_inputs(w, lo=-2, hi=2, blo=-8, bhi=8, seed=31):
     """Small-integer operands and bias: every fp32 partial sum and the
