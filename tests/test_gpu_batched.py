@@ -118,6 +118,19 @@ def test_batched_split_k_tile():
         check_full(w, r)
 
 
+@pytest.mark.parametrize("tile,a,split", [(14, "bf16", 3), (6, "bf16", 0), (16, "e4m3", 0)])
+def test_batched_k_rotation(tile, a, split, monkeypatch):
+    """A rotated K order in a batch and inside K slices: every product and
+    every slice (its own full steps rotated, its ragged step last) must sum
+    each K step once (k = 4100: split-K slices of 1408, 1408 and 1284)."""
+    monkeypatch.setenv("GE_K_STAGGER", "3")
+    w = wl(330, 520, 4100 if tile == 14 else 1000, a, "bf16", "relu_aux_bias", "row", 0, seed=tile)
+    rs = run_batched(w, 2, path=1, tile=tile, split_k=split)
+    assert rs[0].desc.endswith(" k_stagger=3"), rs[0].desc
+    for r in rs:
+        check_full(w, r)
+
+
 def test_batched_ragged_n_with_row_bias_and_col_gradient():
     """n = 201 (bf16 rows of 402 bytes): a row bias is read one value per
     row, and a column bias gradient is written one value at a time, so both
