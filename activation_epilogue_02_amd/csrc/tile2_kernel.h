@@ -752,12 +752,23 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
             step_last(kt, kt % SE, std::false_type{});
             step_last(kt + 1, (kt + 1) % SE, std::true_type{});
         }
+        // one final MFMA call on set 0 (an odd tail moves its last
+        // fragments there): with a call per path, the two paths' ends left
+        // the accumulators in different registers and the join spilled them
         if (kt < KT - 1) {
             step_last(kt, kt % SE, std::false_type{});
-            mfmas(a1, b1, sa1, sb1);
-        } else if (KT > 0) {
-            mfmas(a0, b0, sa0, sb0);
+#pragma unroll
+            for (int f = 0; f < C::FM; ++f) {
+                a0[f] = a1[f];
+                sa0[f] = sa1[f];
+            }
+#pragma unroll
+            for (int f = 0; f < C::FN; ++f) {
+                b0[f] = b1[f];
+                sb0[f] = sb1[f];
+            }
         }
+        if (KT > 0) mfmas(a0, b0, sa0, sb0);
     } else {
         for (; kt < KT - 1; ++kt) step_last(kt, kt % SE, std::false_type{});
         if (KT > 0) {
