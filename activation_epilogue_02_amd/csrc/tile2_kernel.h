@@ -928,93 +928,115 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     const float sd = (OUT8 && p.scale_d) ? *p.scale_d : 1.0f;
     float amax_l = 0.0f;
 
+    // The epilogue, unrolled over the accumulators, tests the epilogue kind
+    // per element: on the 256 x 256 tiles that code holds every kind's
+    // branches (130 KB, twice the instruction cache two CUs share) and is
+    // fetched cold at the end of every tile.  There the ReLU kinds also get
+    // a copy compiled for their kind alone, picked once per tile.
+    auto epilogue = [&](auto ep_c) __attribute__((always_inline)) {
+        const int ep = static_cast<int>(ep_c);   // a constant when ep_c is one
+        const bool has_bias = epilog_has_bias(ep);
+        const bool want_aux = ep == GE_EPILOG_RELU_AUX_BIAS;
+        const bool want_pre = ep == GE_EPILOG_GELU_AUX_BIAS;
+        const bool want_grad = epilog_is_grad(ep);
+        const bool want_bgrad = epilog_is_bgrad(ep);
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-        const int m = m0 + wm * C::TM + fm * 32 + r32;
-        const bool mok = m < M;
-        float brow = 0.0f;
-        if (has_bias && row_bias && mok) brow = load_scalar<DB>(p.bias, m);
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = m0 + wm * C::TM + fm * 32 + r32;
+            const bool mok = m < M;
+            float brow = 0.0f;
+            if (has_bias && row_bias && mok) brow = load_scalar<DB>(p.bias, m);
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-            const int nb = n0 + wn * C::TN + fn * 32;
-            const f32x16 a = acc[fn][fm];
-            float v[2][8];
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int nb = n0 + wn * C::TN + fn * 32;
+                const f32x16 a = acc[fn][fm];
+                float v[2][8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * g + e]),
+                                                                   __float_as_uint(a[8 * g + 4 + e]), false, false);
+                        v[g][e] = __uint_as_float(sw[0]);
+                        v[g][4 + e] = __uint_as_float(sw[1]);
+                    }
+                }
+                uint32_t bits = 0;
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
-                    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * g + e]),
-                                                               __float_as_uint(a[8 * g + 4 + e]), false, false);
-                    v[g][e] = __uint_as_float(sw[0]);
-                    v[g][4 + e] = __uint_as_float(sw[1]);
-                }
-            }
-            uint32_t bits = 0;
+                    const int nc = nb + 16 * g + 8 * h;
+                    const bool full = nc + 8 <= N;
+                    float bc[8];
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int nc = nb + 16 * g + 8 * h;
-                const bool full = nc + 8 <= N;
-                float bc[8];
+                    for (int j = 0; j < 8; ++j) bc[j] = brow;
+                    if (has_bias && !row_bias) {
+                        if (full) load8<DB>(p.bias, nc, bc);
+                        else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) bc[j] = brow;
-                if (has_bias && !row_bias) {
-                    if (full) load8<DB>(p.bias, nc, bc);
-                    else {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DB>(p.bias, nc + j) : 0.0f;
+                            for (int j = 0; j < 8; ++j) bc[j] = (nc + j < N) ? load_scalar<DB>(p.bias, nc + j) : 0.0f;
+                        }
                     }
-                }
-                float gf[8], pre[8], cb[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    cb[j] = 0.0f;
-                    gf[j] = 0.0f;
-                }
-                if constexpr (!OUT8) {
-                    if (with_c && mok) beta_c8<DOUT>(p, beta, m, nc, cb);
-                    if (want_grad && mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float x = (v[g][j] * s + cb[j]) + bc[j];
-                    pre[j] = x;
-                    if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
-                    v[g][j] = want_grad ? grad_apply(ep, x, gf[j]) : activate(ep, x);
-                }
-                if (want_bgrad) {
+                    float gf[8], pre[8], cb[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const float val = (mok && nc + j < N) ? v[g][j] : 0.0f;
-                        if (bgrad_col) bg.col[fn][g][j] += val;
-                        else bg.row[fm] += val;
-                    }
-                }
-                if constexpr (OUT8) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float av = __builtin_fabsf(v[g][j]);   // NaN compares false: not counted
-                        if (mok && nc + j < N && av > amax_l) amax_l = av;
-                        v[g][j] *= sd;
-                    }
-                }
-                if (mok) {
-                    const int64_t idx = (int64_t)m * p.ldd + nc;
-                    if (full) store8<DOUT>(p.D, idx, v[g]);
-                    else {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            if (nc + j < N) store_one<DOUT>(p.D, idx + j, v[g][j]);
+                        cb[j] = 0.0f;
+                        gf[j] = 0.0f;
                     }
                     if constexpr (!OUT8) {
-                        if (want_pre) store_pre8<DOUT>(p, m, nc, pre);
+                        if (with_c && mok) beta_c8<DOUT>(p, beta, m, nc, cb);
+                        if (want_grad && mok) grad_factor8<DOUT>(p, ep, m, nc, gf);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float x = (v[g][j] * s + cb[j]) + bc[j];
+                        pre[j] = x;
+                        if (want_aux && x > 0.0f && nc + j < N) bits |= 1u << (16 * g + 8 * h + j);
+                        v[g][j] = want_grad ? grad_apply(ep, x, gf[j]) : activate(ep, x);
+                    }
+                    if (want_bgrad) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float val = (mok && nc + j < N) ? v[g][j] : 0.0f;
+                            if (bgrad_col) bg.col[fn][g][j] += val;
+                            else bg.row[fm] += val;
+                        }
+                    }
+                    if constexpr (OUT8) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float av = __builtin_fabsf(v[g][j]);   // NaN compares false: not counted
+                            if (mok && nc + j < N && av > amax_l) amax_l = av;
+                            v[g][j] *= sd;
+                        }
+                    }
+                    if (mok) {
+                        const int64_t idx = (int64_t)m * p.ldd + nc;
+                        if (full) store8<DOUT>(p.D, idx, v[g]);
+                        else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                if (nc + j < N) store_one<DOUT>(p.D, idx + j, v[g][j]);
+                        }
+                        if constexpr (!OUT8) {
+                            if (want_pre) store_pre8<DOUT>(p, m, nc, pre);
+                        }
                     }
                 }
-            }
-            if (want_aux) {
-                bits |= (uint32_t)__shfl_xor((int)bits, 32);
-                if (h == 0 && mok && (nb >> 5) < p.ldaux) p.aux[(int64_t)m * p.ldaux + (nb >> 5)] = bits;
+                if (want_aux) {
+                    bits |= (uint32_t)__shfl_xor((int)bits, 32);
+                    if (h == 0 && mok && (nb >> 5) < p.ldaux) p.aux[(int64_t)m * p.ldaux + (nb >> 5)] = bits;
+                }
             }
         }
+    };
+    if constexpr (BM == 256 && BN == 256 && C::SPREAD && !MX && !SPLIT) {
+        switch (p.epilog) {
+        case GE_EPILOG_RELU_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_BIAS>{}); break;
+        case GE_EPILOG_RELU_AUX_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_AUX_BIAS>{}); break;
+        default: epilogue(ep); break;
+        }
+    } else {
+        epilogue(ep);
     }
     if constexpr (OUT8) {
         if (p.amax) {
