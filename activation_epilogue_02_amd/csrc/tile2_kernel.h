@@ -932,7 +932,9 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     // per element: on the 256 x 256 tiles that code holds every kind's
     // branches (130 KB, twice the instruction cache two CUs share) and is
     // fetched cold at the end of every tile.  There the ReLU kinds also get
-    // a copy compiled for their kind alone, picked once per tile.
+    // a copy compiled for their kind alone, picked once per tile, and so do
+    // GELU_AUX_BIAS, DRELU and DGELU with bf16 input and output on the
+    // 8-wave tile.
     auto epilogue = [&](auto ep_c) __attribute__((always_inline)) {
         const int ep = static_cast<int>(ep_c);   // a constant when ep_c is one
         const bool has_bias = epilog_has_bias(ep);
@@ -1033,7 +1035,26 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
         switch (p.epilog) {
         case GE_EPILOG_RELU_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_BIAS>{}); break;
         case GE_EPILOG_RELU_AUX_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_AUX_BIAS>{}); break;
-        default: epilogue(ep); break;
+        default: {
+            // three training kinds, for bf16 in and out on the 8-wave tile
+            // (the planner's choice for the large backward products).  On
+            // the 4-wave 256 x 256 tile, whose 128 accumulators per lane
+            // leave no registers spare, the copy for DGELU_BGRAD gave a wrong
+            // bias gradient, so that tile and the BGRAD kinds keep the
+            // generic code.
+            bool done = false;
+            if constexpr (DIN == GE_BF16 && DOUT == GE_BF16 && WM * WN == 8) {
+                done = true;
+                switch (p.epilog) {
+                case GE_EPILOG_GELU_AUX_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_GELU_AUX_BIAS>{}); break;
+                case GE_EPILOG_DRELU: epilogue(std::integral_constant<int, GE_EPILOG_DRELU>{}); break;
+                case GE_EPILOG_DGELU: epilogue(std::integral_constant<int, GE_EPILOG_DGELU>{}); break;
+                default: done = false; break;
+                }
+            }
+            if (!done) epilogue(ep);
+            break;
+        }
         }
     } else {
         epilogue(ep);
