@@ -25,8 +25,8 @@ def wl(m, n, k, d, ep, axis="row", op_b=0, seed=7, a="mxf8"):
 
 @pytest.mark.parametrize("d", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("op_b", [0, 1])
-@pytest.mark.parametrize("ep,axis", [("relu_aux_bias", "row"), ("gelu_bias", "col"), ("none", "row"),
-                                     ("bias", "col")])
+@pytest.mark.parametrize("ep,axis", [("relu_aux_bias", "row"), ("relu_bias", "row"), ("gelu_bias", "col"),
+                                     ("none", "row"), ("bias", "col")])
 def test_mx_ragged(d, op_b, ep, axis):
     # 300 x 520: three 128-row tiles, five 128-column tiles, ragged; k = 456:
     # three full 128-deep steps and a tail of 72 (blocks 12, 13 whole, 14
