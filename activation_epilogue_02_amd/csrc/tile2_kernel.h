@@ -932,7 +932,7 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     // per element: on the 256 x 256 tiles that code holds every kind's
     // branches (130 KB, twice the instruction cache two CUs share) and is
     // fetched cold at the end of every tile (69 KB on the block-scaled
-    // 128 x 128 tile).  There the ReLU kinds also get
+    // 128 x 128 tile).  There NONE, BIAS and the ReLU kinds also get
     // a copy compiled for their kind alone, picked once per tile, and so do
     // GELU_AUX_BIAS, DRELU and DGELU with bf16 input and output on the
     // 8-wave tile.
@@ -1034,6 +1034,10 @@ __global__ void __launch_bounds__(WM* WN * 64) ge_tile2_kernel(KernelArgs p_all,
     };
     if constexpr ((BM == 256 && BN == 256 && C::SPREAD && !SPLIT) || MX) {
         switch (p.epilog) {
+        // (NONE is the product of the unfused pair: its own copy keeps that
+        // baseline from paying the generic code's cost)
+        case GE_EPILOG_NONE: epilogue(std::integral_constant<int, GE_EPILOG_NONE>{}); break;
+        case GE_EPILOG_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_BIAS>{}); break;
         case GE_EPILOG_RELU_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_BIAS>{}); break;
         case GE_EPILOG_RELU_AUX_BIAS: epilogue(std::integral_constant<int, GE_EPILOG_RELU_AUX_BIAS>{}); break;
         default: {
